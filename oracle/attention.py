@@ -1,0 +1,143 @@
+"""Oracle: attention over a paged KV cache, in float64 (test infrastructure only).
+
+What is computed (the plain definition; paging is only an address translation):
+
+* Paging [P3 §"Anatomy of the KV Cache: Memory Layout, Paging and Quantization Trade-offs";
+  P1 §"PagedAttention: making the KV cache schedulable"; P5 §"PagedAttention: The Other Half
+  of the Story"]: physical KV memory is a pool of fixed-size blocks laid out
+  [num_blocks, block_size, num_heads, head_dim]; each sequence owns a block table listing block
+  ids in logical order, so logical position j lives in block ``table[j // block_size]`` at row
+  ``j % block_size``.  The pool here holds one such plane for K and one for V.
+* Decode and verify rows [P1 §"The core idea"; P2 §"Speculative Decoding: Draft Fast, Verify
+  Cheap"; P3 §"Speculative Decoding: Turning Verification Parallelism into Latency Wins"]: a
+  sequence with context length L (counting this step's Q new tokens) brings Q query rows; row i
+  sits at absolute position L - Q + i and sees keys 0 .. L - Q + i (causal within the draft or
+  prefill chunk), so the Q rows equal Q sequential single-token decode steps.
+* Grouped-query attention [P3 §"Prefill vs. Decode: Two Distinct Bottlenecks"]: query head h
+  reads KV head h // (Hq / Hkv).
+* Scores use the scale 1/sqrt(head_dim) unless a scale is given; weights are the softmax of the
+  scores over the visible keys; the output is the weighted sum of V rows.
+
+Reading taken where the pages are silent: the scale, the head grouping (contiguous groups) and
+"L counts the new tokens" are the plainest readings consistent with the pages.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bf16 bit patterns (bf16 is the upper half of an IEEE fp32)."""
+    u = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def physical_slots(table_row: np.ndarray, n_tokens: int, block_size: int) -> np.ndarray:
+    """Flat pool slot (block * block_size + row) of logical positions 0 .. n_tokens-1."""
+    j = np.arange(n_tokens)
+    blocks = np.asarray(table_row)[j // block_size].astype(np.int64)
+    if n_tokens and (blocks.min() < 0):
+        raise ValueError("block table entry < 0 inside the context")
+    return blocks * block_size + (j % block_size)
+
+
+def gather_sequence_kv(pool_plane: np.ndarray, table_row: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Contiguous [n_tokens, Hkv, D] view of one sequence's K (or V) read through its table.
+
+    ``pool_plane`` is [num_blocks, block_size, Hkv, D] of any dtype; rows are returned as-is.
+    """
+    nb, bs = pool_plane.shape[0], pool_plane.shape[1]
+    flat = pool_plane.reshape(nb * bs, *pool_plane.shape[2:])
+    return flat[physical_slots(table_row, n_tokens, bs)]
+
+
+def attend_row(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * keys @ q_row) @ values for one query row over its visible keys.
+
+    keys, values: [n, D] float64 with n >= 1.  The maximum score is subtracted before the
+    exponential (a shift that leaves the softmax unchanged).
+    """
+    z = scale * (keys @ q_row)
+    w = np.exp(z - z.max())
+    return (w @ values) / w.sum()
+
+
+def attention_sequence(q_seq: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
+                       scale: float | None = None, heads=None, rows=None) -> np.ndarray:
+    """Attention for one sequence with contiguous KV.
+
+    q_seq [Q, Hq, D]; k_seq, v_seq [L, Hkv, D] (float64).  Returns [Q, Hq, D] float64
+    (entries not requested through ``rows`` / ``heads`` are left as NaN).
+    """
+    Q, Hq, D = q_seq.shape
+    L, Hkv, _ = k_seq.shape
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if not 1 <= Q <= L:
+        raise ValueError("need 1 <= q_len <= ctx_len")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.full((Q, Hq, D), np.nan)
+    for i in (range(Q) if rows is None else rows):
+        visible = L - Q + i + 1          # keys 0 .. L-Q+i
+        for h in (range(Hq) if heads is None else heads):
+            g = h // G
+            out[i, h] = attend_row(q_seq[i, h], k_seq[:visible, g], v_seq[:visible, g], scale)
+    return out
+
+
+def paged_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                    block_tables: np.ndarray, ctx_lens, q_lens, scale: float | None = None) -> np.ndarray:
+    """Attention for a ragged batch through block tables.
+
+    q [T, Hq, D] float64 with rows packed by sequence; k_pool, v_pool [NB, bs, Hkv, D] float64;
+    block_tables [B, MB] int; ctx_lens, q_lens [B].  Returns [T, Hq, D] float64.
+    """
+    out = np.empty(q.shape, dtype=np.float64)
+    row = 0
+    for s in range(len(ctx_lens)):
+        L, Q = int(ctx_lens[s]), int(q_lens[s])
+        ks = gather_sequence_kv(k_pool, block_tables[s], L)
+        vs = gather_sequence_kv(v_pool, block_tables[s], L)
+        out[row:row + Q] = attention_sequence(q[row:row + Q], ks, vs, scale)
+        row += Q
+    return out
+
+
+def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables: np.ndarray,
+                         ctx_lens, q_lens, scale: float | None = None, rows=None) -> dict:
+    """Same as ``paged_attention`` from bf16 bit patterns, converting only what is read.
+
+    q_bits [T, Hq, D] uint16; pool_bits [2, NB, bs, Hkv, D] uint16.  ``rows`` optionally
+    restricts the work to a list of (packed row t, head h) pairs; the result maps each computed
+    (t, h) to its [D] float64 output.
+    """
+    T, Hq, D = q_bits.shape
+    starts = np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))])
+    wanted = None
+    if rows is not None:
+        wanted = {}
+        for t, h in rows:
+            s = int(np.searchsorted(starts, t, side="right") - 1)
+            wanted.setdefault(s, []).append((int(t), int(h)))
+    result = {}
+    for s in range(len(ctx_lens)):
+        if wanted is not None and s not in wanted:
+            continue
+        L, Q, r0 = int(ctx_lens[s]), int(q_lens[s]), int(starts[s])
+        ks = bf16_bits_to_f64(gather_sequence_kv(pool_bits[0], block_tables[s], L))
+        vs = bf16_bits_to_f64(gather_sequence_kv(pool_bits[1], block_tables[s], L))
+        qs = bf16_bits_to_f64(q_bits[r0:r0 + Q])
+        if wanted is None:
+            o = attention_sequence(qs, ks, vs, scale)
+            for i in range(Q):
+                for h in range(Hq):
+                    result[(r0 + i, h)] = o[i, h]
+        else:
+            for t, h in wanted[s]:
+                o = attention_sequence(qs, ks, vs, scale, heads=[h], rows=[t - r0])
+                result[(t, h)] = o[t - r0, h]
+    return result

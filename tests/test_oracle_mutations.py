@@ -1,0 +1,190 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case swaps one oracle function for a copy with a plausible bug (a dropped term, a wrong
+sign, index or scale, a transposed role) and runs the pin tests; at least one must fail.
+The oracle itself is restored after every case.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import spec_verify as S
+import tests.test_oracle_attention as TA
+import tests.test_oracle_spec_verify as TS
+
+GOLDEN = TA.os.path.join(TA.os.path.dirname(TA.os.path.abspath(TA.__file__)), "golden")
+
+ATTN_PINS = [
+    lambda: TA.test_golden_worked_cases(GOLDEN),
+    TA.test_single_key_returns_its_value_exactly,
+    TA.test_equal_keys_give_the_mean_of_visible_values,
+    lambda: TA.test_matches_torch_sdpa_fp64(5, 40, 4, 4, 32),
+    lambda: TA.test_matches_torch_sdpa_fp64(5, 77, 32, 8, 128),
+    TA.test_matches_torch_sdpa_with_explicit_scale_and_large_scores,
+    TA.test_verify_rows_equal_sequential_decodes,
+    lambda: TA.test_block_table_permutation_gives_contiguous_result_bit_exact(16),
+    TA.test_physical_slot_translation_by_hand,
+]
+
+
+def _seq_variant(scale_fn=None, visible_fn=None, head_fn=None, row_fn=None):
+    def attention_sequence(q_seq, k_seq, v_seq, scale=None, heads=None, rows=None):
+        Q, Hq, D = q_seq.shape
+        L, Hkv, _ = k_seq.shape
+        if Hq % Hkv or not 1 <= Q <= L:
+            raise ValueError("bad shape")
+        G = Hq // Hkv
+        if scale is None:
+            scale = scale_fn(D) if scale_fn else 1.0 / np.sqrt(D)
+        out = np.full((Q, Hq, D), np.nan)
+        for i in (range(Q) if rows is None else rows):
+            vis = visible_fn(L, Q, i) if visible_fn else L - Q + i + 1
+            vis = max(1, min(L, vis))
+            for h in (range(Hq) if heads is None else heads):
+                g = head_fn(h, G, Hkv) if head_fn else h // G
+                f = row_fn or A.attend_row
+                out[i, h] = f(q_seq[i, h], k_seq[:vis, g], v_seq[:vis, g], scale)
+        return out
+    return attention_sequence
+
+
+def _row_no_shift(q, k, v, scale):
+    w = np.exp(scale * (k @ q))
+    return (w @ v) / w.sum()
+
+
+def _row_no_normalise(q, k, v, scale):
+    z = scale * (k @ q)
+    return np.exp(z - z.max()) @ v
+
+
+def _row_keys_for_values(q, k, v, scale):
+    z = scale * (k @ q)
+    w = np.exp(z - z.max())
+    return (w @ k) / w.sum()
+
+
+def _slots_swapped(table_row, n_tokens, block_size):
+    j = np.arange(n_tokens)
+    blocks = np.asarray(table_row)[j // block_size].astype(np.int64)
+    return blocks + (j % block_size) * block_size
+
+
+ATTN_MUTANTS = {
+    "scale 1/D": ("attention_sequence", _seq_variant(scale_fn=lambda D: 1.0 / D)),
+    "no scale": ("attention_sequence", _seq_variant(scale_fn=lambda D: 1.0)),
+    "causal limit one short": ("attention_sequence", _seq_variant(visible_fn=lambda L, Q, i: L - Q + i)),
+    "causal from the wrong end": ("attention_sequence", _seq_variant(visible_fn=lambda L, Q, i: L - i)),
+    "gqa h % Hkv": ("attention_sequence", _seq_variant(head_fn=lambda h, G, Hkv: h % Hkv)),
+    "no max shift": ("attend_row", _row_no_shift),
+    "no normalisation": ("attend_row", _row_no_normalise),
+    "keys used as values": ("attend_row", _row_keys_for_values),
+    "slot = block + row * bs": ("physical_slots", _slots_swapped),
+}
+
+
+def _any_pin_fails(pins):
+    for pin in pins:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(name, monkeypatch):
+    attr, fn = ATTN_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    assert _any_pin_fails(ATTN_PINS), f"no attention pin caught: {name}"
+
+
+SPEC_PINS = [
+    lambda: TS.test_golden_worked_cases(GOLDEN),
+    TS.test_p_equal_q_accepts_every_draft,
+    TS.test_zero_target_probability_is_always_rejected,
+    TS.test_temperature_zero_reduces_to_exact_matching,
+    TS.test_k_zero_is_numpy_inverse_cdf,
+    TS.test_out_of_range_draft_is_rejected,
+    TS.test_emitted_distribution_exact_by_stratified_enumeration,
+]
+
+
+def _verify_variant(accept=None, residual=None, bonus_row=None, keep_going=False, pad=-1):
+    def verify_sequence(p_rows, q_rows, drafts, uniforms):
+        p_rows = np.asarray(p_rows, dtype=np.float64)
+        q_rows = np.asarray(q_rows, dtype=np.float64)
+        k = len(drafts)
+        V = p_rows.shape[1]
+        out = np.full(k + 1, pad, dtype=np.int64)
+        n = k
+        for i in range(k):
+            x = int(drafts[i])
+            inside = 0 <= x < V
+            P = p_rows[i, x] if inside else 0.0
+            Qx = q_rows[i, x] if inside else 0.0
+            ok = accept(P, Qx, uniforms[i]) if accept else S.accept_draft(P, Qx, uniforms[i])
+            if ok:
+                out[i] = x
+            elif n == k:
+                n = i
+                if not keep_going:
+                    break
+        if n < k:
+            w = residual(p_rows[n], q_rows[n]) if residual else np.maximum(0.0, p_rows[n] - q_rows[n])
+        else:
+            w = p_rows[bonus_row(k)] if bonus_row else p_rows[k]
+        y = S.sample_inverse_cdf(w, uniforms[k])
+        if y < 0:
+            y = S.sample_inverse_cdf(p_rows[n], uniforms[k])
+        out[n] = max(y, 0)
+        return out, n
+    return verify_sequence
+
+
+def _cdf_descending(w, u):
+    w = np.asarray(w, dtype=np.float64)[::-1]
+    cum = np.cumsum(w)
+    if not cum[-1] > 0:
+        return -1
+    return int(w.size - 1 - np.nonzero(cum > u * cum[-1])[0][0])
+
+
+def _cdf_u_not_scaled(w, u):
+    cum = np.cumsum(np.asarray(w, dtype=np.float64))
+    if not cum[-1] > 0:
+        return -1
+    above = np.nonzero(cum > u)[0]
+    return int(above[0]) if above.size else int(np.nonzero(np.asarray(w) > 0)[0][-1])
+
+
+SPEC_MUTANTS = {
+    "inverted ratio": ("verify_sequence", _verify_variant(accept=lambda P, Q, r: Q > 0 and r * P <= Q)),
+    "accept ignores ratio": ("verify_sequence", _verify_variant(accept=lambda P, Q, r: P > 0)),
+    "residual q - p": ("verify_sequence", _verify_variant(residual=lambda p, q: np.maximum(0.0, q - p))),
+    "residual without clamp": ("verify_sequence", _verify_variant(residual=lambda p, q: np.abs(p - q))),
+    "residual is p": ("verify_sequence", _verify_variant(residual=lambda p, q: p)),
+    "bonus from row k-1": ("verify_sequence", _verify_variant(bonus_row=lambda k: max(k - 1, 0))),
+    "keeps checking after a rejection": ("verify_sequence", _verify_variant(keep_going=True)),
+    "pads with 0": ("verify_sequence", _verify_variant(pad=0)),
+    "cdf in descending id": ("sample_inverse_cdf", _cdf_descending),
+    "u not scaled by Z": ("sample_inverse_cdf", _cdf_u_not_scaled),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPEC_MUTANTS))
+def test_spec_verify_mutant_is_caught(name, monkeypatch):
+    attr, fn = SPEC_MUTANTS[name]
+    monkeypatch.setattr(S, attr, fn)
+    assert _any_pin_fails(SPEC_PINS), f"no spec_verify pin caught: {name}"
+
+
+def test_unmodified_wrappers_pass_every_pin(monkeypatch):
+    """Controls: the mutant scaffolding without a planted mistake passes all pins, so a caught
+    mutant is caught for its mistake and not for the scaffolding."""
+    monkeypatch.setattr(A, "attention_sequence", _seq_variant())
+    monkeypatch.setattr(S, "verify_sequence", _verify_variant())
+    assert not _any_pin_fails(ATTN_PINS)
+    assert not _any_pin_fails(SPEC_PINS)

@@ -1,0 +1,349 @@
+"""Seeded input generators (no attention or sampling arithmetic lives here).
+
+Every draw comes from ``numpy.random.Generator(PCG64(seed))`` in a fixed, documented order,
+so a (config, seed) pair names one input exactly on any machine.
+
+Attention inputs, in draw order:
+  1. context lengths L_s and query lengths Q_s (per-config distribution),
+  2. query values q ~ N(0, 1), fp32 rounded to bf16 (round-to-nearest-even),
+  3. pool values K, V ~ N(0, 1) for every pool slot, rounded to bf16,
+  4. a random permutation of pool blocks; sequence s takes the next ceil(L_s / bs) of them
+     as its block table, in logical order.
+Pool slots that no sequence owns, and the rows of a sequence's last block past L_s, are then
+overwritten with a poison value (NaN by default) so that any read past ``ctx_len`` shows up.
+Unused block-table entries are -1.
+
+Speculative-verification inputs, in draw order:
+  1. logits (target rows [B, k+1, V], draft rows [B, k, V]) per the config,
+  2. draft tokens x_i ~ q_i (one categorical draw per draft position),
+  3. uniforms u in the open interval (0, 1), k+1 per sequence, exactly representable in fp32.
+Probability rows are softmax(logits) evaluated in float64 and stored as float32; this is the
+input recipe (the verifier consumes probabilities), not part of the verifier.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+CONFIG_NAMES = ("tiny", "llama3_8b_decode", "spec_verify_step", "llama70b_share", "mixed_step")
+DEFAULT_SEEDS = {name: 1001 + i for i, name in enumerate(CONFIG_NAMES)}
+
+_CHUNK = 1 << 24  # values drawn per numpy call when filling large pools
+
+
+@dataclass
+class AttnInputs:
+    """One ragged batch for a paged attention step (CPU tensors; move with ``.to(device)``).
+
+    q            bf16  [T, Hq, D]     rows packed by sequence, in sequence order
+    kv_pool      bf16  [2, NB, bs, Hkv, D]   plane 0 = K, plane 1 = V
+    block_tables int32 [B, MB]        logical block -> physical block, -1 padded
+    ctx_lens     int32 [B]            L_s, counting this step's Q_s new tokens
+    q_lens       int32 [B]            Q_s (1 = decode, k+1 = verify, chunk = prefill)
+    """
+
+    name: str
+    seed: int
+    q: torch.Tensor
+    kv_pool: torch.Tensor
+    block_tables: torch.Tensor
+    ctx_lens: torch.Tensor
+    q_lens: torch.Tensor
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.ctx_lens.numel())
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_pool.shape[1])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+
+@dataclass
+class VerifyInputs:
+    """One batch for speculative verification (CPU tensors).
+
+    p          fp32  [B, k+1, V]   target probabilities for the k drafts plus the bonus row
+    q          fp32  [B, k, V]     draft probabilities
+    draft_ids  int32 [B, k]
+    uniforms   fp32  [B, k+1]      u[:, :k] for the accept tests, u[:, k] for the final draw
+    """
+
+    name: str
+    seed: int
+    p: torch.Tensor
+    q: torch.Tensor
+    draft_ids: torch.Tensor
+    uniforms: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.p.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def vocab(self) -> int:
+        return int(self.p.shape[2])
+
+
+# ----------------------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------------------
+
+def _normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
+    """N(0,1) fp32 draws rounded to bf16, drawn in chunks to bound host memory."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.bfloat16)
+    for start in range(0, n, _CHUNK):
+        stop = min(n, start + _CHUNK)
+        x = rng.standard_normal(stop - start, dtype=np.float32)
+        out[start:stop] = torch.from_numpy(x).to(torch.bfloat16)
+    return out.view(*shape)
+
+
+def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniforms in the open interval (0, 1): (j + 1/2) / 2^24, exactly representable in fp32."""
+    j = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
+    return ((j.astype(np.float64) + 0.5) / float(1 << 24)).astype(np.float32)
+
+
+def _lognormal_lengths(rng, n, median, sigma, lo, hi):
+    x = np.exp(math.log(median) + sigma * rng.standard_normal(n))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+def _pareto_lengths(rng, n, alpha, lmin, cap):
+    u = rng.random(n)
+    u = np.where(u <= 0.0, np.nextafter(0.0, 1.0), u)
+    return np.minimum(np.floor(lmin * u ** (-1.0 / alpha)), cap).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------------------
+# attention inputs
+# ----------------------------------------------------------------------------------------
+
+def make_attention_inputs(
+    seed: int,
+    *,
+    ctx_lens,
+    q_lens,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    block_size: int,
+    max_ctx: int | None = None,
+    pool_blocks: int | None = None,
+    pool_factor: float = 1.2,
+    poison: float = float("nan"),
+    rng: np.random.Generator | None = None,
+    name: str = "custom",
+) -> AttnInputs:
+    """Build one paged batch from given lengths (steps 2-4 of the draw order above).
+
+    ``max_ctx`` fixes the block-table width (ceil(max_ctx / bs)); by default the realised
+    maximum.  ``pool_blocks`` fixes the pool size; by default ceil(pool_factor * live blocks).
+    """
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    L = np.asarray(ctx_lens, dtype=np.int64)
+    Q = np.asarray(q_lens, dtype=np.int64)
+    assert L.shape == Q.shape and L.ndim == 1
+    assert np.all(Q >= 1) and np.all(L >= Q), "need 1 <= q_len <= ctx_len"
+    B = L.size
+    bs = int(block_size)
+    nblk = (L + bs - 1) // bs
+    live = int(nblk.sum())
+    if max_ctx is None:
+        max_ctx = int(L.max()) if B else bs
+    MB = max(1, (int(max_ctx) + bs - 1) // bs)
+    assert np.all(nblk <= MB)
+    if pool_blocks is None:
+        pool_blocks = max(live, int(math.ceil(pool_factor * live)))
+    NB = int(pool_blocks)
+    assert NB >= live
+    T = int(Q.sum())
+
+    q = _normal_bf16(rng, (T, num_q_heads, head_dim))
+    pool = _normal_bf16(rng, (2, NB, bs, num_kv_heads, head_dim))
+    perm = rng.permutation(NB)
+
+    tables = np.full((B, MB), -1, dtype=np.int32)
+    owned = np.zeros(NB, dtype=bool)
+    cursor = 0
+    for s in range(B):
+        ids = perm[cursor:cursor + nblk[s]]
+        cursor += int(nblk[s])
+        tables[s, : nblk[s]] = ids
+        owned[ids] = True
+        tail = int(L[s] % bs)
+        if tail:
+            pool[:, int(ids[-1]), tail:] = poison
+    unused = np.nonzero(~owned)[0]
+    if unused.size:
+        pool[:, torch.from_numpy(unused)] = poison
+
+    return AttnInputs(
+        name=name,
+        seed=seed,
+        q=q,
+        kv_pool=pool,
+        block_tables=torch.from_numpy(tables),
+        ctx_lens=torch.from_numpy(L.astype(np.int32)),
+        q_lens=torch.from_numpy(Q.astype(np.int32)),
+        num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        block_size=bs,
+    )
+
+
+_ATTN_SHAPES = {
+    # name: (num_q_heads, num_kv_heads, head_dim, block_size, max_ctx)
+    "tiny": (8, 2, 64, 16, 256),
+    "llama3_8b_decode": (32, 8, 128, 16, 8192),
+    "spec_verify_step": (32, 8, 128, 16, 4096),
+    "llama70b_share": (64, 8, 128, 16, 32768),
+    "mixed_step": (32, 8, 128, 32, 4096),
+}
+
+
+def _config_lengths(name: str, rng: np.random.Generator):
+    """Step 1 of the draw order: (ctx_lens, q_lens) of a named workload."""
+    if name == "tiny":
+        return np.array([17, 64, 100, 255]), np.ones(4, np.int64)
+    if name == "llama3_8b_decode":
+        return _lognormal_lengths(rng, 64, 1024, 1.0, 16, 8192), np.ones(64, np.int64)
+    if name == "spec_verify_step":
+        return rng.integers(512, 4096, size=16, endpoint=True), np.full(16, 5, np.int64)
+    if name == "llama70b_share":
+        return _pareto_lengths(rng, 256, 1.5, 128, 32768), np.ones(256, np.int64)
+    if name == "mixed_step":
+        Ld = _lognormal_lengths(rng, 128, 1024, 1.0, 16, 4096)
+        Lv = _lognormal_lengths(rng, 32, 1024, 1.0, 16, 4096)
+        Lp = rng.integers(256, 4096, size=4, endpoint=True)
+        L = np.concatenate([Ld, Lv, Lp])
+        Q = np.concatenate([np.ones(128, np.int64), np.full(32, 5, np.int64), np.full(4, 256, np.int64)])
+        order = rng.permutation(L.size)
+        return L[order], Q[order]
+    raise KeyError(name)
+
+
+def config_lengths(name: str, seed: int | None = None):
+    """(ctx_lens, q_lens, (Hq, Hkv, D, bs, max_ctx)) of a named workload, without its tensors."""
+    if seed is None:
+        seed = DEFAULT_SEEDS[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    L, Q = _config_lengths(name, rng)
+    return L, Q, _ATTN_SHAPES[name]
+
+
+def attention_config(name: str, seed: int | None = None, poison: float = float("nan")) -> AttnInputs:
+    """The five named attention workloads (lengths drawn first, then make_attention_inputs).
+
+    tiny              4 decode seqs, L = {17, 64, 100, 255}, 8 q / 2 kv heads, D 64, bs 16
+    llama3_8b_decode  64 decode seqs, L lognormal(median 1024, sigma 1) clipped [16, 8192],
+                      32 q / 8 kv heads, D 128, bs 16, pool 1.2x live blocks
+    spec_verify_step  16 verify seqs (q_len 5), L uniform in [512, 4096], 32/8 heads, D 128
+    llama70b_share    256 decode seqs, L Pareto(alpha 1.5, min 128) capped at 32768,
+                      64 q / 8 kv heads, D 128, bs 16
+    mixed_step        128 decode + 32 verify (q_len 5) + 4 prefill chunks (q_len 256);
+                      decode/verify L lognormal(1024, 1) clipped [16, 4096], prefill L uniform
+                      in [256, 4096]; 32/8 heads, D 128, bs 32; pool 95% full; order shuffled
+    All other pools hold ceil(1.2 x live blocks).
+    """
+    if seed is None:
+        seed = DEFAULT_SEEDS[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    L, Q = _config_lengths(name, rng)
+    Hq, Hkv, D, bs, max_ctx = _ATTN_SHAPES[name]
+    pool_blocks = None
+    if name == "mixed_step":
+        live = int(((L + bs - 1) // bs).sum())
+        pool_blocks = int(math.ceil(live / 0.95))
+    return make_attention_inputs(seed, ctx_lens=L, q_lens=Q, num_q_heads=Hq, num_kv_heads=Hkv,
+                                 head_dim=D, block_size=bs, max_ctx=max_ctx,
+                                 pool_blocks=pool_blocks, poison=poison, rng=rng, name=name)
+
+
+# ----------------------------------------------------------------------------------------
+# speculative-verification inputs
+# ----------------------------------------------------------------------------------------
+
+def _softmax_rows_f64(logits: np.ndarray) -> np.ndarray:
+    z = logits - logits.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def make_verify_inputs(seed: int, *, p_logits: np.ndarray, q_logits: np.ndarray,
+                       rng: np.random.Generator | None = None, name: str = "custom") -> VerifyInputs:
+    """Probabilities from logits, drafts x_i ~ q_i, and open-interval uniforms."""
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    B, k1, V = p_logits.shape
+    k = k1 - 1
+    assert q_logits.shape == (B, k, V)
+    p32 = _softmax_rows_f64(p_logits.astype(np.float64)).astype(np.float32)
+    q32 = _softmax_rows_f64(q_logits.astype(np.float64)).astype(np.float32)
+    return make_verify_from_probs(seed, p32, q32, rng=rng, name=name)
+
+
+def make_verify_from_probs(seed: int, p32: np.ndarray, q32: np.ndarray,
+                           rng: np.random.Generator | None = None, name: str = "custom") -> VerifyInputs:
+    """Drafts x_i ~ q_i and uniforms for given fp32 probability rows."""
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    B, k1, V = p32.shape
+    k = k1 - 1
+    drafts = np.zeros((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            w = q32[b, i].astype(np.float64)
+            drafts[b, i] = rng.choice(V, p=w / w.sum())
+    u = open_uniforms(rng, (B, k + 1))
+    return VerifyInputs(name=name, seed=seed, p=torch.from_numpy(np.ascontiguousarray(p32)),
+                        q=torch.from_numpy(np.ascontiguousarray(q32)),
+                        draft_ids=torch.from_numpy(drafts), uniforms=torch.from_numpy(u))
+
+
+def verify_config(name: str, seed: int | None = None, batch: int | None = None) -> VerifyInputs:
+    """Named verification workloads.
+
+    tiny              B 4, k 4, V 1000; target and draft logits independent N(0, 2)
+    spec_verify_step  B 16, k 4, V 128256; target logits N(0, 3); draft logits = target logits
+                      of the first k positions + N(0, 0.7) noise
+    ``batch`` overrides B (same recipe) for batch sweeps.
+    """
+    if seed is None:
+        seed = DEFAULT_SEEDS[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if name == "tiny":
+        B, k, V = batch or 4, 4, 1000
+        pl = 2.0 * rng.standard_normal((B, k + 1, V))
+        ql = 2.0 * rng.standard_normal((B, k, V))
+    elif name == "spec_verify_step":
+        B, k, V = batch or 16, 4, 128256
+        pl = 3.0 * rng.standard_normal((B, k + 1, V))
+        ql = pl[:, :k] + 0.7 * rng.standard_normal((B, k, V))
+    else:
+        raise KeyError(name)
+    return make_verify_inputs(seed, p_logits=pl, q_logits=ql, rng=rng, name=name)
