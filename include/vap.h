@@ -1,0 +1,182 @@
+/*
+ * vap.h -- C ABI of the paged decode/verify attention and speculative verification library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations form one continuous-batching step's data-parallel work:
+ *
+ *   paged_attn_step  attention of a ragged batch of query rows over a paged KV cache.  The KV
+ *                    cache is a pool of fixed-size blocks and each sequence owns a block table
+ *                    mapping logical blocks to pool blocks (tempatgunting.com article,
+ *                    section "Anatomy of the KV Cache: Memory Layout, Paging and Quantization
+ *                    Trade-offs"; syslabs.in "Continuous Batching and Speculative Decoding: How
+ *                    Modern LLM Serving Engines Actually Work", section "PagedAttention: making
+ *                    the KV cache schedulable").  A sequence brings 1 decode row, k+1 verify
+ *                    rows, or a prefill chunk; the rows are causal among themselves, so k+1
+ *                    verify rows equal k+1 sequential decodes (syslabs.in, section "The core
+ *                    idea").
+ *
+ *   spec_verify      speculative-decoding verification by modified rejection sampling: accept
+ *                    draft x_i when r_i <= min(1, p_i(x_i)/q_i(x_i)); on the first rejection
+ *                    draw the replacement from max(0, p - q) normalised; if every draft is
+ *                    accepted draw a bonus token from p_k (neuralmasteryai.com "Continuous
+ *                    Batching & Speculative Decoding", section "The Modified Rejection Sampling
+ *                    Algorithm"; syslabs.in, section "The core idea").
+ *
+ * Conventions shared by every entry point:
+ *   - Data pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *     frees or synchronises device memory on these paths (vap_get_device_error is the only
+ *     call that synchronises).  Inputs are read-only; outputs are fully overwritten.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  All work
+ *     is enqueued on it, in order.
+ *   - Return value: VAP_OK (0) or a negative VAP_E* code for an error detected on the host,
+ *     in which case nothing was enqueued.  vap_last_error_message() describes the last host
+ *     error of the calling thread.
+ *   - Errors found in the data on the device (a block id outside the pool, inconsistent
+ *     lengths, a draft id outside the vocabulary) never fault: the kernels clamp, OR a
+ *     VAP_DERR_* bit into a sticky word at the start of the workspace, and leave the affected
+ *     outputs unspecified (but written only inside the output arrays).
+ *   - A workspace must be zero-filled before its first use (vap_workspace_init, or any
+ *     zero-filled allocation); every call leaves it reusable.  Calls that share a workspace
+ *     must be ordered (same stream, or synchronised).  A workspace serves one kind of call:
+ *     either paged_attn_step or spec_verify, never both.
+ */
+#ifndef VAP_H_
+#define VAP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* host-side return codes */
+#define VAP_OK 0
+#define VAP_EINVAL (-1)  /* null pointer, unsupported or inconsistent sizes            */
+#define VAP_ENOSPC (-2)  /* workspace smaller than the required minimum                */
+#define VAP_EHIP (-3)    /* a HIP runtime call or kernel launch failed                  */
+#define VAP_ENODEV (-4)  /* no usable gfx950 device is current                          */
+
+/* device-side data error bits (sticky, OR-ed into the workspace's first 32-bit word) */
+#define VAP_DERR_BLOCK_ID 0x1  /* block table entry outside [0, num_blocks) inside a context */
+#define VAP_DERR_LENS 0x2      /* q_len < 1, q_len > ctx_len, or ctx_len > table capacity     */
+#define VAP_DERR_TOTAL_Q 0x4   /* sum of q_lens differs from total_q                          */
+#define VAP_DERR_DRAFT_ID 0x8  /* draft id outside [0, vocab)                                  */
+#define VAP_DERR_EMPTY_ROW 0x10 /* the row to sample from has no positive weight              */
+
+/*
+ * Shape of one attention step.
+ *   num_seqs            B, 0 <= B <= 8192
+ *   num_q_heads         Hq, a multiple of num_kv_heads
+ *   num_kv_heads        Hkv >= 1 (query head h reads KV head h / (Hq/Hkv))
+ *   head_dim            D, 64 or 128
+ *   block_size          tokens per KV block, 16 or 32
+ *   num_blocks          blocks in the KV pool
+ *   max_blocks_per_seq  width of a block-table row
+ *   total_q             T = number of packed query rows (must equal the sum of q_lens)
+ *   scale               softmax scale; 0 means 1/sqrt(head_dim)
+ */
+typedef struct vap_attn_shape {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t total_q;
+  float scale;
+} vap_attn_shape;
+
+/* Workspace bytes paged_attn_step needs for `shape` on the current device (0 on bad shape).
+ * A smaller workspace (but at least the minimum reported by vap_attn_workspace_min_bytes)
+ * also works: the library then partitions the work into fewer pieces. */
+size_t vap_attn_workspace_bytes(const vap_attn_shape* shape);
+size_t vap_attn_workspace_min_bytes(const vap_attn_shape* shape);
+
+/*
+ * paged_attn_step -- attention for one ragged batch over a paged KV cache.
+ *
+ *   q             bf16 [total_q][Hq][D]; rows packed by sequence, sequences in order, so
+ *                 sequence s owns rows [sum_{r<s} q_lens[r], ... + q_lens[s]).
+ *   kv_pool       bf16 [2][num_blocks][block_size][Hkv][D]; plane 0 holds K, plane 1 holds V.
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entry j of row s is the pool block
+ *                 of logical block j of sequence s.  Entries past ceil(ctx_len/block_size)
+ *                 are never read (any value, e.g. -1).  Rows may share blocks.
+ *   ctx_lens      int32 [num_seqs]; L_s, the number of cached tokens INCLUDING this step's
+ *                 q_len new tokens (whose K and V are already in the pool).
+ *   q_lens        int32 [num_seqs]; Q_s >= 1.  Row i of sequence s sits at position
+ *                 L_s - Q_s + i and attends keys 0 .. L_s - Q_s + i.
+ *   out           fp32 [total_q][Hq][D]; softmax(scale * q k^T) v per row and head.
+ *   workspace     device scratch of workspace_bytes (see vap_attn_workspace_bytes).
+ *
+ * Enqueues a plan kernel, the attention kernel and a split-merge kernel on `stream`.
+ */
+int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tables,
+                    const int32_t* ctx_lens, const int32_t* q_lens, float* out,
+                    const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes spec_verify needs (0 on bad sizes). */
+size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);
+
+/*
+ * spec_verify -- modified rejection sampling for a batch of speculative drafts.
+ *
+ *   p           fp32 [B][k+1][V]  target probabilities at the k draft positions and the
+ *                                 bonus position (used as given; need not sum to 1)
+ *   q           fp32 [B][k][V]    draft probabilities (may be NULL when k == 0)
+ *   draft_ids   int32 [B][k]      draft tokens (may be NULL when k == 0)
+ *   uniforms    fp32 [B][k+1]     values in (0,1): uniforms[b][i] is r_i for i < k and
+ *                                 uniforms[b][k] drives the final draw
+ *   out_ids     int32 [B][k+1]    accepted drafts, then the drawn token, then -1 padding
+ *   n_accepted  int32 [B]         number of accepted drafts n in [0, k]
+ *   0 <= B <= 2^22, 0 <= k <= 64, V >= 1.
+ *
+ * Per sequence: x_i is accepted iff p_i(x_i) > 0 and r_i * q_i(x_i) <= p_i(x_i) (exact in
+ * fp64); the first rejection at n stops the tests.  The emitted token is drawn from
+ * w = max(0, p_n - q_n) (n < k) or w = p_k (n == k) by inverse CDF in ascending token id:
+ * t = uniforms[b][k] * Z with Z = sum(w) in fp64, and the token is the smallest x whose
+ * running sum exceeds t.  If Z == 0 the row p_n is used instead.  A draft id outside [0,V)
+ * is rejected and sets VAP_DERR_DRAFT_ID.
+ */
+int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
+                int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Zero-fill `bytes` of a workspace on `stream` (a fill kernel, no memset node). */
+int vap_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Synchronise `stream` and read the sticky VAP_DERR_* bits of a workspace into *err_out;
+ * clear them afterwards when `clear` is nonzero. */
+int vap_get_device_error(void* workspace, void* stream, int32_t* err_out, int clear);
+
+/* Static text for a VAP_* return code. */
+const char* vap_strerror(int code);
+
+/* Detail of the calling thread's last host-side error ("" if none). */
+const char* vap_last_error_message(void);
+
+/* ---- measurement helpers (not part of the step) ------------------------------------------ */
+
+/* Kernel timer.  While enabled, every paged_attn_step records a hipEvent pair around its
+ * attention kernel (kind 0) and every spec_verify around its kernel (kind 1), on the caller's
+ * stream, into a ring of 4096 pairs per kind.  vap_timer_read synchronises on the recorded
+ * events, returns the summed milliseconds and the number of pairs, and resets the ring when
+ * `reset` is nonzero. */
+int vap_timer_enable(int on);
+int vap_timer_read(int kind, double* total_ms, int32_t* count, int reset);
+
+/* Plain streaming copy kernel (16-byte loads and stores) of `bytes` (a multiple of 16) from
+ * src to dst on `stream`; used to measure the achievable HBM copy rate and to calibrate the
+ * hardware byte counters. */
+int vap_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Number of compute units of the current device and its gfx arch name ("gfx950"). */
+int vap_device_info(int32_t* num_cus, char* arch_name, size_t arch_name_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VAP_H_ */

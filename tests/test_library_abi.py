@@ -1,0 +1,87 @@
+"""The C-ABI library loads, exports every symbol include/vap.h declares, and rejects bad
+arguments on the host before touching a device (CPU only; no kernel is launched)."""
+
+import ctypes
+import os
+
+import pytest
+
+import verify_attention_paged_amd as vap
+from verify_attention_paged_amd import _binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vap.LIB_PATH):
+        from verify_attention_paged_amd.build import build
+        build()
+    return vap.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = vap.header_functions()
+    assert {"paged_attn_step", "spec_verify", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
+            "vap_get_device_error", "vap_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_strerror_and_codes(lib):
+    assert lib.vap_strerror(0) == b"ok"
+    assert lib.vap_strerror(-2) == b"workspace too small"
+    assert lib.vap_strerror(-99) == b"unknown error"
+
+
+def _shape(**kw):
+    base = dict(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                num_blocks=35, max_blocks_per_seq=16, total_q=4, scale=0.0)
+    base.update(kw)
+    return vap.AttnShape(**base)
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(block_size=8), dict(num_q_heads=6, num_kv_heads=4),
+                                 dict(num_seqs=-1), dict(num_seqs=9000), dict(total_q=-1),
+                                 dict(num_blocks=0), dict(scale=float("nan")), dict(scale=-1.0),
+                                 dict(num_kv_heads=0)])
+def test_attention_shape_rejected_on_host(lib, bad):
+    s = _shape(**bad)
+    assert lib.vap_attn_workspace_min_bytes(ctypes.byref(s)) == 0
+    rc = lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(s), None, 0, None)
+    assert rc == B.VAP_EINVAL
+    assert lib.vap_last_error_message()
+
+
+def test_attention_null_pointers_and_empty_batch(lib):
+    s = _shape()
+    assert lib.paged_attn_step(None, None, None, None, None, None, None, None, 0, None) == B.VAP_EINVAL
+    assert lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(s), None, 0, None) == B.VAP_EINVAL
+    empty = _shape(num_seqs=0, total_q=0)
+    assert lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
+    bad_empty = _shape(num_seqs=0, total_q=3)
+    assert lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(bad_empty), None, 0, None) == B.VAP_EINVAL
+
+
+def test_workspace_sizes_are_consistent(lib):
+    s = _shape(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, num_blocks=6000,
+               max_blocks_per_seq=512, total_q=64)
+    lo = lib.vap_attn_workspace_min_bytes(ctypes.byref(s))
+    hi = lib.vap_attn_workspace_bytes(ctypes.byref(s))
+    assert 0 < lo < hi and lo % 256 == 0 and hi % 256 == 0
+    assert lib.vap_verify_workspace_bytes(16, 4, 128256) > 0
+    assert lib.vap_verify_workspace_bytes(16, 65, 100) == 0
+    assert lib.vap_verify_workspace_bytes(-1, 4, 100) == 0
+
+
+def test_verify_rejected_on_host(lib):
+    assert lib.spec_verify(None, None, None, None, None, None, 4, 65, 10, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify(None, None, None, None, None, None, 4, 4, 0, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify(None, None, None, None, None, None, 4, 4, 10, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify(None, None, None, None, None, None, 0, 4, 10, None, 0, None) == B.VAP_OK
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(4, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vap.paged_attn_step(q, q, q, q, q)

@@ -1,0 +1,35 @@
+"""Paged decode/verify attention and speculative verification for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of ``include/vap.h``
+(``lib/libvap.so``); this package is the thin Python binding over it.  PyTorch supplies device
+memory and streams only.
+
+    paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale=0.0)
+    spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None)
+"""
+
+from ._binding import (  # noqa: F401
+    AttnShape,
+    VapError,
+    LIB_PATH,
+    DERR_BLOCK_ID,
+    DERR_LENS,
+    DERR_TOTAL_Q,
+    DERR_DRAFT_ID,
+    DERR_EMPTY_ROW,
+    TIMER_ATTENTION,
+    TIMER_VERIFY,
+    attn_shape,
+    attn_workspace,
+    device_info,
+    get_device_error,
+    header_functions,
+    load_library,
+    paged_attn_step,
+    spec_verify,
+    stream_copy,
+    timer_enable,
+    timer_read,
+    verify_workspace,
+    workspace_init,
+)

@@ -1,0 +1,266 @@
+"""ctypes binding of the C ABI in include/vap.h (argument marshalling only).
+
+Every computation runs in the HIP library ``lib/libvap.so``; this module checks tensor
+dtypes, devices and shapes, passes ``data_ptr()`` values and torch's current HIP stream, and
+turns negative return codes into ``VapError``.  There is no fallback: if the library is
+missing or the device is not gfx950, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libvap.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vap.h")
+
+VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
+DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW = 0x1, 0x2, 0x4, 0x8, 0x10
+TIMER_ATTENTION, TIMER_VERIFY = 0, 1
+
+
+class VapError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} (code {code})")
+        self.code = code
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+_vp, _sz, _i32, _pi32, _pdbl = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+_pshape = ctypes.POINTER(AttnShape)
+
+SIGNATURES = {
+    "vap_attn_workspace_bytes": (_sz, [_pshape]),
+    "vap_attn_workspace_min_bytes": (_sz, [_pshape]),
+    "paged_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
+    "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "vap_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
+    "vap_get_device_error": (ctypes.c_int, [_vp, _vp, _pi32, ctypes.c_int]),
+    "vap_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "vap_last_error_message": (ctypes.c_char_p, []),
+    "vap_timer_enable": (ctypes.c_int, [ctypes.c_int]),
+    "vap_timer_read": (ctypes.c_int, [ctypes.c_int, _pdbl, _pi32, ctypes.c_int]),
+    "vap_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "vap_device_info": (ctypes.c_int, [_pi32, ctypes.c_char_p, _sz]),
+}
+
+_lib = None
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions declared in include/vap.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libvap.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise VapError(VAP_ENODEV, f"HIP library {path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != VAP_OK:
+        lib = load_library()
+        msg = lib.vap_last_error_message().decode() or lib.vap_strerror(rc).decode()
+        raise VapError(rc, msg)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------------------
+
+def attn_shape(q: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
+               scale: float = 0.0) -> AttnShape:
+    T, Hq, D = q.shape
+    two, NB, BS, Hkv, D2 = kv_pool.shape
+    B, MB = block_tables.shape
+    if two != 2 or D2 != D:
+        raise ValueError(f"kv_pool must be [2, num_blocks, block_size, Hkv, {D}], got {tuple(kv_pool.shape)}")
+    return AttnShape(B, Hq, Hkv, D, BS, NB, MB, T, float(scale))
+
+
+def attn_workspace(shape: AttnShape, device=None) -> torch.Tensor:
+    """Zero-filled device workspace sized for ``shape`` on ``device``."""
+    lib = load_library()
+    device = torch.device(device or "cuda")
+    with torch.cuda.device(device):
+        n = lib.vap_attn_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        _check(VAP_EINVAL)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale: float = 0.0,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Paged attention for one ragged batch; see ``paged_attn_step`` in include/vap.h.
+
+    q bf16 [T, Hq, D]; kv_pool bf16 [2, NB, bs, Hkv, D]; block_tables int32 [B, MB];
+    ctx_lens, q_lens int32 [B]; returns out fp32 [T, Hq, D].
+    """
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 5, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    _need(q_lens, "q_lens", torch.int32, 1, dev)
+    shape = attn_shape(q, kv_pool, block_tables, scale)
+    if ctx_lens.numel() != shape.num_seqs or q_lens.numel() != shape.num_seqs:
+        raise ValueError("ctx_lens and q_lens need one entry per block-table row")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = attn_workspace(shape, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.paged_attn_step(q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),
+                                 ctx_lens.data_ptr(), q_lens.data_ptr(), out.data_ptr(),
+                                 ctypes.byref(shape), workspace.data_ptr(), workspace.numel(),
+                                 _stream(stream))
+    _check(rc)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# speculative verification
+# ---------------------------------------------------------------------------------------
+
+def verify_workspace(num_seqs: int, k: int, vocab: int, device=None) -> torch.Tensor:
+    lib = load_library()
+    n = lib.vap_verify_workspace_bytes(num_seqs, k, vocab)
+    if n == 0:
+        _check(VAP_EINVAL)
+    return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
+
+
+def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Modified rejection sampling; see ``spec_verify`` in include/vap.h.
+
+    p fp32 [B, k+1, V]; q fp32 [B, k, V]; draft_ids int32 [B, k]; uniforms fp32 [B, k+1].
+    Returns (out_ids int32 [B, k+1], n_accepted int32 [B]).
+    """
+    lib = load_library()
+    dev = p.device
+    _need(p, "p", torch.float32, 3)
+    B, k1, V = p.shape
+    k = k1 - 1
+    _need(uniforms, "uniforms", torch.float32, 2, dev)
+    if tuple(uniforms.shape) != (B, k + 1):
+        raise ValueError("uniforms must be [B, k+1]")
+    if k > 0:
+        _need(q, "q", torch.float32, 3, dev)
+        _need(draft_ids, "draft_ids", torch.int32, 2, dev)
+        if tuple(q.shape) != (B, k, V) or tuple(draft_ids.shape) != (B, k):
+            raise ValueError("q must be [B, k, V] and draft_ids [B, k]")
+    if out_ids is None:
+        out_ids = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_ids, "out_ids", torch.int32, 2, dev)
+    _need(n_accepted, "n_accepted", torch.int32, 1, dev)
+    if workspace is None:
+        workspace = verify_workspace(B, k, V, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    qp = q.data_ptr() if k > 0 else None
+    ip = draft_ids.data_ptr() if k > 0 else None
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify(p.data_ptr(), qp, ip, uniforms.data_ptr(), out_ids.data_ptr(),
+                             n_accepted.data_ptr(), B, k, V, workspace.data_ptr(),
+                             workspace.numel(), _stream(stream))
+    _check(rc)
+    return out_ids, n_accepted
+
+
+# ---------------------------------------------------------------------------------------
+# workspace, errors, measurement helpers
+# ---------------------------------------------------------------------------------------
+
+def workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check(load_library().vap_workspace_init(workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def get_device_error(workspace: torch.Tensor, stream=None, clear: bool = False) -> int:
+    err = ctypes.c_int32(0)
+    with torch.cuda.device(workspace.device):
+        _check(load_library().vap_get_device_error(workspace.data_ptr(), _stream(stream),
+                                                   ctypes.byref(err), int(clear)))
+    return int(err.value)
+
+
+def timer_enable(on: bool = True) -> None:
+    _check(load_library().vap_timer_enable(int(on)))
+
+
+def timer_read(kind: int, reset: bool = True):
+    """(summed milliseconds, number of recorded kernels) of timer `kind`."""
+    total = ctypes.c_double(0.0)
+    count = ctypes.c_int32(0)
+    _check(load_library().vap_timer_read(kind, ctypes.byref(total), ctypes.byref(count), int(reset)))
+    return total.value, int(count.value)
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ValueError("dst smaller than src")
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().vap_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
+
+
+def device_info():
+    n = ctypes.c_int32(0)
+    buf = ctypes.create_string_buffer(64)
+    _check(load_library().vap_device_info(ctypes.byref(n), buf, 64))
+    return int(n.value), buf.value.decode()

@@ -1,0 +1,380 @@
+// Host side of the C ABI declared in include/vap.h: argument validation, workspace carving,
+// kernel dispatch, error reporting and the measurement helpers.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "vap_internal.h"
+
+namespace {
+
+using namespace vap;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return VAP_OK;
+}
+
+// ---- per-device facts ------------------------------------------------------------------
+
+struct DevInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+  char arch[64] = {0};
+  int attn_occ[2][2][2] = {};   // workgroups per CU of the attention kernel [D128][BS32][NRT2]
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DevInfo g_dev[kMaxDevices];
+
+const DevInfo* device_info() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return nullptr;
+    d.num_cus = prop.multiProcessorCount;
+    std::strncpy(d.arch, prop.gcnArchName, sizeof(d.arch) - 1);
+    d.gfx950 = std::strncmp(d.arch, "gfx950", 6) == 0;
+    for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < 2; ++b)
+        for (int c = 0; c < 2; ++c) {
+          int nb = 0;
+          const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1);
+          if (f == nullptr ||
+              hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads, 0) != hipSuccess || nb < 1)
+            nb = 1;
+          d.attn_occ[a][b][c] = nb;
+        }
+    d.probed = true;
+  }
+  return &d;
+}
+
+// ---- kernel timer ------------------------------------------------------------------------
+
+constexpr int kTimerSlots = 4096;
+struct Timer {
+  bool on = false;
+  bool created = false;
+  hipEvent_t start[2][kTimerSlots];
+  hipEvent_t stop[2][kTimerSlots];
+  int count[2] = {0, 0};
+};
+Timer g_timer;
+
+void timer_begin(int kind, hipStream_t stream) {
+  if (!g_timer.on || g_timer.count[kind] >= kTimerSlots) return;
+  (void)hipEventRecord(g_timer.start[kind][g_timer.count[kind]], stream);
+}
+
+void timer_end(int kind, hipStream_t stream) {
+  if (!g_timer.on || g_timer.count[kind] >= kTimerSlots) return;
+  (void)hipEventRecord(g_timer.stop[kind][g_timer.count[kind]], stream);
+  ++g_timer.count[kind];
+}
+
+// ---- attention shape checks ---------------------------------------------------------------
+
+struct AttnPlanChoice {
+  int D, BS, NRT, RG, G;
+};
+
+int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
+  if (s == nullptr) return fail(VAP_EINVAL, "shape is NULL");
+  if (s->num_seqs < 0 || s->num_seqs > kMaxSeqs)
+    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %d]", s->num_seqs, kMaxSeqs);
+  if (s->num_kv_heads < 1 || s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads)
+    return fail(VAP_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(VAP_EINVAL, "head_dim=%d not supported (64 or 128)", s->head_dim);
+  if (s->block_size != 16 && s->block_size != 32)
+    return fail(VAP_EINVAL, "block_size=%d not supported (16 or 32)", s->block_size);
+  if (s->num_blocks < 1 || s->max_blocks_per_seq < 1)
+    return fail(VAP_EINVAL, "num_blocks=%d and max_blocks_per_seq=%d must be >= 1", s->num_blocks,
+                s->max_blocks_per_seq);
+  if (s->total_q < 0) return fail(VAP_EINVAL, "total_q=%d < 0", s->total_q);
+  if (!(std::isfinite(s->scale) && s->scale >= 0.f)) return fail(VAP_EINVAL, "scale must be finite and >= 0");
+  c->D = s->head_dim;
+  c->BS = s->block_size;
+  c->G = s->num_q_heads / s->num_kv_heads;
+  // decode-only batches (one row per sequence) with at most 16 rows per KV head use one
+  // 16-row MFMA tile per unit; everything else uses two (32 rows per unit)
+  c->NRT = (s->total_q == s->num_seqs && c->G <= 16) ? 1 : 2;
+  c->RG = 16 * c->NRT;
+  const long long cap = (long long)s->max_blocks_per_seq * s->block_size;
+  if (cap * s->num_q_heads >= (1LL << 31))
+    return fail(VAP_EINVAL, "max_blocks_per_seq*block_size*num_q_heads exceeds 2^31");
+  if ((long long)s->total_q * s->num_q_heads >= (1LL << 31))
+    return fail(VAP_EINVAL, "total_q*num_q_heads exceeds 2^31");
+  const long long rows_groups = ((long long)c->G * s->total_q + c->RG - 1) / c->RG + s->num_seqs;
+  if ((long long)s->num_kv_heads * s->max_blocks_per_seq * rows_groups >= (1LL << 31) - 1)
+    return fail(VAP_EINVAL, "work of the step may exceed 2^31 blocks");
+  return VAP_OK;
+}
+
+int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
+  const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2];
+  return d->num_cus * occ * kWavesPerWG;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vap_strerror(int code) {
+  switch (code) {
+    case VAP_OK: return "ok";
+    case VAP_EINVAL: return "invalid argument";
+    case VAP_ENOSPC: return "workspace too small";
+    case VAP_EHIP: return "HIP runtime error";
+    case VAP_ENODEV: return "no gfx950 device is current";
+    default: return "unknown error";
+  }
+}
+
+const char* vap_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t vap_attn_workspace_bytes(const vap_attn_shape* shape) {
+  AttnPlanChoice c;
+  if (check_attn_shape(shape, &c) != VAP_OK) return 0;
+  const DevInfo* d = device_info();
+  const int W = d ? worker_waves(d, c) : 256 * kWavesPerWG * 2;
+  return attn_layout(shape->num_seqs, W, c.RG, c.D).total;
+}
+
+size_t vap_attn_workspace_min_bytes(const vap_attn_shape* shape) {
+  AttnPlanChoice c;
+  if (check_attn_shape(shape, &c) != VAP_OK) return 0;
+  return attn_layout(shape->num_seqs, kWavesPerWG, c.RG, c.D).total;
+}
+
+int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tables,
+                    const int32_t* ctx_lens, const int32_t* q_lens, float* out,
+                    const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
+                    void* stream_) {
+  AttnPlanChoice c;
+  int rc = check_attn_shape(shape, &c);
+  if (rc != VAP_OK) return rc;
+  const vap_attn_shape& s = *shape;
+  if (s.num_seqs == 0) {
+    if (s.total_q != 0) return fail(VAP_EINVAL, "num_seqs=0 but total_q=%d", s.total_q);
+    return ok();
+  }
+  if (!q || !kv_pool || !block_tables || !ctx_lens || !q_lens || !out || !workspace)
+    return fail(VAP_EINVAL, "NULL data pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv_pool) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(VAP_EINVAL, "q, kv_pool, out and workspace must be 16-byte aligned");
+  const DevInfo* d = device_info();
+  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+
+  // worker waves: as many as stay resident, fewer if the workspace is smaller
+  int W = worker_waves(d, c);
+  if (attn_layout(s.num_seqs, W, c.RG, c.D).total > workspace_bytes) {
+    int lo = kWavesPerWG, hi = W;
+    if (attn_layout(s.num_seqs, lo, c.RG, c.D).total > workspace_bytes)
+      return fail(VAP_ENOSPC, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
+                  attn_layout(s.num_seqs, lo, c.RG, c.D).total);
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (attn_layout(s.num_seqs, mid, c.RG, c.D).total <= workspace_bytes) lo = mid; else hi = mid - 1;
+    }
+    W = lo;
+  }
+  W = (W / kWavesPerWG) * kWavesPerWG;
+  const AttnLayout lay = attn_layout(s.num_seqs, W, c.RG, c.D);
+  char* ws = static_cast<char*>(workspace);
+
+  AttnParams P;
+  P.q = static_cast<const uint16_t*>(q);
+  P.kpool = static_cast<const uint16_t*>(kv_pool);
+  P.vpool = P.kpool + (size_t)s.num_blocks * s.block_size * s.num_kv_heads * s.head_dim;
+  P.tables = block_tables;
+  P.ctx_lens = ctx_lens;
+  P.q_lens = q_lens;
+  P.out = out;
+  P.B = s.num_seqs;
+  P.Hq = s.num_q_heads;
+  P.Hkv = s.num_kv_heads;
+  P.G = c.G;
+  P.num_blocks = s.num_blocks;
+  P.MB = s.max_blocks_per_seq;
+  P.total_q = s.total_q;
+  P.W = W;
+  P.RG = c.RG;
+  P.BS = c.BS;
+  const float scale = s.scale > 0.f ? s.scale : 1.0f / std::sqrt((float)s.head_dim);
+  P.scale_log2 = scale * 1.4426950408889634f;
+  P.hdr = reinterpret_cast<AttnHeader*>(ws);
+  P.q_off = reinterpret_cast<int32_t*>(ws + lay.q_off);
+  P.nblk = reinterpret_cast<int32_t*>(ws + lay.nblk);
+  P.n_rg = reinterpret_cast<int32_t*>(ws + lay.n_rg);
+  P.seq_off = reinterpret_cast<int32_t*>(ws + lay.seq_off);
+  P.wave_seq = reinterpret_cast<int32_t*>(ws + lay.wave_seq);
+  P.desc = reinterpret_cast<int4*>(ws + lay.desc);
+  P.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
+  P.part_acc = reinterpret_cast<float*>(ws + lay.part_acc);
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  hipError_t e = launch_attn_plan(P, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
+  timer_begin(0, stream);
+  e = launch_attn_main(P, c.D, c.BS, c.NRT, W / kWavesPerWG, stream);
+  timer_end(0, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
+  e = launch_attn_reduce(P, c.D, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs || k < 0 || k > 64 || vocab < 1) return 0;
+  return verify_bytes(num_seqs);
+}
+
+int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
+                int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
+                void* workspace, size_t workspace_bytes, void* stream_) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs)
+    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
+  if (k < 0 || k > 64) return fail(VAP_EINVAL, "k=%d outside [0, 64]", k);
+  if (vocab < 1) return fail(VAP_EINVAL, "vocab=%d < 1", vocab);
+  if (num_seqs == 0) return ok();
+  if (!p || !uniforms || !out_ids || !n_accepted || !workspace || (k > 0 && (!q || !draft_ids)))
+    return fail(VAP_EINVAL, "NULL data pointer");
+  if (workspace_bytes < vap_verify_workspace_bytes(num_seqs, k, vocab))
+    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes,
+                vap_verify_workspace_bytes(num_seqs, k, vocab));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
+  const DevInfo* d = device_info();
+  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+
+  // chunks per row: about two workgroups per CU over the whole batch, at least 256 elements
+  // per chunk, at most 256 chunks
+  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
+  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
+  C = std::max(1LL, std::min(C, cmax));
+  long long CS = ((long long)vocab + C - 1) / C;
+  CS = (CS + 3) / 4 * 4;
+  C = ((long long)vocab + CS - 1) / CS;
+
+  char* ws = static_cast<char*>(workspace);
+  VerifyParams P;
+  P.p = p;
+  P.q = q;
+  P.draft_ids = draft_ids;
+  P.uniforms = uniforms;
+  P.out_ids = out_ids;
+  P.n_accepted = n_accepted;
+  P.B = num_seqs;
+  P.k = k;
+  P.V = vocab;
+  P.C = (int)C;
+  P.CS = (int)CS;
+  P.err = reinterpret_cast<int32_t*>(ws);
+  P.tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
+  P.chunk_sums = reinterpret_cast<double*>(ws + 256);
+  const bool vec4 = (vocab % 4 == 0) &&
+                    ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(k ? q : p)) & 15) == 0;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  timer_begin(1, stream);
+  hipError_t e = launch_spec_verify(P, vec4, stream);
+  timer_end(1, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int vap_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return fail(VAP_EINVAL, "NULL workspace");
+  if (bytes == 0) return ok();
+  const hipError_t e = launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VAP_EHIP, "fill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int vap_get_device_error(void* workspace, void* stream_, int32_t* err_out, int clear) {
+  if (!workspace || !err_out) return fail(VAP_EINVAL, "NULL pointer");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(err_out, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    e = launch_fill_zero(workspace, sizeof(int32_t), stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  }
+  if (e != hipSuccess) return fail(VAP_EHIP, "reading the error word: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int vap_timer_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (on && !g_timer.created) {
+    for (int k = 0; k < 2; ++k)
+      for (int i = 0; i < kTimerSlots; ++i) {
+        if (hipEventCreate(&g_timer.start[k][i]) != hipSuccess || hipEventCreate(&g_timer.stop[k][i]) != hipSuccess)
+          return fail(VAP_EHIP, "hipEventCreate failed");
+      }
+    g_timer.created = true;
+  }
+  g_timer.on = on != 0;
+  return ok();
+}
+
+int vap_timer_read(int kind, double* total_ms, int32_t* count, int reset) {
+  if (kind < 0 || kind > 1 || !total_ms || !count) return fail(VAP_EINVAL, "bad timer arguments");
+  double sum = 0.0;
+  const int n = g_timer.count[kind];
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timer.stop[kind][i]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.start[kind][i], g_timer.stop[kind][i]) != hipSuccess)
+      return fail(VAP_EHIP, "reading timer events failed");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *count = n;
+  if (reset) g_timer.count[kind] = 0;
+  return ok();
+}
+
+int vap_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return fail(VAP_EINVAL, "NULL pointer");
+  if ((bytes & 15) || ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15))
+    return fail(VAP_EINVAL, "bytes and pointers must be multiples of 16");
+  const hipError_t e = launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VAP_EHIP, "copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int vap_device_info(int32_t* num_cus, char* arch_name, size_t arch_name_len) {
+  const DevInfo* d = device_info();
+  if (d == nullptr) return fail(VAP_ENODEV, "no current HIP device");
+  if (num_cus) *num_cus = d->num_cus;
+  if (arch_name && arch_name_len) {
+    std::strncpy(arch_name, d->arch, arch_name_len - 1);
+    arch_name[arch_name_len - 1] = 0;
+  }
+  return ok();
+}
+
+}  // extern "C"

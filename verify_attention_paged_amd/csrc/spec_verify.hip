@@ -1,0 +1,273 @@
+// Speculative-decoding verification kernel (gfx950).
+//
+// What is computed, per sequence b (neuralmasteryai.com "Continuous Batching & Speculative
+// Decoding", section "The Modified Rejection Sampling Algorithm"; syslabs.in "Continuous
+// Batching and Speculative Decoding: How Modern LLM Serving Engines Actually Work", section
+// "The core idea"):
+//   1. accept test: draft x_i passes when p_i(x_i) > 0 and r_i * q_i(x_i) <= p_i(x_i) (the exact
+//      form of r_i <= min(1, p/q), evaluated in fp64 where the product of two fp32 values is
+//      exact); n = index of the first failure, or k;
+//   2. the row to draw from: w = max(0, p_n - q_n) when n < k, else the bonus row w = p_k;
+//   3. Z = sum(w) and running sums C_x in fp64;
+//   4. t = u_k * Z and the emitted token is the smallest x with C_x > t;
+//   5. out_ids = accepted drafts, the emitted token, then -1; n_accepted = n.
+//
+// How: one launch, one workgroup per (sequence, vocabulary chunk).  Every workgroup redoes the k gathers of
+// step 1 (2k scattered loads, cheaper than a second launch), streams its chunk of the row it
+// needs with 16-byte loads, and publishes the chunk's fp64 sum.  An arrival counter per
+// sequence elects the last workgroup, which scans the C chunk sums, finds the chunk that
+// holds t and rescans only that chunk to pick the token.  The counter returns to 0, so the
+// workspace is ready for the next call.  All bytes of the vocabulary are read once, in
+// parallel over about 2 x (number of CUs) workgroups.
+#include "vap_internal.h"
+
+namespace vap {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ double residual_or_p(float p, float q, bool residual) {
+  const double d = residual ? (double)p - (double)q : (double)p;
+  return residual ? fmax(0.0, d) : d;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+// Fixed-order workgroup sum (same tree every time).
+__device__ __forceinline__ double block_sum(double x, double* s_red) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  x = wave_sum(x);
+  if (lane == 0) s_red[wv] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) t += s_red[i];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive workgroup scan of one double per thread; `total` gets the sum.
+__device__ __forceinline__ double block_exclusive_scan(double x, double* s_red, double& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  double incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_red[wv] = incl;
+  __syncthreads();
+  double before = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    if (i < wv) before += s_red[i];
+    total += s_red[i];
+  }
+  __syncthreads();
+  return before + incl - x;
+}
+
+__device__ __forceinline__ int block_min(int x, int* s_int) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = min(x, __shfl_xor(x, d));
+  if (lane == 0) s_int[wv] = x;
+  __syncthreads();
+  int t = s_int[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) t = min(t, s_int[i]);
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ int block_max(int x, int* s_int) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, __shfl_xor(x, d));
+  if (lane == 0) s_int[wv] = x;
+  __syncthreads();
+  int t = s_int[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) t = max(t, s_int[i]);
+  __syncthreads();
+  return t;
+}
+
+// Sum of w over [x0, x1) with coalesced loads (thread-strided).
+template <bool VEC4>
+__device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, bool residual,
+                                                int x0, int x1) {
+  double acc = 0.0;
+  if (VEC4) {
+    for (int x = x0 + 4 * threadIdx.x; x < x1; x += 4 * kThreads) {
+      const float4 pv = *reinterpret_cast<const float4*>(prow + x);
+      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (residual) qv = *reinterpret_cast<const float4*>(qrow + x);
+      acc += residual_or_p(pv.x, qv.x, residual) + residual_or_p(pv.y, qv.y, residual) +
+             residual_or_p(pv.z, qv.z, residual) + residual_or_p(pv.w, qv.w, residual);
+    }
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) {
+      acc += residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
+    }
+  }
+  return acc;
+}
+
+// Smallest x in chunk [x0, x1) whose running sum base + C exceeds t (INT_MAX if none), with
+// the running sum taken in ascending token id; also the largest x with w_x > 0 (-1 if none).
+__device__ __forceinline__ void chunk_select(const float* prow, const float* qrow, bool residual,
+                                             int x0, int x1, double base, double t,
+                                             double* s_red, int* s_int, int& first_above,
+                                             int& last_positive) {
+  const int len = x1 - x0;
+  const int per = (len + kThreads - 1) / kThreads;
+  const int a = x0 + min(len, threadIdx.x * per);
+  const int b = x0 + min(len, (threadIdx.x + 1) * per);
+  double mine = 0.0;
+  int lastpos = -1;
+  for (int x = a; x < b; ++x) {
+    const double wx = residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
+    mine += wx;
+    if (wx > 0.0) lastpos = x;
+  }
+  double total;
+  const double before = block_exclusive_scan(mine, s_red, total);
+  double run = base + before;
+  int found = INT_MAX;
+  for (int x = a; x < b; ++x) {
+    run += residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
+    if (run > t) { found = x; break; }
+  }
+  first_above = block_min(found, s_int);
+  last_positive = block_max(lastpos, s_int);
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParams P) {
+  __shared__ int s_n;
+  __shared__ int s_last;
+  __shared__ double s_red[kThreads / 64];
+  __shared__ int s_int[kThreads / 64];
+  __shared__ double s_cs[kThreads];
+
+  const int C = P.C;
+  const int b = blockIdx.x / C;
+  const int cidx = blockIdx.x - b * C;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int k = P.k, V = P.V;
+
+  // 1. accept tests (first wave; k <= 64)
+  if (tid < 64) {
+    bool reject = false;
+    if (lane < k) {
+      const int x = P.draft_ids[(long long)b * k + lane];
+      const bool inside = x >= 0 && x < V;
+      float pv = 0.f, qv = 0.f;
+      if (inside) {
+        pv = P.p[((long long)b * (k + 1) + lane) * V + x];
+        qv = P.q[((long long)b * k + lane) * V + x];
+      } else if (cidx == 0) {
+        atomicOr(P.err, VAP_DERR_DRAFT_ID);
+      }
+      const double r = (double)P.uniforms[(long long)b * (k + 1) + lane];
+      reject = !(pv > 0.f && r * (double)qv <= (double)pv);
+    }
+    const unsigned long long m = __ballot(reject);
+    if (lane == 0) s_n = m ? (__ffsll((long long)m) - 1) : k;
+  }
+  __syncthreads();
+  const int n = s_n;
+  const bool residual = n < k;
+  const float* prow = P.p + ((long long)b * (k + 1) + n) * V;
+  const float* qrow = residual ? P.q + ((long long)b * k + n) * V : prow;
+
+  // 2-3. this chunk's sum of w
+  const int x0 = cidx * P.CS;
+  const int x1 = min(V, x0 + P.CS);
+  double part = block_sum(chunk_partial<VEC4>(prow, qrow, residual, x0, x1), s_red);
+  if (tid == 0) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + cidx,
+                       (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (ticket == C - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // 4. last workgroup of sequence b: locate t among the chunk sums, then inside one chunk
+  if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  double cs = 0.0;
+  if (tid < C) {
+    cs = __longlong_as_double((long long)__hip_atomic_load(
+        reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + tid,
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  bool use_res = residual;
+  const float* srow_q = qrow;
+  double Z;
+  double before = block_exclusive_scan(cs, s_red, Z);
+  if (!(Z > 0.0)) {
+    // empty residual: draw from p_n itself (recompute its chunk sums here)
+    use_res = false;
+    srow_q = prow;
+    for (int j = 0; j < C; ++j) {
+      const int a = j * P.CS, e = min(V, a + P.CS);
+      const double sj = block_sum(chunk_partial<VEC4>(prow, prow, false, a, e), s_red);
+      if (tid == j) cs = sj;
+    }
+    before = block_exclusive_scan(cs, s_red, Z);
+  }
+  int token = 0;
+  if (Z > 0.0) {
+    const double t = (double)P.uniforms[(long long)b * (k + 1) + k] * Z;
+    // first chunk whose inclusive running sum exceeds t
+    const int cand = (tid < C && before + cs > t) ? tid : INT_MAX;
+    int cstar = block_min(cand, s_int);
+    const int lastnz = block_max((tid < C && cs > 0.0) ? tid : -1, s_int);
+    if (cstar == INT_MAX) cstar = lastnz;   // rounding left t at or above the total
+    if (tid == cstar) s_cs[0] = before;
+    __syncthreads();
+    const double base = s_cs[0];
+    __syncthreads();
+    const int a = cstar * P.CS, e = min(V, a + P.CS);
+    int first_above, last_positive;
+    chunk_select(prow, srow_q, use_res, a, e, base, t, s_red, s_int, first_above, last_positive);
+    token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
+  } else if (tid == 0) {
+    atomicOr(P.err, VAP_DERR_EMPTY_ROW);
+  }
+
+  // 5. outputs
+  if (tid <= k) {
+    int v;
+    if (tid < n) v = P.draft_ids[(long long)b * k + tid];
+    else if (tid == n) v = token;
+    else v = -1;
+    P.out_ids[(long long)b * (k + 1) + tid] = v;
+  }
+  if (tid == 0) P.n_accepted[b] = n;
+}
+
+}  // namespace
+
+hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.C * p.B));
+  if (vec4) {
+    hipLaunchKernelGGL(spec_verify_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(spec_verify_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vap

@@ -1,0 +1,123 @@
+// Internal declarations shared by the HIP sources of the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vap.h"
+
+namespace vap {
+
+constexpr int kMaxSeqs = 8192;      // plan kernel keeps per-sequence work offsets in LDS
+constexpr int kPlanThreads = 1024;
+constexpr int kAttnThreads = 256;   // 4 independent worker waves per workgroup
+constexpr int kWavesPerWG = kAttnThreads / 64;
+constexpr int kTokTile = 32;        // tokens per inner iteration (two 16-token MFMA tiles)
+
+// ---------------------------------------------------------------------------------------
+// Attention workspace layout (all offsets 256-byte aligned).
+//   header   : err word, total work blocks
+//   q_off    : int32 [B]   first packed row of each sequence
+//   nblk     : int32 [B]   KV blocks of each sequence (0 = sequence skipped as invalid)
+//   n_rg     : int32 [B]   row groups of each sequence (G * q_len rows, RG per group)
+//   seq_off  : int32 [B+1] exclusive prefix of per-sequence work (blocks x row groups x Hkv)
+//   wave_seq : int32 [W]   sequence holding each worker wave's first work block
+//   desc     : int4  [W]   split-merge descriptor written by each worker wave
+//   part_ml  : float2 [W][2][RG]       (running max in log2 units, running sum) per row
+//   part_acc : float  [W][2][RG][D]    unnormalised output per row
+// ---------------------------------------------------------------------------------------
+struct AttnHeader {
+  int32_t err;
+  int32_t pad0;
+  int32_t total_work;   // TB: total work blocks of the step
+  int32_t pad1;
+};
+
+struct AttnLayout {
+  size_t q_off, nblk, n_rg, seq_off, wave_seq, desc, part_ml, part_acc, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline AttnLayout attn_layout(int B, int W, int RG, int D) {
+  AttnLayout L;
+  size_t o = align256(sizeof(AttnHeader));
+  L.q_off = o;    o = align256(o + size_t(B) * 4);
+  L.nblk = o;     o = align256(o + size_t(B) * 4);
+  L.n_rg = o;     o = align256(o + size_t(B) * 4);
+  L.seq_off = o;  o = align256(o + size_t(B + 1) * 4);
+  L.wave_seq = o; o = align256(o + size_t(W) * 4);
+  L.desc = o;     o = align256(o + size_t(W) * 16);
+  L.part_ml = o;  o = align256(o + size_t(W) * 2 * RG * 8);
+  L.part_acc = o; o = align256(o + size_t(W) * 2 * RG * D * 4);
+  L.total = o;
+  return L;
+}
+
+struct AttnParams {
+  const uint16_t* q;        // bf16 [T][Hq][D]
+  const uint16_t* kpool;    // bf16 [NB][BS][Hkv][D]
+  const uint16_t* vpool;    // bf16 [NB][BS][Hkv][D]
+  const int32_t* tables;    // [B][MB]
+  const int32_t* ctx_lens;  // [B]
+  const int32_t* q_lens;    // [B]
+  float* out;               // fp32 [T][Hq][D]
+  int32_t B, Hq, Hkv, G, num_blocks, MB, total_q;
+  int32_t W;                // worker waves
+  int32_t RG;               // rows per unit (16 * row tiles)
+  int32_t BS;               // block size (plan kernel only; the attention kernel templates it)
+  float scale_log2;         // softmax scale * log2(e)
+  AttnHeader* hdr;
+  int32_t* q_off;
+  int32_t* nblk;
+  int32_t* n_rg;
+  int32_t* seq_off;
+  int32_t* wave_seq;
+  int4* desc;
+  float2* part_ml;
+  float* part_acc;
+};
+
+// ---------------------------------------------------------------------------------------
+// Verification workspace layout.
+//   [0, 256)            header: err word
+//   [256, ...)          chunk_sums: double [B][C], per-chunk residual / bonus row sums
+//   [..., end)          tickets: int32, ticket of sequence b at end - 4*(b+1) (growing down
+//                       from the end, so its place does not depend on B).  Arrival counters
+//                       return to 0 at the end of every call.  Because every call checks
+//                       bytes >= 256 + B*(256*8 + 4), a call's tickets never overlap the chunk
+//                       sums an earlier call (any B) left behind.
+// ---------------------------------------------------------------------------------------
+constexpr int kMaxChunks = 256;
+constexpr long long kMaxVerifySeqs = 1LL << 22;
+
+inline size_t verify_bytes(long long B) {
+  return align256(256 + (size_t)B * (kMaxChunks * 8 + 4));
+}
+
+struct VerifyParams {
+  const float* p;
+  const float* q;
+  const int32_t* draft_ids;
+  const float* uniforms;
+  int32_t* out_ids;
+  int32_t* n_accepted;
+  int32_t B, k, V;
+  int32_t C;        // chunks per row
+  int32_t CS;       // elements per chunk (multiple of 4)
+  int32_t* err;
+  int32_t* tickets_end;   // ticket of sequence b is tickets_end[-(b + 1)]
+  double* chunk_sums;
+};
+
+// launchers (defined in the .hip files); return hipError_t of the launch
+hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int num_wg, hipStream_t stream);
+hipError_t launch_attn_reduce(const AttnParams& p, int D, hipStream_t stream);
+const void* attn_main_kernel_ptr(int D, int BS, int NRT);
+hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream);
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace vap
