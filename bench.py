@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode/verify attention step and the speculative verifier on one GPU.
+
+Default run (one JSON line on stdout):
+  * value: HBM GB/s of paged_attn_step on the Llama-3-8B-shaped decode batch (64 sequences,
+    32 q / 8 kv heads, head_dim 128, 16-token blocks, lognormal context lengths), i.e. the
+    algorithmic bytes of one step divided by its time, with K steps timed back to back;
+  * verify step: paged_attn_step + spec_verify on the speculative-verify batch (16 sequences,
+    q_len 5, vocab 128256) -> verified tokens/s and the verifier's own GB/s;
+  * roofline: the attention kernel's average duration from HIP events recorded on its own
+    stream (the library's kernel timer) against the 8 TB/s HBM peak;
+  * cpu_baseline: the fp64 CPU oracle on the same decode batch, on the host's cores.
+
+Inputs are resident in HBM before timing starts.  The KV pool (and the verifier's
+probability rows) are rotated over several device copies so that consecutive steps never
+find their bytes in the 256 MB Infinity Cache.
+
+Other modes: --mode copy (streaming copy kernel: the measured HBM ceiling), --mode attn-only /
+verify-only (one kernel family, for profiling).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode/verify attention HBM GB/s (% of peak); verified tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_decode_traffic.txt")
+KERNEL_SOURCES = ["verify_attention_paged_amd/csrc/attn_paged.hip",
+                  "verify_attention_paged_amd/csrc/vap_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; no padding, no partials)
+# ---------------------------------------------------------------------------------------
+
+def attn_bytes(ctx_lens, q_lens, Hq, Hkv, D, bs) -> int:
+    total = 0
+    for L, Q in zip(ctx_lens, q_lens):
+        L, Q = int(L), int(Q)
+        total += 4 * L * Hkv * D          # K and V rows (bf16), each KV head once for all its rows
+        total += 2 * Q * Hq * D           # q (bf16)
+        total += 4 * Q * Hq * D           # out (fp32)
+        total += 4 * ((L + bs - 1) // bs) + 8   # block ids and the two lengths
+    return total
+
+
+def verify_bytes(n_accepted, k, V) -> int:
+    total = 0
+    for n in n_accepted:
+        total += 8 * k + 4 * (k + 1) + 4 * k + 4 * (k + 2)   # gathers, uniforms, ids, outputs
+        total += 8 * V if int(n) < k else 4 * V                 # residual row pair or bonus row
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on
+    the current kernel source (else None)."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------------------
+# device-side setup
+# ---------------------------------------------------------------------------------------
+
+def rotating_copies(t, min_bytes):
+    """Enough device copies of `t` that cycling through them spans at least `min_bytes`."""
+    import torch
+    n = max(2, math.ceil(min_bytes / max(1, t.numel() * t.element_size())))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def setup_attention(name, dev):
+    import torch
+    import workloads
+    import verify_attention_paged_amd as vap
+    inp = workloads.attention_config(name)
+    d = dict(q=inp.q.to(dev), block_tables=inp.block_tables.to(dev), ctx_lens=inp.ctx_lens.to(dev),
+             q_lens=inp.q_lens.to(dev))
+    pools = rotating_copies(inp.kv_pool.to(dev), 1 << 30)
+    out = torch.empty(inp.q.shape, dtype=torch.float32, device=dev)
+    ws = vap.attn_workspace(vap.attn_shape(d["q"], pools[0], d["block_tables"]), dev)
+    nbytes = attn_bytes(inp.ctx_lens.tolist(), inp.q_lens.tolist(), inp.num_q_heads, inp.num_kv_heads,
+                        inp.head_dim, inp.block_size)
+    return inp, d, pools, out, ws, nbytes
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / max(steps, 1), wall
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host's cores
+# ---------------------------------------------------------------------------------------
+
+def cpu_baseline(inp, nbytes, budget_s=10.0):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as OA
+    qb = inp.q.view(torch.int16).numpy().view(np.uint16)
+    pb = inp.kv_pool.view(torch.int16).numpy().view(np.uint16)
+    tables, L, Q = inp.block_tables.numpy(), inp.ctx_lens.numpy(), inp.q_lens.numpy()
+    passes = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            OA.paged_attention_bf16(qb, pb, tables, L, Q)
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {inp.name} batch ({inp.num_seqs} sequences, all {inp.num_q_heads} heads, "
+                      f"fp64 NumPy, 1 BLAS thread), {passes} passes in {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------------------
+# modes
+# ---------------------------------------------------------------------------------------
+
+def run_copy(args, dev):
+    import torch
+    import verify_attention_paged_amd as vap
+    nbytes = args.copy_mib << 20
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    ms, wall = time_loop(lambda i: vap.stream_copy(dsts[i % 2], src), args.steps, args.warmup)
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "ms_per_copy": round(ms, 5),
+                      "GB_per_s": round(gbs, 2), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}))
+
+
+def run_attention_only(args, dev, name):
+    import verify_attention_paged_amd as vap
+    inp, d, pools, out, ws, nbytes = setup_attention(name, dev)
+    step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
+                                         d["q_lens"], out=out, workspace=ws)
+    vap.timer_enable(True)
+    time_loop(step, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    ms, wall = time_loop(step, args.steps, 0)
+    kms, cnt = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    vap.timer_enable(False)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"mode": "attn-only", "workload": name, "bytes": nbytes, "ms_per_step": round(ms, 5),
+                      "GB_per_s": round(gbs, 2), "kernel_ms": round(kms / max(cnt, 1), 5),
+                      "kernel_GB_per_s": round(nbytes / (kms / max(cnt, 1) * 1e-3) / 1e9, 2)}))
+
+
+def run_default(args, dev):
+    import numpy as np
+    import torch
+    import verify_attention_paged_amd as vap
+    import workloads
+
+    # ---- decode step (the headline workload)
+    inp, d, pools, out, ws, nbytes = setup_attention("llama3_8b_decode", dev)
+    log(f"decode batch: {inp.num_seqs} seqs, {int(inp.ctx_lens.sum())} tokens, {nbytes / 1e6:.1f} MB/step, "
+        f"{len(pools)} pool copies")
+    step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
+                                         d["q_lens"], out=out, workspace=ws)
+    vap.timer_enable(True)
+    time_loop(step, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    ms, wall = time_loop(step, args.steps, 0)
+    kms_total, kcount = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    if vap.get_device_error(ws):
+        raise RuntimeError("device reported a data error on the decode batch")
+    kernel_ms = kms_total / max(1, kcount)
+    value = nbytes / (ms * 1e-3) / 1e9
+    kernel_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    log(f"decode step {ms * 1e3:.1f} us -> {value:.1f} GB/s; attention kernel {kernel_ms * 1e3:.1f} us "
+        f"-> {kernel_gbs:.1f} GB/s ({wall:.2f} s wall for {args.steps} steps)")
+
+    # ---- speculative verify step: attention (q_len 5) + spec_verify (vocab 128256)
+    vinp, vd, vpools, vout, vws, vnbytes = setup_attention("spec_verify_step", dev)
+    ver = workloads.verify_config("spec_verify_step")
+    p = ver.p.to(dev)
+    ps = rotating_copies(p, 768 << 20)
+    qs = [ver.q.to(dev) for _ in range(len(ps))]
+    ids, uni = ver.draft_ids.to(dev), ver.uniforms.to(dev)
+    out_ids = torch.empty((ver.num_seqs, ver.k + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((ver.num_seqs,), dtype=torch.int32, device=dev)
+    sws = vap.verify_workspace(ver.num_seqs, ver.k, ver.vocab, dev)
+
+    def vstep(i):
+        vap.paged_attn_step(vd["q"], vpools[i % len(vpools)], vd["block_tables"], vd["ctx_lens"], vd["q_lens"],
+                            out=vout, workspace=vws)
+        vap.spec_verify(ps[i % len(ps)], qs[i % len(qs)], ids, uni, out_ids, n_acc, workspace=sws)
+
+    time_loop(vstep, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    vap.timer_read(vap.TIMER_VERIFY, reset=True)
+    vms, _ = time_loop(vstep, args.steps, 0)
+    vattn_ms, c0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    sv_ms, c1 = vap.timer_read(vap.TIMER_VERIFY, reset=True)
+    vap.timer_enable(False)
+    n_host = n_acc.cpu().numpy()
+    emitted = int((n_host + 1).sum())
+    sv_bytes = verify_bytes(n_host, ver.k, ver.vocab)
+    sv_kernel_ms = sv_ms / max(1, c1)
+    verify_tok_s = emitted / (vms * 1e-3)
+    log(f"verify step {vms * 1e3:.1f} us ({emitted} tokens emitted, acceptance "
+        f"{float(n_host.sum()) / (ver.k * ver.num_seqs):.3f}); spec_verify kernel {sv_kernel_ms * 1e3:.2f} us "
+        f"-> {sv_bytes / (sv_kernel_ms * 1e-3) / 1e9:.1f} GB/s; verify attention kernel "
+        f"{vattn_ms / max(1, c0) * 1e3:.1f} us -> {vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9:.1f} GB/s")
+
+    # ---- CPU baseline (oracle), rank 0 at N = 1 only
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, nbytes, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
+
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_decode: 64 decode seqs, 32 q / 8 kv heads, head_dim 128, "
+                               "block 16, ctx lognormal(1024, 1) in [16, 8192], pool 1.2x live blocks",
+                   "tokens": int(inp.ctx_lens.sum()), "bytes_per_step": nbytes, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "verified_tokens_per_s": round(verify_tok_s, 1),
+        "verify_step": {"workload": "spec_verify_step: 16 seqs, q_len 5, 32/8 heads, head_dim 128, ctx "
+                                    "uniform [512, 4096]; spec_verify vocab 128256, k 4",
+                        "ms_per_step": round(vms, 5), "tokens_emitted": emitted,
+                        "attention_kernel_ms": round(vattn_ms / max(1, c0), 5),
+                        "attention_GB_per_s": round(vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9, 2),
+                        "spec_verify_kernel_ms": round(sv_kernel_ms, 5),
+                        "spec_verify_GB_per_s": round(sv_bytes / (sv_kernel_ms * 1e-3) / 1e9, 2),
+                        "spec_verify_bytes": sv_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "attn_main_kernel<128,16,1>",
+                     "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["default", "copy", "attn-only", "verify-only"], default="default")
+    ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the step has no cross-GPU part in this library "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        run_copy(args, dev)
+    elif args.mode == "attn-only":
+        run_attention_only(args, dev, args.workload)
+    elif args.mode == "verify-only":
+        run_verify_only(args, dev)
+    else:
+        run_default(args, dev)
+
+
+def run_verify_only(args, dev):
+    import torch
+    import verify_attention_paged_amd as vap
+    import workloads
+    ver = workloads.verify_config("spec_verify_step")
+    ps = rotating_copies(ver.p.to(dev), 768 << 20)
+    qs = [ver.q.to(dev) for _ in range(len(ps))]
+    ids, uni = ver.draft_ids.to(dev), ver.uniforms.to(dev)
+    out_ids = torch.empty((ver.num_seqs, ver.k + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((ver.num_seqs,), dtype=torch.int32, device=dev)
+    sws = vap.verify_workspace(ver.num_seqs, ver.k, ver.vocab, dev)
+    step = lambda i: vap.spec_verify(ps[i % len(ps)], qs[i % len(qs)], ids, uni, out_ids, n_acc, workspace=sws)
+    vap.timer_enable(True)
+    time_loop(step, 0, args.warmup)
+    vap.timer_read(vap.TIMER_VERIFY, reset=True)
+    ms, _ = time_loop(step, args.steps, 0)
+    kms, cnt = vap.timer_read(vap.TIMER_VERIFY, reset=True)
+    n = n_acc.cpu().numpy()
+    nbytes = verify_bytes(n, ver.k, ver.vocab)
+    print(json.dumps({"mode": "verify-only", "bytes": nbytes, "ms_per_call": round(ms, 5),
+                      "kernel_ms": round(kms / max(cnt, 1), 5),
+                      "kernel_GB_per_s": round(nbytes / (kms / max(cnt, 1) * 1e-3) / 1e9, 2)}))
+
+
+if __name__ == "__main__":
+    main()

@@ -110,7 +110,8 @@ size_t vap_attn_workspace_min_bytes(const vap_attn_shape* shape);
  *   out           fp32 [total_q][Hq][D]; softmax(scale * q k^T) v per row and head.
  *   workspace     device scratch of workspace_bytes (see vap_attn_workspace_bytes).
  *
- * Enqueues a plan kernel, the attention kernel and a split-merge kernel on `stream`.
+ * Enqueues the attention kernel and a combine kernel for the units split across worker waves
+ * on `stream` (preceded by a plan kernel when num_seqs > 2048).
  */
 int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tables,
                     const int32_t* ctx_lens, const int32_t* q_lens, float* out,
@@ -131,7 +132,7 @@ size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);
  *                                 uniforms[b][k] drives the final draw
  *   out_ids     int32 [B][k+1]    accepted drafts, then the drawn token, then -1 padding
  *   n_accepted  int32 [B]         number of accepted drafts n in [0, k]
- *   0 <= B <= 2^22, 0 <= k <= 64, V >= 1.
+ *   0 <= B <= 2^22, 0 <= k <= 64, 1 <= V <= 2^20.
  *
  * Per sequence: x_i is accepted iff p_i(x_i) > 0 and r_i * q_i(x_i) <= p_i(x_i) (exact in
  * fp64); the first rejection at n stops the tests.  The emitted token is drawn from
@@ -171,6 +172,12 @@ int vap_timer_read(int kind, double* total_ms, int32_t* count, int reset);
  * src to dst on `stream`; used to measure the achievable HBM copy rate and to calibrate the
  * hardware byte counters. */
 int vap_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Plain streaming read kernel over `bytes` (a multiple of 16) of src: the achievable HBM read
+ * rate.  Writes at most one 16-byte value per workgroup into `sink` (16-byte aligned, room for
+ * 16 * (8 * number of CUs) bytes) only if a checksum matches a sentinel, so the loads cannot be
+ * elided. */
+int vap_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /* Number of compute units of the current device and its gfx arch name ("gfx950"). */
 int vap_device_info(int32_t* num_cus, char* arch_name, size_t arch_name_len);

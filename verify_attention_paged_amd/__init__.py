@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     paged_attn_step,
     spec_verify,
     stream_copy,
+    stream_read,
     timer_enable,
     timer_read,
     verify_workspace,

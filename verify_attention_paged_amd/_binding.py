@@ -58,6 +58,7 @@ SIGNATURES = {
     "vap_timer_enable": (ctypes.c_int, [ctypes.c_int]),
     "vap_timer_read": (ctypes.c_int, [ctypes.c_int, _pdbl, _pi32, ctypes.c_int]),
     "vap_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "vap_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "vap_device_info": (ctypes.c_int, [_pi32, ctypes.c_char_p, _sz]),
 }
 
@@ -257,6 +258,11 @@ def stream_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
         raise ValueError("dst smaller than src")
     nbytes = src.numel() * src.element_size()
     _check(load_library().vap_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().vap_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)))
 
 
 def device_info():

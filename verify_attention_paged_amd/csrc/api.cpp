@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -59,9 +60,12 @@ const DevInfo* device_info() {
       for (int b = 0; b < 2; ++b)
         for (int c = 0; c < 2; ++c) {
           int nb = 0;
-          const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1);
+          // occupancy with the largest in-workgroup plan (LDS never binds before registers)
+          const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1, true);
           if (f == nullptr ||
-              hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads, 0) != hipSuccess || nb < 1)
+              hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads,
+                                                            attn_main_lds_bytes(kLdsPlanMaxSeqs)) != hipSuccess ||
+              nb < 1)
             nb = 1;
           d.attn_occ[a][b][c] = nb;
         }
@@ -135,7 +139,7 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
 
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2];
-  return d->num_cus * occ * kWavesPerWG;
+  return std::min(kMaxWaves, d->num_cus * occ * kWavesPerWG);
 }
 
 }  // namespace
@@ -227,24 +231,27 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
   const float scale = s.scale > 0.f ? s.scale : 1.0f / std::sqrt((float)s.head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.hdr = reinterpret_cast<AttnHeader*>(ws);
+  P.desc = reinterpret_cast<int32_t*>(ws + lay.desc);
+  P.g_L = reinterpret_cast<int32_t*>(ws + lay.g_L);
+  P.g_Q = reinterpret_cast<int32_t*>(ws + lay.g_Q);
   P.q_off = reinterpret_cast<int32_t*>(ws + lay.q_off);
-  P.nblk = reinterpret_cast<int32_t*>(ws + lay.nblk);
-  P.n_rg = reinterpret_cast<int32_t*>(ws + lay.n_rg);
   P.seq_off = reinterpret_cast<int32_t*>(ws + lay.seq_off);
   P.wave_seq = reinterpret_cast<int32_t*>(ws + lay.wave_seq);
-  P.desc = reinterpret_cast<int4*>(ws + lay.desc);
   P.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
   P.part_acc = reinterpret_cast<float*>(ws + lay.part_acc);
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  hipError_t e = launch_attn_plan(P, stream);
-  if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  if (s.num_seqs > kLdsPlanMaxSeqs) {
+    e = launch_attn_plan(P, stream);
+    if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
+  }
   timer_begin(0, stream);
   e = launch_attn_main(P, c.D, c.BS, c.NRT, W / kWavesPerWG, stream);
   timer_end(0, stream);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
-  e = launch_attn_reduce(P, c.D, stream);
-  if (e != hipSuccess) return fail(VAP_EHIP, "merge launch: %s", hipGetErrorString(e));
+  e = launch_attn_combine(P, c.D, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "combine launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -270,11 +277,14 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
   const DevInfo* d = device_info();
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
 
-  // chunks per row: about two workgroups per CU over the whole batch, at least 256 elements
-  // per chunk, at most 256 chunks
+  // chunks per row: about two workgroups per CU over the whole batch, at least 256 and at
+  // most 4096 elements per chunk (the selecting workgroup holds a chunk in registers)
+  if ((long long)vocab > (long long)kMaxChunks * 4096)
+    return fail(VAP_EINVAL, "vocab=%d above %d", vocab, kMaxChunks * 4096);
   long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
   const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
   C = std::max(1LL, std::min(C, cmax));
+  C = std::max(C, ((long long)vocab + 4095) / 4096);
   long long CS = ((long long)vocab + C - 1) / C;
   CS = (CS + 3) / 4 * 4;
   C = ((long long)vocab + CS - 1) / CS;
@@ -363,6 +373,15 @@ int vap_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return fail(VAP_EINVAL, "bytes and pointers must be multiples of 16");
   const hipError_t e = launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VAP_EHIP, "copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int vap_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(VAP_EINVAL, "NULL pointer");
+  if ((bytes & 15) || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15))
+    return fail(VAP_EINVAL, "bytes and pointers must be multiples of 16");
+  const hipError_t e = launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VAP_EHIP, "read launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -1,18 +1,17 @@
-// Plan kernel of paged_attn_step: per-sequence bookkeeping and the work partition.
+// Plan kernel of paged_attn_step for batches above 2048 sequences (smaller batches build the
+// same tables inside every attention workgroup, in LDS).
 //
-// One workgroup of 1024 threads runs before the attention kernel.  It
+// One workgroup of 1024 threads
 //   * validates each sequence's lengths (1 <= q_len <= ctx_len <= table capacity, packed rows
 //     inside total_q) and flags the rest in the sticky error word; invalid sequences get no
 //     work,
-//   * computes each sequence's first packed query row (exclusive scan of q_lens, the ragged
-//     packing that replaces padding -- tempatgunting.com article, section "Implementation
-//     Details That Affect Tail Latency"),
-//   * counts each sequence's work in KV blocks: ceil(ctx_len / block_size) blocks for every
-//     (KV head, row group) unit, where a row group is RG of the G * q_len query rows that
-//     share one KV head (grouped-query attention),
-//   * splits the total work evenly over the W worker waves of the attention kernel (each
-//     wave gets [w*TB/W, (w+1)*TB/W) of the concatenated block list) and records the
-//     sequence holding each wave's first block.
+//   * computes each sequence's first packed query row (exclusive scan of q_lens: ragged rows
+//     without padding -- tempatgunting.com article, section "Implementation Details That Affect
+//     Tail Latency"),
+//   * counts each sequence's work: ceil(ctx_len / block_size) KV blocks for every (KV head,
+//     row group) unit, where a row group is RG of the G * q_len query rows sharing a KV head,
+//   * records the sequence holding the first work block of each worker wave, the waves
+//     splitting the total work TB evenly: wave w owns [w*TB/W', (w+1)*TB/W'), W' = min(W, TB).
 #include "vap_internal.h"
 
 namespace vap {
@@ -73,26 +72,17 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(const AttnParam
     const long long qoff = block_exclusive_scan<long long>(qc, s_tmp64, qtot) + carry_q;
     bool valid = false;
     if (s < P.B) {
-      if (Q < 1 || L < Q || (long long)L > cap) {
-        errbits |= VAP_DERR_LENS;
-      } else if (qoff + Q > P.total_q) {
-        errbits |= VAP_DERR_TOTAL_Q;
-      } else {
-        valid = true;
-      }
+      if (Q < 1 || L < Q || (long long)L > cap) errbits |= VAP_DERR_LENS;
+      else if (qoff + Q > P.total_q) errbits |= VAP_DERR_TOTAL_Q;
+      else valid = true;
     }
-    int32_t nb = 0, nrg = 0, work = 0;
-    if (valid) {
-      nb = (L + P.BS - 1) / P.BS;
-      nrg = (P.G * Q + P.RG - 1) / P.RG;
-      work = nb * nrg * P.Hkv;   // the host bounds the total below 2^31
-    }
+    const int32_t work = valid ? ((L + P.BS - 1) / P.BS) * ((P.G * Q + P.RG - 1) / P.RG) * P.Hkv : 0;
     int32_t wtot;
     const int32_t woff = block_exclusive_scan<int32_t>(work, s_tmp32, wtot) + carry_w;
     if (s < P.B) {
+      P.g_L[s] = valid ? L : 0;
+      P.g_Q[s] = valid ? Q : 1;
       P.q_off[s] = valid ? (int32_t)qoff : 0;
-      P.nblk[s] = nb;
-      P.n_rg[s] = nrg;
       P.seq_off[s] = woff;
       s_off[s] = woff;
     }
@@ -107,10 +97,10 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(const AttnParam
   }
   __syncthreads();
 
-  // sequence holding each worker wave's first block: the largest s with s_off[s] <= b0
   const int32_t TB = s_off[P.B];
-  for (int w = tid; w < P.W; w += kPlanThreads) {
-    const long long b0 = (long long)w * TB / P.W;
+  const int W = min(P.W, TB);
+  for (int w = tid; w < W; w += kPlanThreads) {
+    const long long b0 = (long long)w * TB / W;
     int lo = 0, hi = P.B;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;

@@ -121,28 +121,55 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
 
 // Smallest x in chunk [x0, x1) whose running sum base + C exceeds t (INT_MAX if none), with
 // the running sum taken in ascending token id; also the largest x with w_x > 0 (-1 if none).
+// Each thread takes a contiguous slice of at most kSlice elements held in registers (chunks
+// are at most kThreads * kSlice long), so the scan never goes back to memory.
+constexpr int kSlice = 16;
+
+template <bool VEC4>
 __device__ __forceinline__ void chunk_select(const float* prow, const float* qrow, bool residual,
                                              int x0, int x1, double base, double t,
                                              double* s_red, int* s_int, int& first_above,
                                              int& last_positive) {
   const int len = x1 - x0;
-  const int per = (len + kThreads - 1) / kThreads;
-  const int a = x0 + min(len, threadIdx.x * per);
-  const int b = x0 + min(len, (threadIdx.x + 1) * per);
+  const int per = ((len + kThreads - 1) / kThreads + 3) & ~3;   // multiple of 4, <= kSlice
+  const int a = x0 + min(len, (int)threadIdx.x * per);
+  const int b = x0 + min(len, (int)threadIdx.x * per + per);
+  float pv[kSlice], qv[kSlice];
+#pragma unroll
+  for (int j = 0; j < kSlice; j += 4) {
+    if (VEC4 && a + j + 4 <= b) {
+      const float4 x = *reinterpret_cast<const float4*>(prow + a + j);
+      pv[j] = x.x; pv[j + 1] = x.y; pv[j + 2] = x.z; pv[j + 3] = x.w;
+      if (residual) {
+        const float4 y = *reinterpret_cast<const float4*>(qrow + a + j);
+        qv[j] = y.x; qv[j + 1] = y.y; qv[j + 2] = y.z; qv[j + 3] = y.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = a + j + u;
+        pv[j + u] = (x < b) ? prow[x] : 0.f;
+        if (residual) qv[j + u] = (x < b) ? qrow[x] : 0.f;
+      }
+    }
+  }
   double mine = 0.0;
   int lastpos = -1;
-  for (int x = a; x < b; ++x) {
-    const double wx = residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
+#pragma unroll
+  for (int j = 0; j < kSlice; ++j) {
+    const double wx = (a + j < b) ? residual_or_p(pv[j], residual ? qv[j] : 0.f, residual) : 0.0;
     mine += wx;
-    if (wx > 0.0) lastpos = x;
+    if (wx > 0.0) lastpos = a + j;
   }
   double total;
   const double before = block_exclusive_scan(mine, s_red, total);
   double run = base + before;
   int found = INT_MAX;
-  for (int x = a; x < b; ++x) {
-    run += residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
-    if (run > t) { found = x; break; }
+#pragma unroll
+  for (int j = 0; j < kSlice; ++j) {
+    const double wx = (a + j < b) ? residual_or_p(pv[j], residual ? qv[j] : 0.f, residual) : 0.0;
+    run += wx;
+    if (found == INT_MAX && a + j < b && run > t) found = a + j;
   }
   first_above = block_min(found, s_int);
   last_positive = block_max(lastpos, s_int);
@@ -193,16 +220,20 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const int x1 = min(V, x0 + P.CS);
   double part = block_sum(chunk_partial<VEC4>(prow, qrow, residual, x0, x1), s_red);
   if (tid == 0) {
+    // publish the chunk sum with an agent-coherent (write-through) store, wait until it has
+    // completed, then arrive; the L2-wide writeback/invalidate of an agent-scope fence is not
+    // needed because every cross-workgroup value goes through agent-scope accesses
     __hip_atomic_store(reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + cidx,
                        (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (ticket == C - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // 4. last workgroup of sequence b: locate t among the chunk sums, then inside one chunk
   if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -241,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     __syncthreads();
     const int a = cstar * P.CS, e = min(V, a + P.CS);
     int first_above, last_positive;
-    chunk_select(prow, srow_q, use_res, a, e, base, t, s_red, s_int, first_above, last_positive);
+    chunk_select<VEC4>(prow, srow_q, use_res, a, e, base, t, s_red, s_int, first_above, last_positive);
     token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
   } else if (tid == 0) {
     atomicOr(P.err, VAP_DERR_EMPTY_ROW);

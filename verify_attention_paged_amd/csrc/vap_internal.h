@@ -13,44 +13,48 @@ constexpr int kMaxSeqs = 8192;      // plan kernel keeps per-sequence work offse
 constexpr int kPlanThreads = 1024;
 constexpr int kAttnThreads = 256;   // 4 independent worker waves per workgroup
 constexpr int kWavesPerWG = kAttnThreads / 64;
-constexpr int kTokTile = 32;        // tokens per inner iteration (two 16-token MFMA tiles)
+
 
 // ---------------------------------------------------------------------------------------
 // Attention workspace layout (all offsets 256-byte aligned).
-//   header   : err word, total work blocks
-//   q_off    : int32 [B]   first packed row of each sequence
-//   nblk     : int32 [B]   KV blocks of each sequence (0 = sequence skipped as invalid)
-//   n_rg     : int32 [B]   row groups of each sequence (G * q_len rows, RG per group)
-//   seq_off  : int32 [B+1] exclusive prefix of per-sequence work (blocks x row groups x Hkv)
-//   wave_seq : int32 [W]   sequence holding each worker wave's first work block
-//   desc     : int4  [W]   split-merge descriptor written by each worker wave
-//   part_ml  : float2 [W][2][RG]       (running max in log2 units, running sum) per row
-//   part_acc : float  [W][2][RG][D]    unnormalised output per row
+//   [0, 256)   header: sticky err word, total work blocks
+//   desc       int32 [W][8]       split-unit descriptor written by every worker wave (valid=0
+//              when the wave opens no split unit); read by the combine kernel
+//   g_L, g_Q   int32 [B]          per-sequence lengths (g_L = 0 for a skipped sequence)   \  only
+//   q_off      int32 [B]          first packed row of each sequence                        |  for
+//   seq_off    int32 [B+1]        exclusive prefix of per-sequence work                   |  B >
+//   wave_seq   int32 [W]          sequence holding each worker wave's first work block    /  2048
+//   part_ml    float2 [W][2][RG]      (running max in log2 units, running sum) per row
+//   part_acc   float  [W][2][RG][D]   unnormalised output per row
+// A unit of work is (sequence, KV head, row group); a sequence has ceil(L/BS) work blocks
+// per unit.  Worker wave w owns work blocks [w*TB/W', (w+1)*TB/W') with W' = min(W, TB).
 // ---------------------------------------------------------------------------------------
+constexpr int kMaxWaves = 16384;
+constexpr int kLdsPlanMaxSeqs = 2048;   // above this the plan kernel builds the tables
+
 struct AttnHeader {
   int32_t err;
-  int32_t pad0;
-  int32_t total_work;   // TB: total work blocks of the step
-  int32_t pad1;
+  int32_t total_work;   // TB: total work blocks of the step (plan kernel path)
+  int32_t pad[2];
 };
 
 struct AttnLayout {
-  size_t q_off, nblk, n_rg, seq_off, wave_seq, desc, part_ml, part_acc, total;
+  size_t desc, g_L, g_Q, q_off, seq_off, wave_seq, part_ml, part_acc, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline AttnLayout attn_layout(int B, int W, int RG, int D) {
   AttnLayout L;
-  size_t o = align256(sizeof(AttnHeader));
-  L.q_off = o;    o = align256(o + size_t(B) * 4);
-  L.nblk = o;     o = align256(o + size_t(B) * 4);
-  L.n_rg = o;     o = align256(o + size_t(B) * 4);
-  L.seq_off = o;  o = align256(o + size_t(B + 1) * 4);
-  L.wave_seq = o; o = align256(o + size_t(W) * 4);
-  L.desc = o;     o = align256(o + size_t(W) * 16);
-  L.part_ml = o;  o = align256(o + size_t(W) * 2 * RG * 8);
-  L.part_acc = o; o = align256(o + size_t(W) * 2 * RG * D * 4);
+  size_t o = 256;
+  L.desc = o;      o = align256(o + size_t(W) * 32);
+  L.g_L = o;       o = align256(o + size_t(B) * 4);
+  L.g_Q = o;       o = align256(o + size_t(B) * 4);
+  L.q_off = o;     o = align256(o + size_t(B) * 4);
+  L.seq_off = o;   o = align256(o + size_t(B + 1) * 4);
+  L.wave_seq = o;  o = align256(o + size_t(W) * 4);
+  L.part_ml = o;   o = align256(o + size_t(W) * 2 * RG * 8);
+  L.part_acc = o;  o = align256(o + size_t(W) * 2 * RG * D * 4);
   L.total = o;
   return L;
 }
@@ -64,17 +68,17 @@ struct AttnParams {
   const int32_t* q_lens;    // [B]
   float* out;               // fp32 [T][Hq][D]
   int32_t B, Hq, Hkv, G, num_blocks, MB, total_q;
-  int32_t W;                // worker waves
+  int32_t W;                // worker waves launched
   int32_t RG;               // rows per unit (16 * row tiles)
-  int32_t BS;               // block size (plan kernel only; the attention kernel templates it)
+  int32_t BS;               // block size (the attention kernel also templates it)
   float scale_log2;         // softmax scale * log2(e)
   AttnHeader* hdr;
+  int32_t* desc;
+  int32_t* g_L;
+  int32_t* g_Q;
   int32_t* q_off;
-  int32_t* nblk;
-  int32_t* n_rg;
   int32_t* seq_off;
   int32_t* wave_seq;
-  int4* desc;
   float2* part_ml;
   float* part_acc;
 };
@@ -114,10 +118,12 @@ struct VerifyParams {
 // launchers (defined in the .hip files); return hipError_t of the launch
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int num_wg, hipStream_t stream);
-hipError_t launch_attn_reduce(const AttnParams& p, int D, hipStream_t stream);
-const void* attn_main_kernel_ptr(int D, int BS, int NRT);
+hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
+const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan);
+size_t attn_main_lds_bytes(int B);
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
 }  // namespace vap
