@@ -536,18 +536,16 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
 }
 
 // Combine kernel: one workgroup per split unit (described by the wave w holding its first
-// block).  For every row, M = max_p m_p, L = sum_p 2^(m_p - M) l_p and
-// out = sum_p 2^(m_p - M) acc_p / L over the unit's partials p = w .. wb in wave order
-// (flash-decoding's combine).  Partials are taken kCombineBatch at a time, and a batch's
-// (max, sum) values and rows are loaded together, so a batch costs one memory round trip.
+// block); wave j of the workgroup takes rows j, j+4, ... and lane l dims (D/64)*l .. +D/64-1.
+// Per row it folds the partials p = w .. wb in wave order with flash-decoding's combine
+// (running max M, sum L = sum 2^(m_p - M) l_p, rows sum 2^(m_p - M) acc_p), loading
+// kCombineBatch partials per round trip; out = rows / L.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBatch = 8;
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const AttnParams P) {
-  __shared__ float s_w[kCombineBatch][32];   // per (partial, row): max, then weight
-  __shared__ float s_l[kCombineBatch][32];
-  __shared__ float s_M[32], s_L[32], s_scale[32];
+  constexpr int DPL = D / 64;
   const int w = blockIdx.x;
   const int TB = P.hdr->total_work;
   if (w >= min(P.W, TB)) return;
@@ -559,75 +557,54 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Att
   const int wb = d1.x, slot_a = d1.y;
   const int G = P.G, RG = P.RG;
   const int nrows = min(RG, G * Q - rg * RG);
-  const int np = wb - w + 1;
-  const int tid = threadIdx.x;
-  constexpr int kPer = 32 * D / kCombineThreads;   // elements per thread at most (32 rows)
-  float acc[kPer];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  for (int r = wave; r < nrows; r += kCombineThreads / 64) {
+    float M = kNegInf, L = 0.f;
+    float a[DPL];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
-  if (tid < 32) {
-    s_M[tid] = kNegInf;
-    s_L[tid] = 0.f;
-  }
-  for (int p0 = 0; p0 < np; p0 += kCombineBatch) {
-    // one round trip: this batch's (max, sum) per row and every element of its rows
-    float2 ml = make_float2(kNegInf, 0.f);
-    const int mp = tid / 32, mr = tid % 32;          // (partial, row) of this thread's (max, sum)
-    if (mp < kCombineBatch && p0 + mp < np && mr < nrows) {
-      const int wp = w + p0 + mp;
-      ml = P.part_ml[((long long)wp * 2 + (wp == w ? slot_a : 0)) * RG + mr];
-    }
-    float v[kCombineBatch][kPer];
+    for (int k = 0; k < DPL; ++k) a[k] = 0.f;
+    for (int p0 = w; p0 <= wb; p0 += kCombineBatch) {
+      float2 ml[kCombineBatch];
+      float v[kCombineBatch][DPL];
 #pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
-      const int wp = w + p0 + j;
-      const long long base = ((long long)wp * 2 + (wp == w ? slot_a : 0)) * RG * D;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int e = tid + k * kCombineThreads;
-        v[j][k] = (p0 + j < np && e < nrows * D) ? P.part_acc[base + e] : 0.f;
-      }
-    }
-    __syncthreads();
-    if (mp < kCombineBatch) {
-      s_w[mp][mr] = ml.x;
-      s_l[mp][mr] = ml.y;
-    }
-    __syncthreads();
-    if (tid < nrows) {
-      float M = s_M[tid];
-      for (int j = 0; j < kCombineBatch; ++j) M = fmaxf(M, s_w[j][tid]);
-      const float scale = (s_M[tid] == kNegInf) ? 0.f : fast_exp2(s_M[tid] - M);
-      float L = s_L[tid] * scale;
       for (int j = 0; j < kCombineBatch; ++j) {
-        const float wgt = (s_w[j][tid] == kNegInf) ? 0.f : fast_exp2(s_w[j][tid] - M);
-        s_w[j][tid] = wgt;
-        L += s_l[j][tid] * wgt;
+        const int wp = p0 + j;
+        if (wp <= wb) {
+          const long long prow = ((long long)wp * 2 + (wp == w ? slot_a : 0)) * RG + r;
+          ml[j] = P.part_ml[prow];
+          const float* pa = P.part_acc + prow * D + DPL * lane;
+          if constexpr (DPL == 2) {
+            const float2 x = *reinterpret_cast<const float2*>(pa);
+            v[j][0] = x.x;
+            v[j][1] = x.y;
+          } else {
+            v[j][0] = pa[0];
+          }
+        }
       }
-      s_M[tid] = M;
-      s_L[tid] = L;
-      s_scale[tid] = scale;
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        if (p0 + j <= wb) {
+          const float Mn = fmaxf(M, ml[j].x);
+          if (Mn != kNegInf) {
+            const float fa = fast_exp2(M - Mn), fb = fast_exp2(ml[j].x - Mn);
+            L = L * fa + ml[j].y * fb;
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) a[k] = a[k] * fa + v[j][k] * fb;
+            M = Mn;
+          }
+        }
+      }
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid + k * kCombineThreads;
-      const int r = min(e / D, 31);
-      float a = acc[k] * s_scale[r];
-#pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j) a += s_w[j][r] * v[j][k];
-      acc[k] = a;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = tid + k * kCombineThreads;
-    if (e < nrows * D) {
-      const int r = e / D, dd = e - r * D;
-      const int row = rg * RG + r;
-      const int i = row / G;
-      P.out[((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + dd] = acc[k] / s_L[r];
+    const int row = rg * RG + r;
+    const int i = row / G;
+    float* op = P.out + ((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + DPL * lane;
+    const float inv = 1.f / L;
+    if constexpr (DPL == 2) {
+      *reinterpret_cast<float2*>(op) = make_float2(a[0] * inv, a[1] * inv);
+    } else {
+      op[0] = a[0] * inv;
     }
   }
 }
