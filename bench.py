@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -67,11 +68,21 @@ def verify_bytes(n_accepted, k, V) -> int:
     return total
 
 
+def code_only(text: str) -> str:
+    """C/C++ source with comments and blank lines removed, so that a comment edit does not
+    count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
+    """Fingerprint of the attention kernel's code (comments ignored); the committed counter
+    summary is valid only for the fingerprint it records."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

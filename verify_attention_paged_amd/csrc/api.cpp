@@ -99,6 +99,14 @@ void timer_end(int kind, hipStream_t stream) {
 
 // ---- attention shape checks ---------------------------------------------------------------
 
+// Fixed cost of starting a unit of work, in work blocks: about four 16-token tiles of
+// streaming time (its query rows and block-table window are dependent loads that the tile
+// pipeline cannot hide).  Counting it balances waves that start many short units.
+#ifndef VAP_UNIT_SETUP_TILES
+#define VAP_UNIT_SETUP_TILES 4
+#endif
+int unit_setup_blocks(int block_size) { return VAP_UNIT_SETUP_TILES * 16 / block_size; }
+
 struct AttnPlanChoice {
   int D, BS, NRT, RG, G;
 };
@@ -132,14 +140,19 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
   if ((long long)s->total_q * s->num_q_heads >= (1LL << 31))
     return fail(VAP_EINVAL, "total_q*num_q_heads exceeds 2^31");
   const long long rows_groups = ((long long)c->G * s->total_q + c->RG - 1) / c->RG + s->num_seqs;
-  if ((long long)s->num_kv_heads * s->max_blocks_per_seq * rows_groups >= (1LL << 31) - 1)
+  if ((long long)s->num_kv_heads * (s->max_blocks_per_seq + unit_setup_blocks(c->BS)) * rows_groups >= (1LL << 31) - 1)
     return fail(VAP_EINVAL, "work of the step may exceed 2^31 blocks");
   return VAP_OK;
 }
 
+// Worker waves: one per SIMD (one workgroup of four per CU).  Each wave keeps two tiles in
+// flight; at that depth the memory system is already saturated for this access pattern, so
+// more waves only add latency to every dependent load (and partials to merge).
+constexpr int kWorkgroupsPerCU = 1;
+
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2];
-  return std::min(kMaxWaves, d->num_cus * occ * kWavesPerWG);
+  return std::min(kMaxWaves, d->num_cus * std::min(occ, kWorkgroupsPerCU) * kWavesPerWG);
 }
 
 }  // namespace
@@ -228,6 +241,7 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
   P.W = W;
   P.RG = c.RG;
   P.BS = c.BS;
+  P.UH = unit_setup_blocks(c.BS);
   const float scale = s.scale > 0.f ? s.scale : 1.0f / std::sqrt((float)s.head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.hdr = reinterpret_cast<AttnHeader*>(ws);

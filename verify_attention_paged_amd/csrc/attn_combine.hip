@@ -1,0 +1,162 @@
+// Combine kernel of paged_attn_step: merges the partials of every unit of work that the main
+// kernel split over several worker waves and writes the unit's output rows.
+//
+// A split unit's partials are (m_p, l_p, acc_p) per row: running max in log2 units, running
+// sum and unnormalised output over one block range.  They merge as in flash-decoding's
+// combine (the split-KV reduction the pages' long-context batches need -- tempatgunting.com
+// article, section "Implementation Details That Affect Tail Latency"):
+//     M = max_p m_p,   L = sum_p 2^(m_p - M) l_p,   out = sum_p 2^(m_p - M) acc_p / L,
+// folded in a fixed order, so a step's output does not depend on timing.
+//
+// Layout of the work (the step is latency-bound: every partial was written by the previous
+// kernel, so each dependent round trip to L2/MALL costs more than the bytes):
+//  * one workgroup (8 waves) per descriptor; wave w's descriptor is valid when w holds the
+//    first block of a split unit, and then names the last wave wb holding part of it;
+//  * 16 lanes per row, each lane D/16 consecutive dims (float4 loads), so a wave covers a
+//    quad of 4 rows;
+//  * nq = ceil(rows/4) quads; with nq < 8 the partial list is split too: S = 8 / nq waves per
+//    quad take partials p, p+S, p+2S, ... and merge in LDS in wave order;
+//  * up to kBatch partials are loaded before any is folded (one round trip per batch).
+#include "vap_internal.h"
+
+namespace vap {
+namespace {
+
+constexpr int kCombineWaves = 8;
+constexpr int kCombineThreads = 64 * kCombineWaves;
+constexpr int kBatch = 8;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int DPL>
+struct RowState {
+  float M, L;
+  float a[DPL];
+};
+
+// fold (m, l, v) into the running state s
+template <int DPL>
+__device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const float (&v)[DPL]) {
+  const float Mn = fmaxf(s.M, m);
+  if (Mn == kNegInf) return;   // both empty
+  const float fa = __builtin_amdgcn_exp2f(s.M - Mn), fb = __builtin_amdgcn_exp2f(m - Mn);
+  s.L = s.L * fa + l * fb;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) s.a[k] = s.a[k] * fa + v[k] * fb;
+  s.M = Mn;
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const AttnParams P) {
+  constexpr int DPL = D / 16;   // dims per lane
+  constexpr int NV4 = DPL / 4;  // float4 loads per lane and partial
+  __shared__ float s_ml[kCombineWaves][64][2];
+  __shared__ float4 s_acc[kCombineWaves][NV4][64];
+
+  const int w = blockIdx.x;
+  const int TB = P.hdr->total_work;
+  if (w >= min(P.W, TB)) return;
+  const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * w;
+  const int4 d1 = dp[1];
+  if (d1.z == 0) return;                 // whole workgroup leaves: no barrier is pending
+  const int4 d0 = dp[0];
+  const int kvh = d0.x, rg = d0.y, qoff = d0.z, Q = d0.w;
+  const int wb = d1.x, slot_a = d1.y;
+  const int G = P.G, RG = P.RG;
+  const int nrows = min(RG, G * Q - rg * RG);
+  const int n = wb - w + 1;              // partials of this unit, in wave order
+  const int nq = (nrows + 3) >> 2;
+  const int S = nq >= kCombineWaves ? 1 : kCombineWaves / nq;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int quad = wave % nq;
+  const int sub = wave / nq;
+  const int r_raw = 4 * quad + (lane >> 4);
+  const int r = min(r_raw, nrows - 1);   // rows past the unit load a valid row, write nothing
+
+  RowState<DPL> st;
+  st.M = kNegInf;
+  st.L = 0.f;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) st.a[k] = 0.f;
+
+  if (sub < S) {
+    const int cnt = (n - sub + S - 1) / S;          // partials of this wave: sub, sub+S, ...
+    for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+      float2 ml[kBatch];
+      float v[kBatch][DPL];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = min(i0 + j, cnt - 1);
+        const int wp = w + sub + i * S;
+        const long long prow = ((long long)wp * 2 + (wp == w ? slot_a : 0)) * RG + r;
+        ml[j] = P.part_ml[prow];
+        const float4* pa = reinterpret_cast<const float4*>(P.part_acc + prow * D + DPL * li);
+#pragma unroll
+        for (int t = 0; t < NV4; ++t) {
+          const float4 x = pa[t];
+          v[j][4 * t] = x.x;
+          v[j][4 * t + 1] = x.y;
+          v[j][4 * t + 2] = x.z;
+          v[j][4 * t + 3] = x.w;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (i0 + j < cnt) fold<DPL>(st, ml[j].x, ml[j].y, v[j]);
+    }
+  }
+
+  if (S > 1) {                          // S is uniform over the workgroup
+    s_ml[wave][lane][0] = st.M;
+    s_ml[wave][lane][1] = st.L;
+#pragma unroll
+    for (int t = 0; t < NV4; ++t)
+      s_acc[wave][t][lane] = make_float4(st.a[4 * t], st.a[4 * t + 1], st.a[4 * t + 2], st.a[4 * t + 3]);
+    __syncthreads();
+    if (sub != 0) return;
+    for (int t2 = 1; t2 < S; ++t2) {
+      const int ow = quad + t2 * nq;
+      float v[DPL];
+#pragma unroll
+      for (int t = 0; t < NV4; ++t) {
+        const float4 x = s_acc[ow][t][lane];
+        v[4 * t] = x.x;
+        v[4 * t + 1] = x.y;
+        v[4 * t + 2] = x.z;
+        v[4 * t + 3] = x.w;
+      }
+      fold<DPL>(st, s_ml[ow][lane][0], s_ml[ow][lane][1], v);
+    }
+  } else if (sub != 0) {
+    return;
+  }
+
+  if (r_raw >= nrows) return;
+  const int row = rg * RG + r_raw;
+  const int i = row / G;
+  float* op = P.out + ((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + DPL * li;
+  const float inv = 1.f / st.L;
+#pragma unroll
+  for (int t = 0; t < NV4; ++t)
+    reinterpret_cast<float4*>(op)[t] =
+        make_float4(st.a[4 * t] * inv, st.a[4 * t + 1] * inv, st.a[4 * t + 2] * inv, st.a[4 * t + 3] * inv);
+}
+
+}  // namespace
+
+hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream) {
+  if (D == 64) {
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
+  } else if (D == 128) {
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vap

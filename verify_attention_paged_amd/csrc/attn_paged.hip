@@ -1,4 +1,5 @@
-// Attention kernel of paged_attn_step (gfx950).
+// Main attention kernel of paged_attn_step (gfx950); partials of split units are merged by
+// the combine kernel (attn_combine.hip).
 //
 // What is computed: for every query row of every sequence, softmax(scale * q k^T) v over the
 // keys the row may see, reading K and V through the sequence's block table (position j lives
@@ -9,42 +10,43 @@
 // Modern LLM Serving Engines Actually Work", section "The core idea").
 //
 // How (MI355X-first):
-//  * One launch.  Every workgroup first rebuilds the step's plan in LDS from q_lens/ctx_lens
-//    (validation, packed-row offsets, per-sequence work); batches above 2048 sequences take
-//    the plan from a separate plan kernel instead.
+//  * Every workgroup of the main kernel first rebuilds the step's plan in LDS from
+//    q_lens/ctx_lens (validation, packed-row offsets, per-sequence work); batches above 2048
+//    sequences take the plan from a separate plan kernel instead.
 //  * The work -- ceil(L/BS) KV blocks for each (sequence, KV head, row group) unit -- is split
-//    evenly in blocks over W persistent worker waves, so long-tail sequences spread over many
-//    waves and every CU streams the same number of bytes.  A wave covers consecutive units and
-//    may cover only part of one; then it writes a partial (running max, running sum,
-//    unnormalised output) and the last wave of that unit to arrive merges the partials
-//    (flash-decoding's combine, in wave order) and writes the output.  No second kernel.
+//    evenly in blocks over W persistent worker waves, W being the number of waves the GPU
+//    holds resident at once, so long-tail sequences spread over many waves and every CU
+//    streams the same number of bytes.  A wave covers consecutive units and may cover only
+//    part of one; then it writes a partial (running max, running sum, unnormalised rows) and
+//    the combine kernel merges the partials of each split unit in wave order (flash-decoding's
+//    combine) and writes its rows.
 //  * One wave processes all rows of a unit at once: the G query heads of a GQA group times
 //    the q_len rows (up to 16 * NRT rows).  Every K and V byte is loaded once from HBM,
-//    straight into MFMA operand registers, and serves all those rows.  The next 32-token tile
-//    is loaded while the current one is computed (register double buffering).
+//    straight into MFMA operand registers (16 bytes per lane per load), and serves all those
+//    rows.  A wave keeps one 16-token tile in flight; the 8 to 12 other resident waves of its
+//    CU hide the latency.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the K tile is
 //    the A operand (lane = token, 16 contiguous bytes per lane), the query rows the B operand.
 //    Each lane then holds one query row and four tokens, so a row's softmax statistics live
 //    in the four lanes {c, c+16, c+32, c+48}: a row max takes two cross-lane exchanges and the
 //    accumulator rescale is lane-local.
-//  * The output is accumulated transposed too, O^T += V^T P^T: P (fp32) is split into
-//    bf16 hi + lo parts that together keep ~16 mantissa bits; V^T is built from 4-byte loads
-//    (two dims of one token) with byte permutes.  P never leaves registers.
+//  * The output is accumulated transposed too, O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k):
+//    the S^T accumulator already is the P^T operand; P (fp32) is split into bf16 hi + lo parts
+//    that together keep ~16 mantissa bits; V^T comes from the 16-byte V loads by byte
+//    permutes.  P never leaves registers.
 //  * Only edge tiles (segment end, causal region of verify/prefill rows) are masked, and the
 //    masking is select-based: tokens past the segment -- including a block's unused tail,
 //    which may hold anything, even NaN -- get probability 0 and a zeroed V operand.
 #include "vap_internal.h"
 
-// Tuning knobs: waves per SIMD the register allocation must allow (occupancy), and the depth
-// of the register pipeline (tiles in flight per wave: 2 or 3).
+#include <type_traits>
+
+// Tuning knobs: waves per SIMD the register allocation must allow (occupancy).
 #ifndef VAP_ATTN_WAVES_1RT
 #define VAP_ATTN_WAVES_1RT 3     // waves per SIMD with one 16-row tile per unit
 #endif
 #ifndef VAP_ATTN_WAVES_2RT
 #define VAP_ATTN_WAVES_2RT 2     // waves per SIMD with two 16-row tiles per unit
-#endif
-#ifndef VAP_ATTN_STAGES
-#define VAP_ATTN_STAGES 1
 #endif
 
 namespace vap {
@@ -53,6 +55,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -67,20 +70,13 @@ __device__ __forceinline__ f32x4 mfma16x16x16(uint2 a, uint2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// bf16 bits of a finite float, round to nearest even
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// token offset (0..31 inside a 32-token tile) of element e of lane group g in the MFMA
-// k-slots shared by the P^T (B) and V^T (A) operands of the output product
-__device__ __forceinline__ int tile_token(int g, int e) { return (e < 4) ? (4 * g + e) : (12 + 4 * g + e); }
+// Keeps the instruction scheduler from moving code across a pipeline stage boundary (it would
+// otherwise hoist a tile's math up to its loads and serialise the pipeline).
+__device__ __forceinline__ void stage_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---------------------------------------------------------------------------------------
 // in-workgroup plan
@@ -133,7 +129,7 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
       else if (qoff + Q > P.total_q) err |= VAP_DERR_TOTAL_Q;
       else valid = true;
     }
-    const int work = valid ? ((L + P.BS - 1) / P.BS) * ((P.G * Q + P.RG - 1) / P.RG) * P.Hkv : 0;
+    const int work = valid ? (P.UH + (L + P.BS - 1) / P.BS) * ((P.G * Q + P.RG - 1) / P.RG) * P.Hkv : 0;
     int wtot;
     const int woff = wg_exclusive_scan<int>(work, s_t32, wtot) + carry_w;
     if (s < P.B) {
@@ -154,7 +150,7 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
 }
 
 // ---------------------------------------------------------------------------------------
-// one 32-token tile: loads and math
+// one 16-token tile: loads and math
 // ---------------------------------------------------------------------------------------
 
 // A tile is 16 consecutive tokens of one block (tiles start at multiples of 16).
@@ -173,26 +169,70 @@ struct KVTile {
   uint32_t vw[4][D / 32];
 };
 
+// Raw buffer loads: the tile's block base lives in a buffer resource in scalar registers (it
+// is uniform over the wave), so a lane needs one 32-bit offset register per plane instead of
+// a 64-bit address per load.  Loads past the resource's range return zeros.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufFlags = 0x00020000;   // raw (untyped) dword access
+
+// base and bytes are uniform over the wave; readfirstlane states it, so the resource stays in
+// scalar registers (a resource the compiler thinks divergent costs a loop around every load)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufFlags);
+}
+
+// vo_k = c * tok_bytes + 16 * g, vo_v = 4 * g * tok_bytes + 2 * (D/16) * c: fixed per lane.
+// A tile that is not live gets an empty range: its loads return zeros without a memory access,
+// which lets the pipelined loop issue loads unconditionally.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile(KVTile<D>& t, const uint16_t* kbase, const uint16_t* vbase,
-                                          long long tok_stride, int tg, int blk, int c, int g) {
+                                          long long tok_stride, int tg, int blk, int vo_k, int vo_v, bool live) {
   constexpr int NKK = D / 32;
   const long long row0 = (long long)blk * BS + (tg % BS);
-  const uint16_t* kp = kbase + (row0 + c) * tok_stride + 8 * g;
+  const int tok_bytes = (int)tok_stride * 2;
+  const int range = live ? kTile * tok_bytes : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0 * tok_stride, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * tok_stride, range);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) t.ka[kk] = as_bf16x8(ld16(kp + 32 * kk));
+  for (int kk = 0; kk < NKK; ++kk)
+    t.ka[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k + 64 * kk, 0, 0));
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint16_t* vp = vbase + (row0 + 4 * g + r) * tok_stride + (D / 16) * c;
     if constexpr (D == 128) {
-      const uint4 x = ld16(vp);
-      t.vw[r][0] = x.x; t.vw[r][1] = x.y; t.vw[r][2] = x.z; t.vw[r][3] = x.w;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_v, r * tok_bytes, 0);
+      t.vw[r][0] = x[0]; t.vw[r][1] = x[1]; t.vw[r][2] = x[2]; t.vw[r][3] = x[3];
     } else {
-      const uint2 x = ld8(vp);
-      t.vw[r][0] = x.x; t.vw[r][1] = x.y;
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, vo_v, r * tok_bytes, 0);
+      t.vw[r][0] = x[0]; t.vw[r][1] = x[1];
     }
   }
 }
+
+// Max over the four lanes {c, c+16, c+32, c+48} holding one row: two lane swaps (odd/even
+// 16-lane rows, then the two 32-lane halves), no LDS round trip.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Softmax reference: a row's exponentials are taken against m_run, which moves only when the
+// row's running max exceeds it by more than kRescaleLog2 (so P <= 2^kRescaleLog2); the
+// running sum and the accumulator always share m_run, so the result is the same up to
+// rounding, and most tiles skip the accumulator rescale.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int NRT, bool MASKED>
 __device__ __forceinline__ void compute_tile(const KVTile<D>& t, int tg, int t_end, const int (&lim)[NRT],
@@ -201,49 +241,57 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, int tg, int t_e
                                              f32x4 (&acc)[NRT][D / 16], int g) {
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
+  f32x4 sc[NRT];
+  bool ok[NRT][4];
+  float mx[NRT];
+  bool grow = false;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) sc[rt] = mfma16x16x32(t.ka[kk], qb[rt][kk], sc[rt]);
+    float m = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (MASKED) {
+        const int tok = tg + 4 * g + r;
+        ok[rt][r] = (tok < t_end) && (tok <= lim[rt]);
+        m = ok[rt][r] ? fmaxf(m, sc[rt][r]) : m;
+      } else {
+        m = fmaxf(m, sc[rt][r]);
+      }
+    }
+    mx[rt] = row_max4(m) * scale_log2;     // scale_log2 > 0
+    grow = grow || (mx[rt] > m_run[rt] + kRescaleLog2);
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // uniform branch
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const float m_new = fmaxf(m_run[rt], mx[rt]);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[rt] - m_new);
+      l_run[rt] *= alpha;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] *= alpha;
+      m_run[rt] = m_new;
+    }
+  }
   uint2 ph[NRT], pl[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) sc = mfma16x16x32(t.ka[kk], qb[rt][kk], sc);
-    float sv[4];
-    bool ok[4];
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = sc[r] * scale_log2;
-      if (MASKED) {
-        const int tok = tg + 4 * g + r;
-        ok[r] = (tok < t_end) && (tok <= lim[rt]);
-        mx = ok[r] ? fmaxf(mx, sv[r]) : mx;
-      } else {
-        mx = fmaxf(mx, sv[r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run[rt], mx);
-    const float ref = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run[rt] - ref);
+    const float ref = (m_run[rt] == kNegInf) ? 0.f : m_run[rt];
     float pv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pv[r] = fast_exp2(sv[r] - ref);
-      if (MASKED) pv[r] = ok[r] ? pv[r] : 0.f;
+      pv[r] = fast_exp2(sc[rt][r] * scale_log2 - ref);
+      if (MASKED) pv[r] = ok[rt][r] ? pv[r] : 0.f;
     }
-    l_run[rt] = l_run[rt] * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
-    m_run[rt] = m_new;
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] *= alpha;
-    uint32_t h[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      h[r] = bf16_bits(pv[r]);
-      lo[r] = bf16_bits(pv[r] - __uint_as_float(h[r] << 16));
-    }
-    ph[rt] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    pl[rt] = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    l_run[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    // P = hi + lo, both bf16: ~16 significant bits for the output product
+    const uint32_t h01 = pack_bf16(pv[0], pv[1]), h23 = pack_bf16(pv[2], pv[3]);
+    const uint32_t l01 = pack_bf16(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = pack_bf16(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+    ph[rt] = make_uint2(h01, h23);
+    pl[rt] = make_uint2(l01, l23);
   }
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt) {
@@ -334,6 +382,8 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   const long long tok_stride = (long long)P.Hkv * D;
   const uint16_t* kbase = P.kpool + (long long)sg.kvh * D;
   const uint16_t* vbase = P.vpool + (long long)sg.kvh * D;
+  const int vo_k = c * (int)tok_stride * 2 + 16 * g;
+  const int vo_v = 4 * g * (int)tok_stride * 2 + 2 * (D / 16) * c;
   const int jend = sg.ub + sg.seg;
 
   int out_row[NRT];
@@ -366,12 +416,15 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
 
   // The tile loop walks the segment in windows of 64 KV blocks.  A window's pool block ids are
   // loaded once (one per lane) before its tiles, so no vector load inside the tile loop depends
-  // on a branch.  Each wave keeps VAP_ATTN_STAGES tiles in flight; latency is mostly hidden by
-  // the other waves of the CU (up to 16).
+  // on a branch.
   int derr = 0;
   constexpr int kWinBlocks = 64;
   constexpr int kWinTiles = kWinBlocks * BS / kTile;
   const int ntiles = (t_end - t_start + kTile - 1) / kTile;
+  // Tiles that need no mask form a prefix: tile i (first token t_start + 16 i) needs none when
+  // it ends inside the segment and every row sees all its tokens.
+  const int last_free = min(t_end - kTile, full_until - (kTile - 1)) - t_start;
+  const int n_unmasked = last_free < 0 ? 0 : min(ntiles, last_free / kTile + 1);
   for (int wt = 0; wt < ntiles; wt += kWinTiles) {
     const int wbase = sg.ub + wt * kTile / BS;    // first block of the window
     int win;
@@ -385,39 +438,43 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     }
     const int nt = min(kWinTiles, ntiles - wt);
     const int tw0 = t_start + wt * kTile;          // first token of the window
-    auto issue = [&](KVTile<D>& X, int i) {
-      const int tg = tw0 + i * kTile;
-      load_tile<D, BS>(X, kbase, vbase, tok_stride, tg, __builtin_amdgcn_readlane(win, tg / BS - wbase), c, g);
+    auto issue = [&](KVTile<D>& X, int i, bool live) {
+      const int ic = min(i, nt - 1);
+      const int tg = tw0 + ic * kTile;
+      load_tile<D, BS>(X, kbase, vbase, tok_stride, tg, __builtin_amdgcn_readlane(win, tg / BS - wbase), vo_k, vo_v,
+                       live);
     };
-    auto compute = [&](const KVTile<D>& X, int i) {
-      const int tg = tw0 + i * kTile;
-      if (tg + kTile > t_end || tg + kTile - 1 > full_until)
-        compute_tile<D, NRT, true>(X, tg, t_end, lim, qb, P.scale_log2, m_run, l_run, acc, g);
-      else
-        compute_tile<D, NRT, false>(X, tg, t_end, lim, qb, P.scale_log2, m_run, l_run, acc, g);
+    auto compute = [&](const KVTile<D>& X, int i, auto masked) {
+      compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, P.scale_log2, m_run,
+                                                    l_run, acc, g);
     };
-#if VAP_ATTN_STAGES >= 2
-    KVTile<D> t0, t1;
-    issue(t0, 0);
-    int i = 0;
-    bool done = false;
-    while (i + 1 < nt) {             // two buffers in rotation, no register copies
-      issue(t1, i + 1);
-      compute(t0, i);
-      ++i;
-      if (i + 1 >= nt) { compute(t1, i); done = true; break; }
-      issue(t0, i + 1);
-      compute(t1, i);
-      ++i;
+    // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
+    // which would make the compiler keep a second copy of the accumulators.  The unmasked loop
+    // is a two-stage pipeline: tile i+1 is in flight while tile i is computed; the two
+    // buffers rotate (no register copies) and every load is issued unconditionally, so the
+    // compiler never has to drain the load counter at a branch.
+    const int nu = min(nt, max(0, n_unmasked - wt));
+    if (nu > 0) {
+      KVTile<D> ta, tb;
+      issue(ta, 0, true);
+      int i = 0;
+      for (; i + 1 < nu; i += 2) {    // both tiles of a pair are always computed
+        issue(tb, i + 1, true);
+        stage_fence();
+        compute(ta, i, std::false_type{});
+        stage_fence();
+        issue(ta, i + 2, i + 2 < nu);  // the next pair's first tile, or the odd last one
+        stage_fence();
+        compute(tb, i + 1, std::false_type{});
+        stage_fence();
+      }
+      if (i < nu) compute(ta, i, std::false_type{});
     }
-    if (!done) compute(t0, i);
-#else
-    for (int i = 0; i < nt; ++i) {
+    for (int i = nu; i < nt; ++i) {
       KVTile<D> t0;
-      issue(t0, i);
-      compute(t0, i);
+      issue(t0, i, true);
+      compute(t0, i, std::true_type{});
     }
-#endif
   }
   if (derr && lane == 0) atomicOr(&P.hdr->err, derr);
 
@@ -453,7 +510,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   }
   if (sg.ub == 0) {
     // this wave opens the unit: waves w .. wb hold its segments, this one in slot sg.slot
-    const long long U1 = (long long)sg.soff + (long long)(sg.unit + 1) * sg.nb;
+    const long long U1 = (long long)sg.soff + (long long)(sg.unit + 1) * (P.UH + sg.nb);
     desc.kvh = sg.kvh;
     desc.rg = sg.rg;
     desc.qoff = sg.qoff;
@@ -515,10 +572,16 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
     sg.qoff = uniform(plan_qoff(s));
     sg.soff = soff;
     sg.nb = (sg.L + BS - 1) / BS;
+    const int ns = P.UH + sg.nb;          // work blocks per unit
     const int nrg = (P.G * sg.Q + 16 * NRT - 1) / (16 * NRT);
     const int local = pos - soff;
-    sg.unit = local / sg.nb;
-    sg.ub = local - sg.unit * sg.nb;
+    sg.unit = local / ns;
+    const int uoff = local - sg.unit * ns;
+    if (uoff < P.UH) {                    // inside the unit's virtual blocks: start at its KV
+      pos += P.UH - uoff;
+      continue;
+    }
+    sg.ub = uoff - P.UH;
     sg.seg = min(sg.nb - sg.ub, (int)(b1 - pos));
     sg.kvh = sg.unit / nrg;
     sg.rg = sg.unit - sg.kvh * nrg;
@@ -532,80 +595,6 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
     int4* dp = reinterpret_cast<int4*>(P.desc) + 2 * w;
     dp[0] = make_int4(desc.kvh, desc.rg, desc.qoff, desc.Q);
     dp[1] = make_int4(desc.wb, desc.slot_a, desc.valid, 0);
-  }
-}
-
-// Combine kernel: one workgroup per split unit (described by the wave w holding its first
-// block); wave j of the workgroup takes rows j, j+4, ... and lane l dims (D/64)*l .. +D/64-1.
-// Per row it folds the partials p = w .. wb in wave order with flash-decoding's combine
-// (running max M, sum L = sum 2^(m_p - M) l_p, rows sum 2^(m_p - M) acc_p), loading
-// kCombineBatch partials per round trip; out = rows / L.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineBatch = 8;
-
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const AttnParams P) {
-  constexpr int DPL = D / 64;
-  const int w = blockIdx.x;
-  const int TB = P.hdr->total_work;
-  if (w >= min(P.W, TB)) return;
-  const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * w;
-  const int4 d1 = dp[1];
-  if (d1.z == 0) return;
-  const int4 d0 = dp[0];
-  const int kvh = d0.x, rg = d0.y, qoff = d0.z, Q = d0.w;
-  const int wb = d1.x, slot_a = d1.y;
-  const int G = P.G, RG = P.RG;
-  const int nrows = min(RG, G * Q - rg * RG);
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  for (int r = wave; r < nrows; r += kCombineThreads / 64) {
-    float M = kNegInf, L = 0.f;
-    float a[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) a[k] = 0.f;
-    for (int p0 = w; p0 <= wb; p0 += kCombineBatch) {
-      float2 ml[kCombineBatch];
-      float v[kCombineBatch][DPL];
-#pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j) {
-        const int wp = p0 + j;
-        if (wp <= wb) {
-          const long long prow = ((long long)wp * 2 + (wp == w ? slot_a : 0)) * RG + r;
-          ml[j] = P.part_ml[prow];
-          const float* pa = P.part_acc + prow * D + DPL * lane;
-          if constexpr (DPL == 2) {
-            const float2 x = *reinterpret_cast<const float2*>(pa);
-            v[j][0] = x.x;
-            v[j][1] = x.y;
-          } else {
-            v[j][0] = pa[0];
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j) {
-        if (p0 + j <= wb) {
-          const float Mn = fmaxf(M, ml[j].x);
-          if (Mn != kNegInf) {
-            const float fa = fast_exp2(M - Mn), fb = fast_exp2(ml[j].x - Mn);
-            L = L * fa + ml[j].y * fb;
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) a[k] = a[k] * fa + v[j][k] * fb;
-            M = Mn;
-          }
-        }
-      }
-    }
-    const int row = rg * RG + r;
-    const int i = row / G;
-    float* op = P.out + ((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + DPL * lane;
-    const float inv = 1.f / L;
-    if constexpr (DPL == 2) {
-      *reinterpret_cast<float2*>(op) = make_float2(a[0] * inv, a[1] * inv);
-    } else {
-      op[0] = a[0] * inv;
-    }
   }
 }
 
@@ -633,17 +622,6 @@ hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int num
   VAP_ATTN_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream) {
-  if (D == 64) {
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
-  } else if (D == 128) {
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan) {

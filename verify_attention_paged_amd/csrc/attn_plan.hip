@@ -8,8 +8,9 @@
 //   * computes each sequence's first packed query row (exclusive scan of q_lens: ragged rows
 //     without padding -- tempatgunting.com article, section "Implementation Details That Affect
 //     Tail Latency"),
-//   * counts each sequence's work: ceil(ctx_len / block_size) KV blocks for every (KV head,
-//     row group) unit, where a row group is RG of the G * q_len query rows sharing a KV head,
+//   * counts each sequence's work: UH + ceil(ctx_len / block_size) work blocks for every (KV
+//     head, row group) unit, where a row group is RG of the G * q_len query rows sharing a KV
+//     head and UH stands for the fixed cost of starting a unit,
 //   * records the sequence holding the first work block of each worker wave, the waves
 //     splitting the total work TB evenly: wave w owns [w*TB/W', (w+1)*TB/W'), W' = min(W, TB).
 #include "vap_internal.h"
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(const AttnParam
       else if (qoff + Q > P.total_q) errbits |= VAP_DERR_TOTAL_Q;
       else valid = true;
     }
-    const int32_t work = valid ? ((L + P.BS - 1) / P.BS) * ((P.G * Q + P.RG - 1) / P.RG) * P.Hkv : 0;
+    const int32_t work = valid ? (P.UH + (L + P.BS - 1) / P.BS) * ((P.G * Q + P.RG - 1) / P.RG) * P.Hkv : 0;
     int32_t wtot;
     const int32_t woff = block_exclusive_scan<int32_t>(work, s_tmp32, wtot) + carry_w;
     if (s < P.B) {

@@ -18,16 +18,22 @@ constexpr int kWavesPerWG = kAttnThreads / 64;
 // ---------------------------------------------------------------------------------------
 // Attention workspace layout (all offsets 256-byte aligned).
 //   [0, 256)   header: sticky err word, total work blocks
-//   desc       int32 [W][8]       split-unit descriptor written by every worker wave (valid=0
-//              when the wave opens no split unit); read by the combine kernel
+//   desc       int32 [W][8]       split-unit descriptor written by every worker wave:
+//              {kv head, row group, first packed row of the sequence, q_len,
+//               last wave holding part of the unit, slot of this wave's partial, valid, 0};
+//              valid = 0 when the wave holds the first block of no split unit.  Read by
+//              the combine kernel.  A unit has at most 32 rows (RG = 16 or 32).
 //   g_L, g_Q   int32 [B]          per-sequence lengths (g_L = 0 for a skipped sequence)   \  only
 //   q_off      int32 [B]          first packed row of each sequence                        |  for
 //   seq_off    int32 [B+1]        exclusive prefix of per-sequence work                   |  B >
 //   wave_seq   int32 [W]          sequence holding each worker wave's first work block    /  2048
 //   part_ml    float2 [W][2][RG]      (running max in log2 units, running sum) per row
 //   part_acc   float  [W][2][RG][D]   unnormalised output per row
-// A unit of work is (sequence, KV head, row group); a sequence has ceil(L/BS) work blocks
-// per unit.  Worker wave w owns work blocks [w*TB/W', (w+1)*TB/W') with W' = min(W, TB).
+// A unit of work is (sequence, KV head, row group).  Its work is UH + ceil(L/BS) blocks: UH
+// virtual blocks stand for the fixed cost of starting a unit (its query rows and block-table
+// window are dependent loads), followed by its ceil(L/BS) KV blocks.  Worker wave w owns work
+// blocks [w*TB/W', (w+1)*TB/W') with W' = min(W, TB); a wave whose range starts inside a
+// unit's virtual blocks begins at the unit's first KV block.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxWaves = 16384;
 constexpr int kLdsPlanMaxSeqs = 2048;   // above this the plan kernel builds the tables
@@ -71,6 +77,7 @@ struct AttnParams {
   int32_t W;                // worker waves launched
   int32_t RG;               // rows per unit (16 * row tiles)
   int32_t BS;               // block size (the attention kernel also templates it)
+  int32_t UH;               // setup cost of a unit, in work blocks (see the layout comment)
   float scale_log2;         // softmax scale * log2(e)
   AttnHeader* hdr;
   int32_t* desc;
