@@ -98,23 +98,42 @@ __device__ __forceinline__ int block_max(int x, int* s_int) {
   return t;
 }
 
-// Sum of w over [x0, x1) with coalesced loads (thread-strided).
+// Sum of w over [x0, x1) (at most kMaxChunkLen elements).  Thread-strided 16-byte loads, all
+// issued before the first is used (one memory round trip for the whole chunk); loads past
+// the chunk read a clamped in-bounds address and are discarded.
+constexpr int kMaxChunkLen = 4096;
+
 template <bool VEC4>
 __device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, bool residual,
                                                 int x0, int x1) {
   double acc = 0.0;
   if (VEC4) {
-    for (int x = x0 + 4 * threadIdx.x; x < x1; x += 4 * kThreads) {
-      const float4 pv = *reinterpret_cast<const float4*>(prow + x);
-      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (residual) qv = *reinterpret_cast<const float4*>(qrow + x);
-      acc += residual_or_p(pv.x, qv.x, residual) + residual_or_p(pv.y, qv.y, residual) +
-             residual_or_p(pv.z, qv.z, residual) + residual_or_p(pv.w, qv.w, residual);
+    constexpr int kIt = kMaxChunkLen / (4 * kThreads);
+    float4 pv[kIt], qv[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int x = min(x0 + 4 * ((int)threadIdx.x + i * kThreads), x1 - 4);
+      pv[i] = *reinterpret_cast<const float4*>(prow + x);
+      qv[i] = residual ? *reinterpret_cast<const float4*>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      if (x0 + 4 * ((int)threadIdx.x + i * kThreads) < x1)
+        acc += residual_or_p(pv[i].x, qv[i].x, residual) + residual_or_p(pv[i].y, qv[i].y, residual) +
+               residual_or_p(pv[i].z, qv[i].z, residual) + residual_or_p(pv[i].w, qv[i].w, residual);
     }
   } else {
-    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) {
-      acc += residual_or_p(prow[x], residual ? qrow[x] : 0.f, residual);
+    constexpr int kIt = kMaxChunkLen / kThreads;
+    float pv[kIt], qv[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int x = min(x0 + (int)threadIdx.x + i * kThreads, x1 - 1);
+      pv[i] = prow[x];
+      qv[i] = residual ? qrow[x] : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i)
+      if (x0 + (int)threadIdx.x + i * kThreads < x1) acc += residual_or_p(pv[i], qv[i], residual);
   }
   return acc;
 }
@@ -134,22 +153,23 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
   const int per = ((len + kThreads - 1) / kThreads + 3) & ~3;   // multiple of 4, <= kSlice
   const int a = x0 + min(len, (int)threadIdx.x * per);
   const int b = x0 + min(len, (int)threadIdx.x * per + per);
+  // every load is issued up front at a clamped in-bounds address; elements past the slice
+  // are masked below (a + j < b)
   float pv[kSlice], qv[kSlice];
 #pragma unroll
   for (int j = 0; j < kSlice; j += 4) {
-    if (VEC4 && a + j + 4 <= b) {
-      const float4 x = *reinterpret_cast<const float4*>(prow + a + j);
-      pv[j] = x.x; pv[j + 1] = x.y; pv[j + 2] = x.z; pv[j + 3] = x.w;
-      if (residual) {
-        const float4 y = *reinterpret_cast<const float4*>(qrow + a + j);
-        qv[j] = y.x; qv[j + 1] = y.y; qv[j + 2] = y.z; qv[j + 3] = y.w;
-      }
+    if (VEC4) {   // chunk and slice lengths are multiples of 4
+      const int x = min(a + j, x1 - 4);
+      const float4 u = *reinterpret_cast<const float4*>(prow + x);
+      const float4 y = residual ? *reinterpret_cast<const float4*>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pv[j] = u.x; pv[j + 1] = u.y; pv[j + 2] = u.z; pv[j + 3] = u.w;
+      qv[j] = y.x; qv[j + 1] = y.y; qv[j + 2] = y.z; qv[j + 3] = y.w;
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int x = a + j + u;
-        pv[j + u] = (x < b) ? prow[x] : 0.f;
-        if (residual) qv[j + u] = (x < b) ? qrow[x] : 0.f;
+        const int x = min(a + j + u, x1 - 1);
+        pv[j + u] = prow[x];
+        qv[j + u] = residual ? qrow[x] : 0.f;
       }
     }
   }
@@ -179,9 +199,12 @@ template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParams P) {
   __shared__ int s_n;
   __shared__ int s_last;
+  __shared__ int s_ids[64];          // draft ids (accepted ones are copied to the output)
+  __shared__ float s_uk;             // u_k, the uniform of the final draw
+  __shared__ double s_loc[2];        // base (sum before the chosen chunk), t
+  __shared__ int s_cstar;
   __shared__ double s_red[kThreads / 64];
   __shared__ int s_int[kThreads / 64];
-  __shared__ double s_cs[kThreads];
 
   const int C = P.C;
   const int b = blockIdx.x / C;
@@ -190,7 +213,8 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const int lane = tid & 63;
   const int k = P.k, V = P.V;
 
-  // 1. accept tests (first wave; k <= 64)
+  // 1. accept tests (first wave; k <= 64); the second wave fetches u_k meanwhile
+  if (tid == 64) s_uk = P.uniforms[(long long)b * (k + 1) + k];
   if (tid < 64) {
     bool reject = false;
     if (lane < k) {
@@ -205,7 +229,9 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
       }
       const double r = (double)P.uniforms[(long long)b * (k + 1) + lane];
       reject = !(pv > 0.f && r * (double)qv <= (double)pv);
+      s_ids[lane] = x;
     }
+
     const unsigned long long m = __ballot(reject);
     if (lane == 0) s_n = m ? (__ffsll((long long)m) - 1) : k;
   }
@@ -235,53 +261,97 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   __syncthreads();
   if (!s_last) return;
 
-  // 4. last workgroup of sequence b: locate t among the chunk sums, then inside one chunk
+  // 4. last workgroup of sequence b: locate t among the chunk sums (one wave, each lane holds
+  // up to four consecutive chunks; C <= 256), then inside one chunk
   if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  double cs = 0.0;
-  if (tid < C) {
-    cs = __longlong_as_double((long long)__hip_atomic_load(
-        reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + tid,
-        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  }
   bool use_res = residual;
   const float* srow_q = qrow;
-  double Z;
-  double before = block_exclusive_scan(cs, s_red, Z);
-  if (!(Z > 0.0)) {
-    // empty residual: draw from p_n itself (recompute its chunk sums here)
+  double Z = 0.0;
+  if (tid < 64) {
+    double cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ci = 4 * lane + j;
+      cs[j] = ci < C ? __longlong_as_double((long long)__hip_atomic_load(
+                           reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + ci,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                     : 0.0;
+    }
+    const double mine = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+    double incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    Z = __shfl(incl, 63);
+    if (Z > 0.0) {
+      const double t = (double)s_uk * Z;
+      // first chunk whose inclusive running sum exceeds t; else (rounding left t at or above
+      // the total) the last chunk with a positive sum
+      double run = incl - mine;
+      int first = INT_MAX, lastnz = -1;
+      double base_first = 0.0, base_last = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ci = 4 * lane + j;
+        if (ci < C && first == INT_MAX && run + cs[j] > t) { first = ci; base_first = run; }
+        if (ci < C && cs[j] > 0.0) { lastnz = ci; base_last = run; }
+        run += cs[j];
+      }
+      const unsigned long long mf = __ballot(first != INT_MAX);
+      const unsigned long long ml = __ballot(lastnz >= 0);
+      if (mf) {
+        const int src = __ffsll((long long)mf) - 1;
+        if (lane == src) { s_cstar = first; s_loc[0] = base_first; s_loc[1] = t; }
+      } else {
+        const int src = 63 - __clzll((long long)ml);
+        if (lane == src) { s_cstar = lastnz; s_loc[0] = base_last; s_loc[1] = t; }
+      }
+    } else if (lane == 0) {
+      s_cstar = -1;
+    }
+  }
+  __syncthreads();
+  int token = 0;
+  int cstar = s_cstar;
+  double base = s_loc[0], t = s_loc[1];
+  if (cstar < 0) {
+    // empty residual: draw from p_n itself (its chunk sums are computed here)
     use_res = false;
     srow_q = prow;
+    double cs = 0.0;
     for (int j = 0; j < C; ++j) {
       const int a = j * P.CS, e = min(V, a + P.CS);
       const double sj = block_sum(chunk_partial<VEC4>(prow, prow, false, a, e), s_red);
       if (tid == j) cs = sj;
     }
-    before = block_exclusive_scan(cs, s_red, Z);
+    double before = block_exclusive_scan(cs, s_red, Z);
+    if (Z > 0.0) {
+      t = (double)s_uk * Z;
+      const int cand = (tid < C && before + cs > t) ? tid : INT_MAX;
+      cstar = block_min(cand, s_int);
+      const int lastnz = block_max((tid < C && cs > 0.0) ? tid : -1, s_int);
+      if (cstar == INT_MAX) cstar = lastnz;
+      if (tid == cstar) s_loc[0] = before;
+      __syncthreads();
+      base = s_loc[0];
+      __syncthreads();
+    } else if (tid == 0) {
+      atomicOr(P.err, VAP_DERR_EMPTY_ROW);
+    }
   }
-  int token = 0;
-  if (Z > 0.0) {
-    const double t = (double)P.uniforms[(long long)b * (k + 1) + k] * Z;
-    // first chunk whose inclusive running sum exceeds t
-    const int cand = (tid < C && before + cs > t) ? tid : INT_MAX;
-    int cstar = block_min(cand, s_int);
-    const int lastnz = block_max((tid < C && cs > 0.0) ? tid : -1, s_int);
-    if (cstar == INT_MAX) cstar = lastnz;   // rounding left t at or above the total
-    if (tid == cstar) s_cs[0] = before;
-    __syncthreads();
-    const double base = s_cs[0];
-    __syncthreads();
+  if (cstar >= 0) {
     const int a = cstar * P.CS, e = min(V, a + P.CS);
     int first_above, last_positive;
     chunk_select<VEC4>(prow, srow_q, use_res, a, e, base, t, s_red, s_int, first_above, last_positive);
     token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
-  } else if (tid == 0) {
-    atomicOr(P.err, VAP_DERR_EMPTY_ROW);
   }
 
   // 5. outputs
   if (tid <= k) {
     int v;
-    if (tid < n) v = P.draft_ids[(long long)b * k + tid];
+    if (tid < n) v = s_ids[tid];
     else if (tid == n) v = token;
     else v = -1;
     P.out_ids[(long long)b * (k + 1) + tid] = v;
