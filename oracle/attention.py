@@ -18,8 +18,15 @@ What is computed (the plain definition; paging is only an address translation):
 * Scores use the scale 1/sqrt(head_dim) unless a scale is given; weights are the softmax of the
   scores over the visible keys; the output is the weighted sum of V rows.
 
+* 8-bit KV [P3 §"Quantization and Precision Choices for KV"]: INT8 KV needs per-head or
+  per-token scale factors and dequantisation inside the attention kernel, with asymmetric
+  quantisation and separate scales for K and V.  Read here as affine uint8 codes with one
+  (scale, zero point) pair per token, KV head and plane: value = scale * (code - zero_point).
+  Attention over such a cache is the plain definition above applied to the dequantised values.
+
 Reading taken where the pages are silent: the scale, the head grouping (contiguous groups) and
-"L counts the new tokens" are the plainest readings consistent with the pages.
+"L counts the new tokens" are the plainest readings consistent with the pages; for 8-bit KV,
+the finer of the two granularities the pages name (per token and head) and the affine form.
 """
 
 from __future__ import annotations
@@ -107,14 +114,31 @@ def paged_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     return out
 
 
-def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables: np.ndarray,
-                         ctx_lens, q_lens, scale: float | None = None, rows=None) -> dict:
-    """Same as ``paged_attention`` from bf16 bit patterns, converting only what is read.
+def dequantize_u8(codes: np.ndarray, scale: np.ndarray, zero_point: np.ndarray) -> np.ndarray:
+    """Affine 8-bit dequantisation in float64: scale * (code - zero_point).
 
-    q_bits [T, Hq, D] uint16; pool_bits [2, NB, bs, Hkv, D] uint16.  ``rows`` optionally
-    restricts the work to a list of (packed row t, head h) pairs; the result maps each computed
-    (t, h) to its [D] float64 output.
+    codes [..., D] uint8; scale, zero_point [...] (one pair per token and KV head).
     """
+    c = np.asarray(codes).astype(np.float64)
+    return np.asarray(scale, np.float64)[..., None] * (c - np.asarray(zero_point, np.float64)[..., None])
+
+
+def gather_sequence_kv_u8(codes: np.ndarray, kv_scales: np.ndarray, table_row: np.ndarray, n_tokens: int):
+    """Dequantised contiguous K and V [n_tokens, Hkv, D] (float64) of one sequence.
+
+    codes [2, NB, bs, Hkv, D] uint8; kv_scales [NB, Hkv, bs, 4] float32 holding
+    (k_scale, k_zero, v_scale, v_zero) per block, KV head and row.
+    """
+    sc = np.transpose(np.asarray(kv_scales), (0, 2, 1, 3))     # [NB, bs, Hkv, 4]
+    s = gather_sequence_kv(sc, table_row, n_tokens)             # [n, Hkv, 4]
+    kc = gather_sequence_kv(codes[0], table_row, n_tokens)      # [n, Hkv, D]
+    vc = gather_sequence_kv(codes[1], table_row, n_tokens)
+    return dequantize_u8(kc, s[..., 0], s[..., 1]), dequantize_u8(vc, s[..., 2], s[..., 3])
+
+
+def _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv) -> dict:
+    """Attention of the requested (packed row, head) pairs; ``sequence_kv(s, L)`` returns the
+    float64 [L, Hkv, D] keys and values of sequence s."""
     T, Hq, D = q_bits.shape
     starts = np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))])
     wanted = None
@@ -128,8 +152,7 @@ def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables
         if wanted is not None and s not in wanted:
             continue
         L, Q, r0 = int(ctx_lens[s]), int(q_lens[s]), int(starts[s])
-        ks = bf16_bits_to_f64(gather_sequence_kv(pool_bits[0], block_tables[s], L))
-        vs = bf16_bits_to_f64(gather_sequence_kv(pool_bits[1], block_tables[s], L))
+        ks, vs = sequence_kv(s, L)
         qs = bf16_bits_to_f64(q_bits[r0:r0 + Q])
         if wanted is None:
             o = attention_sequence(qs, ks, vs, scale)
@@ -141,3 +164,27 @@ def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables
                 o = attention_sequence(qs, ks, vs, scale, heads=[h], rows=[t - r0])
                 result[(t, h)] = o[t - r0, h]
     return result
+
+
+def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables: np.ndarray,
+                         ctx_lens, q_lens, scale: float | None = None, rows=None) -> dict:
+    """Same as ``paged_attention`` from bf16 bit patterns, converting only what is read.
+
+    q_bits [T, Hq, D] uint16; pool_bits [2, NB, bs, Hkv, D] uint16.  ``rows`` optionally
+    restricts the work to a list of (packed row t, head h) pairs; the result maps each computed
+    (t, h) to its [D] float64 output.
+    """
+    def sequence_kv(s, L):
+        return (bf16_bits_to_f64(gather_sequence_kv(pool_bits[0], block_tables[s], L)),
+                bf16_bits_to_f64(gather_sequence_kv(pool_bits[1], block_tables[s], L)))
+    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv)
+
+
+def paged_attention_u8(q_bits: np.ndarray, codes: np.ndarray, kv_scales: np.ndarray,
+                       block_tables: np.ndarray, ctx_lens, q_lens, scale: float | None = None,
+                       rows=None) -> dict:
+    """``paged_attention_bf16`` over an 8-bit KV cache: codes [2, NB, bs, Hkv, D] uint8 and
+    kv_scales [NB, Hkv, bs, 4] float32, dequantised (``dequantize_u8``) as they are read."""
+    def sequence_kv(s, L):
+        return gather_sequence_kv_u8(codes, kv_scales, block_tables[s], L)
+    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv)

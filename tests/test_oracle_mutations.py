@@ -11,6 +11,7 @@ import pytest
 from oracle import attention as A
 from oracle import spec_verify as S
 import tests.test_oracle_attention as TA
+import tests.test_oracle_kv8 as TK
 import tests.test_oracle_spec_verify as TS
 
 GOLDEN = TA.os.path.join(TA.os.path.dirname(TA.os.path.abspath(TA.__file__)), "golden")
@@ -84,6 +85,46 @@ ATTN_MUTANTS = {
 }
 
 
+KV8_PINS = [
+    lambda: TK.test_dequantize_matches_torch_per_channel_affine(0),
+    lambda: TK.test_u8_attention_equals_bf16_attention_on_exact_values(
+        dict(ctx_lens=[1, 17, 40, 64], q_lens=[1, 1, 1, 1], Hq=8, Hkv=2, D=64, bs=16)),
+    lambda: TK.test_u8_attention_equals_bf16_attention_on_exact_values(
+        dict(ctx_lens=[100, 31], q_lens=[1, 8], Hq=6, Hkv=3, D=16, bs=32)),
+    TK.test_u8_block_placement_invariance,
+]
+
+
+def _deq_plus_zero(codes, scale, zero_point):
+    c = np.asarray(codes).astype(np.float64)
+    return np.asarray(scale, np.float64)[..., None] * (c + np.asarray(zero_point, np.float64)[..., None])
+
+
+def _deq_no_zero(codes, scale, zero_point):
+    return np.asarray(scale, np.float64)[..., None] * np.asarray(codes).astype(np.float64)
+
+
+def _gather_u8_variant(k_cols=(0, 1), v_cols=(2, 3), transpose=True):
+    def gather_sequence_kv_u8(codes, kv_scales, table_row, n_tokens):
+        sc = np.asarray(kv_scales)
+        sc = np.transpose(sc, (0, 2, 1, 3)) if transpose else sc
+        s = A.gather_sequence_kv(sc, table_row, n_tokens)
+        kc = A.gather_sequence_kv(codes[0], table_row, n_tokens)
+        vc = A.gather_sequence_kv(codes[1], table_row, n_tokens)
+        return (A.dequantize_u8(kc, s[..., k_cols[0]], s[..., k_cols[1]]),
+                A.dequantize_u8(vc, s[..., v_cols[0]], s[..., v_cols[1]]))
+    return gather_sequence_kv_u8
+
+
+KV8_MUTANTS = {
+    "zero point added": ("dequantize_u8", _deq_plus_zero),
+    "zero point dropped": ("dequantize_u8", _deq_no_zero),
+    "K scales used for V": ("gather_sequence_kv_u8", _gather_u8_variant(v_cols=(0, 1))),
+    "scale and zero swapped": ("gather_sequence_kv_u8", _gather_u8_variant(k_cols=(1, 0))),
+    "scale layout not transposed": ("gather_sequence_kv_u8", _gather_u8_variant(transpose=False)),
+}
+
+
 def _any_pin_fails(pins):
     for pin in pins:
         try:
@@ -99,6 +140,13 @@ def test_attention_mutant_is_caught(name, monkeypatch):
     attr, fn = ATTN_MUTANTS[name]
     monkeypatch.setattr(A, attr, fn)
     assert _any_pin_fails(ATTN_PINS), f"no attention pin caught: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(KV8_MUTANTS))
+def test_kv8_mutant_is_caught(name, monkeypatch):
+    attr, fn = KV8_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    assert _any_pin_fails(KV8_PINS), f"no 8-bit KV pin caught: {name}"
 
 
 SPEC_PINS = [
@@ -186,5 +234,7 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     mutant is caught for its mistake and not for the scaffolding."""
     monkeypatch.setattr(A, "attention_sequence", _seq_variant())
     monkeypatch.setattr(S, "verify_sequence", _verify_variant())
+    monkeypatch.setattr(A, "gather_sequence_kv_u8", _gather_u8_variant())
     assert not _any_pin_fails(ATTN_PINS)
     assert not _any_pin_fails(SPEC_PINS)
+    assert not _any_pin_fails(KV8_PINS)

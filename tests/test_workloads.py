@@ -70,3 +70,25 @@ def test_verify_inputs_shapes_and_uniforms():
     v2 = W.verify_config("tiny")
     assert torch.equal(v.p, v2.p) and torch.equal(v.draft_ids, v2.draft_ids)
     assert torch.equal(v.uniforms, v2.uniforms)
+
+
+def test_u8_inputs_share_lengths_and_tables_and_poison_scales_only():
+    a = W.attention_config("tiny")
+    b = W.attention_config("tiny", kv_format="u8")
+    assert torch.equal(a.ctx_lens, b.ctx_lens) and torch.equal(a.q_lens, b.q_lens)
+    assert torch.equal(a.q, b.q)                       # q is drawn before the pool
+    assert b.kv_pool.dtype == torch.uint8 and b.kv_pool.shape == a.kv_pool.shape
+    NB, bs, Hkv = b.num_blocks, b.block_size, b.num_kv_heads
+    assert b.kv_scales.shape == (NB, Hkv, bs, 4) and b.kv_scales.dtype == torch.float32
+    sc = b.kv_scales.numpy()
+    tables = b.block_tables.numpy()
+    owned = np.zeros((NB, bs), bool)
+    for s in range(b.num_seqs):
+        L = int(b.ctx_lens[s])
+        for j in range(L):
+            owned[tables[s, j // bs], j % bs] = True
+    live = sc.transpose(0, 2, 1, 3)[owned]              # [n_owned, Hkv, 4]
+    assert np.isfinite(live).all()
+    assert ((live[..., 0] >= 0.01) & (live[..., 0] <= 0.03)).all()
+    assert ((live[..., 1] >= 112) & (live[..., 1] <= 143) & (live[..., 1] == np.round(live[..., 1]))).all()
+    assert np.isnan(sc.transpose(0, 2, 1, 3)[~owned]).all()

@@ -13,6 +13,13 @@ Pool slots that no sequence owns, and the rows of a sequence's last block past L
 overwritten with a poison value (NaN by default) so that any read past ``ctx_len`` shows up.
 Unused block-table entries are -1.
 
+8-bit KV inputs (``kv_format="u8"``) replace step 3 by
+  3a. codes for every pool slot, uint8 = clip(round(N(128, 40)), 0, 255),
+  3b. per (block, KV head, token) the four fp32 numbers (k_scale, k_zero, v_scale, v_zero):
+      scales uniform in [0.01, 0.03], zero points integers uniform in [112, 143].
+They are drawn directly in that shape (no quantiser runs here); the scales of unowned slots and
+of rows past L_s are poisoned instead of the codes.
+
 Speculative-verification inputs, in draw order:
   1. logits (target rows [B, k+1, V], draft rows [B, k, V]) per the config,
   2. draft tokens x_i ~ q_i (one categorical draw per draft position),
@@ -41,6 +48,8 @@ class AttnInputs:
 
     q            bf16  [T, Hq, D]     rows packed by sequence, in sequence order
     kv_pool      bf16  [2, NB, bs, Hkv, D]   plane 0 = K, plane 1 = V
+                 (uint8 codes of the same shape when kv_scales is set)
+    kv_scales    None, or fp32 [NB, Hkv, bs, 4] = (k_scale, k_zero, v_scale, v_zero) per token
     block_tables int32 [B, MB]        logical block -> physical block, -1 padded
     ctx_lens     int32 [B]            L_s, counting this step's Q_s new tokens
     q_lens       int32 [B]            Q_s (1 = decode, k+1 = verify, chunk = prefill)
@@ -57,6 +66,11 @@ class AttnInputs:
     num_kv_heads: int
     head_dim: int
     block_size: int
+    kv_scales: torch.Tensor | None = None
+
+    @property
+    def kv_format(self) -> str:
+        return "bf16" if self.kv_scales is None else "u8"
 
     @property
     def num_seqs(self) -> int:
@@ -120,6 +134,26 @@ def _normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
     return out.view(*shape)
 
 
+def _codes_u8(rng: np.random.Generator, shape) -> torch.Tensor:
+    """uint8 codes clip(round(N(128, 40)), 0, 255), drawn in chunks."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.uint8)
+    for start in range(0, n, _CHUNK):
+        stop = min(n, start + _CHUNK)
+        x = np.clip(np.rint(128.0 + 40.0 * rng.standard_normal(stop - start, dtype=np.float32)), 0, 255)
+        out[start:stop] = torch.from_numpy(x.astype(np.uint8))
+    return out.view(*shape)
+
+
+def _scales_u8(rng: np.random.Generator, shape) -> torch.Tensor:
+    """[..., 4] fp32 (k_scale, k_zero, v_scale, v_zero): scales U[0.01, 0.03], zeros U{112..143}."""
+    n = int(np.prod(shape))
+    sc = rng.uniform(0.01, 0.03, size=(n, 2)).astype(np.float32)
+    zp = rng.integers(112, 143, size=(n, 2), endpoint=True).astype(np.float32)
+    out = np.stack([sc[:, 0], zp[:, 0], sc[:, 1], zp[:, 1]], axis=1)
+    return torch.from_numpy(out).view(*shape, 4)
+
+
 def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
     """Uniforms in the open interval (0, 1): (j + 1/2) / 2^24, exactly representable in fp32."""
     j = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
@@ -156,6 +190,7 @@ def make_attention_inputs(
     poison: float = float("nan"),
     rng: np.random.Generator | None = None,
     name: str = "custom",
+    kv_format: str = "bf16",
 ) -> AttnInputs:
     """Build one paged batch from given lengths (steps 2-4 of the draw order above).
 
@@ -183,7 +218,14 @@ def make_attention_inputs(
     T = int(Q.sum())
 
     q = _normal_bf16(rng, (T, num_q_heads, head_dim))
-    pool = _normal_bf16(rng, (2, NB, bs, num_kv_heads, head_dim))
+    scales = None
+    if kv_format == "bf16":
+        pool = _normal_bf16(rng, (2, NB, bs, num_kv_heads, head_dim))
+    elif kv_format == "u8":
+        pool = _codes_u8(rng, (2, NB, bs, num_kv_heads, head_dim))
+        scales = _scales_u8(rng, (NB, num_kv_heads, bs))
+    else:
+        raise ValueError(f"kv_format {kv_format!r}")
     perm = rng.permutation(NB)
 
     tables = np.full((B, MB), -1, dtype=np.int32)
@@ -196,10 +238,16 @@ def make_attention_inputs(
         owned[ids] = True
         tail = int(L[s] % bs)
         if tail:
-            pool[:, int(ids[-1]), tail:] = poison
+            if scales is None:
+                pool[:, int(ids[-1]), tail:] = poison
+            else:
+                scales[int(ids[-1]), :, tail:] = poison
     unused = np.nonzero(~owned)[0]
     if unused.size:
-        pool[:, torch.from_numpy(unused)] = poison
+        if scales is None:
+            pool[:, torch.from_numpy(unused)] = poison
+        else:
+            scales[torch.from_numpy(unused)] = poison
 
     return AttnInputs(
         name=name,
@@ -213,6 +261,7 @@ def make_attention_inputs(
         num_kv_heads=num_kv_heads,
         head_dim=head_dim,
         block_size=bs,
+        kv_scales=scales,
     )
 
 
@@ -256,7 +305,8 @@ def config_lengths(name: str, seed: int | None = None):
     return L, Q, _ATTN_SHAPES[name]
 
 
-def attention_config(name: str, seed: int | None = None, poison: float = float("nan")) -> AttnInputs:
+def attention_config(name: str, seed: int | None = None, poison: float = float("nan"),
+                     kv_format: str = "bf16") -> AttnInputs:
     """The five named attention workloads (lengths drawn first, then make_attention_inputs).
 
     tiny              4 decode seqs, L = {17, 64, 100, 255}, 8 q / 2 kv heads, D 64, bs 16
@@ -268,7 +318,8 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
     mixed_step        128 decode + 32 verify (q_len 5) + 4 prefill chunks (q_len 256);
                       decode/verify L lognormal(1024, 1) clipped [16, 4096], prefill L uniform
                       in [256, 4096]; 32/8 heads, D 128, bs 32; pool 95% full; order shuffled
-    All other pools hold ceil(1.2 x live blocks).
+    All other pools hold ceil(1.2 x live blocks).  ``kv_format="u8"`` gives the same lengths
+    and shapes with 8-bit codes and per-token scales.
     """
     if seed is None:
         seed = DEFAULT_SEEDS[name]
@@ -281,7 +332,8 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
         pool_blocks = int(math.ceil(live / 0.95))
     return make_attention_inputs(seed, ctx_lens=L, q_lens=Q, num_q_heads=Hq, num_kv_heads=Hkv,
                                  head_dim=D, block_size=bs, max_ctx=max_ctx,
-                                 pool_blocks=pool_blocks, poison=poison, rng=rng, name=name)
+                                 pool_blocks=pool_blocks, poison=poison, rng=rng, name=name,
+                                 kv_format=kv_format)
 
 
 # ----------------------------------------------------------------------------------------
