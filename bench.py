@@ -60,6 +60,17 @@ def attn_bytes(ctx_lens, q_lens, Hq, Hkv, D, bs) -> int:
     return total
 
 
+def attn_bytes_u8(ctx_lens, q_lens, Hq, Hkv, D, bs) -> int:
+    """Algorithmic bytes of one step over an 8-bit KV cache: one code per K and V element,
+    16 bytes of (scale, zero) pairs per token and KV head, q, out, block ids, lengths."""
+    total = 0
+    for L, Q in zip(ctx_lens, q_lens):
+        total += 2 * L * Hkv * D + 16 * L * Hkv
+        total += 2 * Q * Hq * D + 4 * Q * Hq * D
+        total += 4 * ((L + bs - 1) // bs) + 8
+    return total
+
+
 def verify_bytes(n_accepted, k, V) -> int:
     total = 0
     for n in n_accepted:
@@ -113,18 +124,23 @@ def rotating_copies(t, min_bytes):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def setup_attention(name, dev):
+def setup_attention(name, dev, kv_format="bf16"):
+    """Device inputs of a named workload; the KV pool (and for 8-bit KV its scales) is copied
+    until the copies span at least 1 GiB, so consecutive steps never hit in the 256 MB MALL."""
     import torch
     import workloads
     import verify_attention_paged_amd as vap
-    inp = workloads.attention_config(name)
+    inp = workloads.attention_config(name, kv_format=kv_format)
     d = dict(q=inp.q.to(dev), block_tables=inp.block_tables.to(dev), ctx_lens=inp.ctx_lens.to(dev),
              q_lens=inp.q_lens.to(dev))
     pools = rotating_copies(inp.kv_pool.to(dev), 1 << 30)
+    scales = [inp.kv_scales.to(dev) for _ in pools] if inp.kv_scales is not None else None
     out = torch.empty(inp.q.shape, dtype=torch.float32, device=dev)
     ws = vap.attn_workspace(vap.attn_shape(d["q"], pools[0], d["block_tables"]), dev)
-    nbytes = attn_bytes(inp.ctx_lens.tolist(), inp.q_lens.tolist(), inp.num_q_heads, inp.num_kv_heads,
-                        inp.head_dim, inp.block_size)
+    size = attn_bytes_u8 if inp.kv_scales is not None else attn_bytes
+    nbytes = size(inp.ctx_lens.tolist(), inp.q_lens.tolist(), inp.num_q_heads, inp.num_kv_heads,
+                  inp.head_dim, inp.block_size)
+    d["scales"] = scales
     return inp, d, pools, out, ws, nbytes
 
 
@@ -190,9 +206,11 @@ def run_copy(args, dev):
 
 def run_attention_only(args, dev, name):
     import verify_attention_paged_amd as vap
-    inp, d, pools, out, ws, nbytes = setup_attention(name, dev)
+    inp, d, pools, out, ws, nbytes = setup_attention(name, dev, args.kv_format)
+    sc = d["scales"]
     step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
-                                         d["q_lens"], out=out, workspace=ws)
+                                         d["q_lens"], out=out, workspace=ws,
+                                         kv_scales=None if sc is None else sc[i % len(pools)])
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
@@ -200,7 +218,8 @@ def run_attention_only(args, dev, name):
     kms, cnt = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_enable(False)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    print(json.dumps({"mode": "attn-only", "workload": name, "bytes": nbytes, "ms_per_step": round(ms, 5),
+    print(json.dumps({"mode": "attn-only", "workload": name, "kv_format": args.kv_format, "bytes": nbytes,
+                      "ms_per_step": round(ms, 5),
                       "GB_per_s": round(gbs, 2), "kernel_ms": round(kms / max(cnt, 1), 5),
                       "kernel_GB_per_s": round(nbytes / (kms / max(cnt, 1) * 1e-3) / 1e9, 2)}))
 
@@ -263,6 +282,24 @@ def run_default(args, dev):
         f"-> {sv_bytes / (sv_kernel_ms * 1e-3) / 1e9:.1f} GB/s; verify attention kernel "
         f"{vattn_ms / max(1, c0) * 1e3:.1f} us -> {vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9:.1f} GB/s")
 
+    # ---- decode step over an 8-bit KV cache (same lengths and shapes)
+    qinp, qd, qpools, qout, qws, qnbytes = setup_attention("llama3_8b_decode", dev, kv_format="u8")
+    qstep = lambda i: vap.paged_attn_step(qd["q"], qpools[i % len(qpools)], qd["block_tables"], qd["ctx_lens"],
+                                          qd["q_lens"], out=qout, workspace=qws,
+                                          kv_scales=qd["scales"][i % len(qpools)])
+    vap.timer_enable(True)
+    time_loop(qstep, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    qms, _ = time_loop(qstep, args.steps, 0)
+    qk_total, qk_count = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    vap.timer_enable(False)
+    if vap.get_device_error(qws):
+        raise RuntimeError("device reported a data error on the 8-bit decode batch")
+    qkernel_ms = qk_total / max(1, qk_count)
+    log(f"8-bit KV decode step {qms * 1e3:.1f} us ({ms / qms:.2f}x the bf16 step) -> "
+        f"{qnbytes / (qms * 1e-3) / 1e9:.1f} GB/s of {qnbytes / 1e6:.1f} MB; attention kernel "
+        f"{qkernel_ms * 1e3:.1f} us -> {qnbytes / (qkernel_ms * 1e-3) / 1e9:.1f} GB/s")
+
     # ---- CPU baseline (oracle), rank 0 at N = 1 only
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,6 +333,12 @@ def run_default(args, dev):
                         "spec_verify_kernel_ms": round(sv_kernel_ms, 5),
                         "spec_verify_GB_per_s": round(sv_bytes / (sv_kernel_ms * 1e-3) / 1e9, 2),
                         "spec_verify_bytes": sv_bytes},
+        "kv8_decode_step": {"workload": "llama3_8b_decode with uint8 K/V codes and per-token (scale, zero) "
+                                        "pairs, dequantised in the kernel",
+                            "ms_per_step": round(qms, 5), "bytes_per_step": qnbytes,
+                            "GB_per_s": round(qnbytes / (qms * 1e-3) / 1e9, 2),
+                            "attention_kernel_ms": round(qkernel_ms, 5),
+                            "speedup_vs_bf16_step": round(ms / qms, 3)},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attn_main_kernel<128,16,1>",
@@ -312,6 +355,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["default", "copy", "attn-only", "verify-only"], default="default")
     ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--kv-format", choices=["bf16", "u8"], default="bf16", help="KV cache format (attn-only mode)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

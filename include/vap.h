@@ -118,6 +118,24 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
                     const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * paged_attn_step_u8 -- paged_attn_step over an 8-bit KV cache, dequantised inside the kernel
+ * (tempatgunting.com article, section "Quantization and Precision Choices for KV": INT8 KV with
+ * per-token or per-head scale factors, asymmetric, separate scales for K and V).
+ *
+ *   kv_codes   uint8 [2][num_blocks][block_size][Hkv][D]; plane 0 holds K, plane 1 holds V.
+ *   kv_scales  fp32 [num_blocks][Hkv][block_size][4] = (k_scale, k_zero, v_scale, v_zero) for
+ *              each cached token and KV head.  The value of code c is scale * (c - zero).
+ *
+ * Everything else (shape, q, tables, lengths, out, workspace and its size, errors) is as for
+ * paged_attn_step; the same workspace serves both.  All pointers 16-byte aligned.  Scales of
+ * rows past ctx_len are never read.
+ */
+int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scales,
+                       const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
+                       float* out, const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Workspace bytes spec_verify needs (0 on bad sizes). */
 size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);
 

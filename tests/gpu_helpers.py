@@ -20,9 +20,14 @@ def device():
 
 
 def to_device(inp: workloads.AttnInputs, dev=None):
+    """Device copies of the inputs as keyword arguments of ``vap.paged_attn_step`` (with
+    ``kv_scales`` for an 8-bit cache)."""
     dev = dev or device()
-    return dict(q=inp.q.to(dev), kv_pool=inp.kv_pool.to(dev), block_tables=inp.block_tables.to(dev),
-                ctx_lens=inp.ctx_lens.to(dev), q_lens=inp.q_lens.to(dev))
+    d = dict(q=inp.q.to(dev), kv_pool=inp.kv_pool.to(dev), block_tables=inp.block_tables.to(dev),
+             ctx_lens=inp.ctx_lens.to(dev), q_lens=inp.q_lens.to(dev))
+    if inp.kv_scales is not None:
+        d["kv_scales"] = inp.kv_scales.to(dev)
+    return d
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -31,6 +36,10 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 
 def oracle_rows(inp: workloads.AttnInputs, rows=None, scale=None) -> dict:
+    if inp.kv_scales is not None:
+        return OA.paged_attention_u8(bits(inp.q), inp.kv_pool.numpy(), inp.kv_scales.numpy(),
+                                     inp.block_tables.numpy(), inp.ctx_lens.numpy(), inp.q_lens.numpy(),
+                                     scale=scale, rows=rows)
     return OA.paged_attention_bf16(bits(inp.q), bits(inp.kv_pool), inp.block_tables.numpy(),
                                    inp.ctx_lens.numpy(), inp.q_lens.numpy(), scale=scale, rows=rows)
 
@@ -75,5 +84,5 @@ def sample_rows(inp: workloads.AttnInputs, n: int, seed: int = 0):
 
 
 @functools.lru_cache(maxsize=None)
-def config_inputs(name: str) -> workloads.AttnInputs:
-    return workloads.attention_config(name)
+def config_inputs(name: str, kv_format: str = "bf16") -> workloads.AttnInputs:
+    return workloads.attention_config(name, kv_format=kv_format)

@@ -20,7 +20,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = vap.header_functions()
-    assert {"paged_attn_step", "spec_verify", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
+    assert {"paged_attn_step", "paged_attn_step_u8", "spec_verify", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
             "vap_get_device_error", "vap_strerror"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -60,6 +60,16 @@ def test_attention_null_pointers_and_empty_batch(lib):
     assert lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
     bad_empty = _shape(num_seqs=0, total_q=3)
     assert lib.paged_attn_step(None, None, None, None, None, None, ctypes.byref(bad_empty), None, 0, None) == B.VAP_EINVAL
+
+
+def test_u8_attention_null_pointers_and_empty_batch(lib):
+    s = B.AttnShape(4, 8, 2, 64, 16, 35, 16, 4, 0.0)
+    fake = ctypes.c_void_p(16)        # never dereferenced: the host check fails first
+    assert lib.paged_attn_step_u8(None, None, None, None, None, None, None, ctypes.byref(s), None, 0, None) == B.VAP_EINVAL
+    # codes given but no scales
+    assert lib.paged_attn_step_u8(fake, fake, None, fake, fake, fake, fake, ctypes.byref(s), fake, 1 << 20, None) == B.VAP_EINVAL
+    empty = B.AttnShape(0, 8, 2, 64, 16, 35, 16, 0, 0.0)
+    assert lib.paged_attn_step_u8(None, None, None, None, None, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
 
 
 def test_workspace_sizes_are_consistent(lib):

@@ -49,6 +49,7 @@ SIGNATURES = {
     "vap_attn_workspace_bytes": (_sz, [_pshape]),
     "vap_attn_workspace_min_bytes": (_sz, [_pshape]),
     "paged_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
+    "paged_attn_step_u8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
@@ -141,20 +142,26 @@ def attn_workspace(shape: AttnShape, device=None) -> torch.Tensor:
 
 
 def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale: float = 0.0,
-                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                    workspace: torch.Tensor | None = None, stream=None, kv_scales=None) -> torch.Tensor:
     """Paged attention for one ragged batch; see ``paged_attn_step`` in include/vap.h.
 
     q bf16 [T, Hq, D]; kv_pool bf16 [2, NB, bs, Hkv, D]; block_tables int32 [B, MB];
-    ctx_lens, q_lens int32 [B]; returns out fp32 [T, Hq, D].
+    ctx_lens, q_lens int32 [B]; returns out fp32 [T, Hq, D].  With ``kv_scales`` (fp32
+    [NB, Hkv, bs, 4]) the pool holds uint8 codes and ``paged_attn_step_u8`` is called.
     """
     lib = load_library()
     dev = q.device
+    kv8 = kv_scales is not None
     _need(q, "q", torch.bfloat16, 3)
-    _need(kv_pool, "kv_pool", torch.bfloat16, 5, dev)
+    _need(kv_pool, "kv_pool", torch.uint8 if kv8 else torch.bfloat16, 5, dev)
     _need(block_tables, "block_tables", torch.int32, 2, dev)
     _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
     _need(q_lens, "q_lens", torch.int32, 1, dev)
     shape = attn_shape(q, kv_pool, block_tables, scale)
+    if kv8:
+        _need(kv_scales, "kv_scales", torch.float32, 4, dev)
+        if tuple(kv_scales.shape) != (shape.num_blocks, shape.num_kv_heads, shape.block_size, 4):
+            raise ValueError("kv_scales must be [num_blocks, Hkv, block_size, 4]")
     if ctx_lens.numel() != shape.num_seqs or q_lens.numel() != shape.num_seqs:
         raise ValueError("ctx_lens and q_lens need one entry per block-table row")
     if out is None:
@@ -166,10 +173,16 @@ def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, sca
         workspace = attn_workspace(shape, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
     with torch.cuda.device(dev):
-        rc = lib.paged_attn_step(q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),
-                                 ctx_lens.data_ptr(), q_lens.data_ptr(), out.data_ptr(),
-                                 ctypes.byref(shape), workspace.data_ptr(), workspace.numel(),
-                                 _stream(stream))
+        if kv8:
+            rc = lib.paged_attn_step_u8(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr(),
+                                        block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
+                                        out.data_ptr(), ctypes.byref(shape), workspace.data_ptr(),
+                                        workspace.numel(), _stream(stream))
+        else:
+            rc = lib.paged_attn_step(q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),
+                                     ctx_lens.data_ptr(), q_lens.data_ptr(), out.data_ptr(),
+                                     ctypes.byref(shape), workspace.data_ptr(), workspace.numel(),
+                                     _stream(stream))
     _check(rc)
     return out
 

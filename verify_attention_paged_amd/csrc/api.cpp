@@ -38,7 +38,7 @@ struct DevInfo {
   bool gfx950 = false;
   int num_cus = 0;
   char arch[64] = {0};
-  int attn_occ[2][2][2] = {};   // workgroups per CU of the attention kernel [D128][BS32][NRT2]
+  int attn_occ[2][2][2][2] = {};   // workgroups per CU of the attention kernel [D128][BS32][NRT2][KV8]
 };
 
 constexpr int kMaxDevices = 64;
@@ -58,17 +58,18 @@ const DevInfo* device_info() {
     d.gfx950 = std::strncmp(d.arch, "gfx950", 6) == 0;
     for (int a = 0; a < 2; ++a)
       for (int b = 0; b < 2; ++b)
-        for (int c = 0; c < 2; ++c) {
-          int nb = 0;
-          // occupancy with the largest in-workgroup plan (LDS never binds before registers)
-          const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1, true);
-          if (f == nullptr ||
-              hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads,
-                                                            attn_main_lds_bytes(kLdsPlanMaxSeqs)) != hipSuccess ||
-              nb < 1)
-            nb = 1;
-          d.attn_occ[a][b][c] = nb;
-        }
+        for (int c = 0; c < 2; ++c)
+          for (int k8 = 0; k8 < 2; ++k8) {
+            int nb = 0;
+            // occupancy with the largest in-workgroup plan (LDS never binds before registers)
+            const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1, true, k8 != 0);
+            if (f == nullptr ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads,
+                                                              attn_main_lds_bytes(kLdsPlanMaxSeqs)) != hipSuccess ||
+                nb < 1)
+              nb = 1;
+            d.attn_occ[a][b][c][k8] = nb;
+          }
     d.probed = true;
   }
   return &d;
@@ -109,6 +110,8 @@ int unit_setup_blocks(int block_size) { return VAP_UNIT_SETUP_TILES * 16 / block
 
 struct AttnPlanChoice {
   int D, BS, NRT, RG, G;
+  bool kv8;
+  int rows_per_seq;   // total_q / num_seqs, rounded down
 };
 
 int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
@@ -127,6 +130,8 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
                 s->max_blocks_per_seq);
   if (s->total_q < 0) return fail(VAP_EINVAL, "total_q=%d < 0", s->total_q);
   if (!(std::isfinite(s->scale) && s->scale >= 0.f)) return fail(VAP_EINVAL, "scale must be finite and >= 0");
+  c->kv8 = false;
+  c->rows_per_seq = s->num_seqs > 0 ? s->total_q / s->num_seqs : 0;
   c->D = s->head_dim;
   c->BS = s->block_size;
   c->G = s->num_q_heads / s->num_kv_heads;
@@ -145,14 +150,15 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
   return VAP_OK;
 }
 
-// Worker waves: one per SIMD (one workgroup of four per CU).  Each wave keeps two tiles in
-// flight; at that depth the memory system is already saturated for this access pattern, so
-// more waves only add latency to every dependent load (and partials to merge).
-constexpr int kWorkgroupsPerCU = 1;
-
+// Worker waves: one per SIMD (one workgroup of four per CU) for decode- and verify-shaped
+// batches.  Each wave keeps two tiles in flight; at that depth the memory system is already
+// saturated for this access pattern, so more waves only add latency to every dependent load
+// (and partials to merge).  Batches averaging 8 or more query rows per sequence (prefill
+// chunks) make the MFMA work per byte large enough that a second wave per SIMD pays.
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
-  const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2];
-  return std::min(kMaxWaves, d->num_cus * std::min(occ, kWorkgroupsPerCU) * kWavesPerWG);
+  const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2][c.kv8 ? 1 : 0];
+  const int per_cu = c.rows_per_seq >= 8 ? 2 : 1;
+  return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * kWavesPerWG);
 }
 
 }  // namespace
@@ -186,23 +192,28 @@ size_t vap_attn_workspace_min_bytes(const vap_attn_shape* shape) {
   return attn_layout(shape->num_seqs, kWavesPerWG, c.RG, c.D).total;
 }
 
-int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tables,
-                    const int32_t* ctx_lens, const int32_t* q_lens, float* out,
-                    const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
-                    void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the bf16 and 8-bit entry points: kv_scales == nullptr selects the bf16 pool.
+int attn_step(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,
+              const int32_t* ctx_lens, const int32_t* q_lens, float* out, const vap_attn_shape* shape,
+              void* workspace, size_t workspace_bytes, void* stream_, bool kv8) {
   AttnPlanChoice c;
   int rc = check_attn_shape(shape, &c);
   if (rc != VAP_OK) return rc;
+  c.kv8 = kv8;
   const vap_attn_shape& s = *shape;
   if (s.num_seqs == 0) {
     if (s.total_q != 0) return fail(VAP_EINVAL, "num_seqs=0 but total_q=%d", s.total_q);
     return ok();
   }
-  if (!q || !kv_pool || !block_tables || !ctx_lens || !q_lens || !out || !workspace)
+  if (!q || !kv || !block_tables || !ctx_lens || !q_lens || !out || !workspace || (kv8 && !kv_scales))
     return fail(VAP_EINVAL, "NULL data pointer");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv_pool) |
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(kv_scales) |
        reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
-    return fail(VAP_EINVAL, "q, kv_pool, out and workspace must be 16-byte aligned");
+    return fail(VAP_EINVAL, "q, the KV pool, its scales, out and workspace must be 16-byte aligned");
   const DevInfo* d = device_info();
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
 
@@ -225,8 +236,12 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
 
   AttnParams P;
   P.q = static_cast<const uint16_t*>(q);
-  P.kpool = static_cast<const uint16_t*>(kv_pool);
-  P.vpool = P.kpool + (size_t)s.num_blocks * s.block_size * s.num_kv_heads * s.head_dim;
+  const size_t plane = (size_t)s.num_blocks * s.block_size * s.num_kv_heads * s.head_dim;
+  P.kpool = kv8 ? nullptr : static_cast<const uint16_t*>(kv);
+  P.vpool = kv8 ? nullptr : P.kpool + plane;
+  P.kcodes = kv8 ? static_cast<const uint8_t*>(kv) : nullptr;
+  P.vcodes = kv8 ? P.kcodes + plane : nullptr;
+  P.kv_scales = kv8 ? kv_scales : nullptr;
   P.tables = block_tables;
   P.ctx_lens = ctx_lens;
   P.q_lens = q_lens;
@@ -261,12 +276,32 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
     if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
   }
   timer_begin(0, stream);
-  e = launch_attn_main(P, c.D, c.BS, c.NRT, W / kWavesPerWG, stream);
+  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / kWavesPerWG, stream);
   timer_end(0, stream);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
   e = launch_attn_combine(P, c.D, stream);
   if (e != hipSuccess) return fail(VAP_EHIP, "combine launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tables,
+                    const int32_t* ctx_lens, const int32_t* q_lens, float* out,
+                    const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return attn_step(q, kv_pool, nullptr, block_tables, ctx_lens, q_lens, out, shape, workspace,
+                   workspace_bytes, stream, false);
+}
+
+int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scales,
+                       const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
+                       float* out, const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return attn_step(q, kv_codes, kv_scales, block_tables, ctx_lens, q_lens, out, shape, workspace,
+                   workspace_bytes, stream, true);
 }
 
 size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {

@@ -163,10 +163,23 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
 //   16-bit word jt of its four V loads, and its P^T operand is exactly its four S^T values.
 constexpr int kTile = 16;
 
+template <int D, bool KV8>
+struct KVTile;
+
 template <int D>
-struct KVTile {
+struct KVTile<D, false> {
   bf16x8 ka[D / 32];
   uint32_t vw[4][D / 32];
+};
+
+// 8-bit cache: lane (c, g) holds the K codes of token c, dims (D/4) g .. +D/4-1; the V codes of
+// tokens 4g + r, dims (D/16) c .. +D/16-1; and (k_scale, k_zero, v_scale, v_zero) of tokens
+// 4g + r (r = 0..3).
+template <int D>
+struct KVTile<D, true> {
+  uint32_t kc[D / 16];
+  uint32_t vc[4][D / 64];
+  float4 sc[4];
 };
 
 // Raw buffer loads: the tile's block base lives in a buffer resource in scalar registers (it
@@ -178,7 +191,7 @@ constexpr int kBufFlags = 0x00020000;   // raw (untyped) dword access
 
 // base and bytes are uniform over the wave; readfirstlane states it, so the resource stays in
 // scalar registers (a resource the compiler thinks divergent costs a loop around every load)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
@@ -190,7 +203,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
 // A tile that is not live gets an empty range: its loads return zeros without a memory access,
 // which lets the pipelined loop issue loads unconditionally.
 template <int D, int BS>
-__device__ __forceinline__ void load_tile(KVTile<D>& t, const uint16_t* kbase, const uint16_t* vbase,
+__device__ __forceinline__ void load_tile(KVTile<D, false>& t, const uint16_t* kbase, const uint16_t* vbase,
                                           long long tok_stride, int tg, int blk, int vo_k, int vo_v, bool live) {
   constexpr int NKK = D / 32;
   const long long row0 = (long long)blk * BS + (tg % BS);
@@ -211,6 +224,37 @@ __device__ __forceinline__ void load_tile(KVTile<D>& t, const uint16_t* kbase, c
       t.vw[r][0] = x[0]; t.vw[r][1] = x[1];
     }
   }
+}
+
+// 8-bit tile: codes and scales through buffer resources built from the wave-uniform block
+// base (empty range when the tile is not live).  vo_k = c * tok_bytes + (D/4) g,
+// vo_v = 4 g * tok_bytes + (D/16) c, vo_s = 64 g; sblk = floats per block of the scale array.
+template <int D, int BS>
+__device__ __forceinline__ void load_tile8(KVTile<D, true>& t, const uint8_t* kbase, const uint8_t* vbase,
+                                           const float* sbase, long long sblk, int tok_bytes, int tg, int blk,
+                                           int vo_k, int vo_v, int vo_s, bool live) {
+  const long long row0 = (long long)blk * BS + (tg % BS);
+  const int range = live ? kTile * tok_bytes : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0 * tok_bytes, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * tok_bytes, range);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase + (long long)blk * sblk + (tg % BS) * 4, live ? kTile * 16 : 0);
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k + 16 * h, 0, 0);
+    t.kc[4 * h] = x[0]; t.kc[4 * h + 1] = x[1]; t.kc[4 * h + 2] = x[2]; t.kc[4 * h + 3] = x[3];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (D == 128) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, vo_v, r * tok_bytes, 0);
+      t.vc[r][0] = x[0]; t.vc[r][1] = x[1];
+    } else {
+      t.vc[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo_v, r * tok_bytes, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    t.sc[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_s, 16 * r, 0));
 }
 
 // Max over the four lanes {c, c+16, c+32, c+48} holding one row: two lane swaps (odd/even
@@ -235,7 +279,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int NRT, bool MASKED>
-__device__ __forceinline__ void compute_tile(const KVTile<D>& t, int tg, int t_end, const int (&lim)[NRT],
+__device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, int t_end, const int (&lim)[NRT],
                                              const bf16x8 (&qb)[NRT][D / 32], float scale_log2,
                                              float (&m_run)[NRT], float (&l_run)[NRT],
                                              f32x4 (&acc)[NRT][D / 16], int g) {
@@ -311,6 +355,113 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, int tg, int t_e
   }
 }
 
+// Sum over the four lanes {c, c+16, c+32, c+48} holding one row (fixed order).
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// byte i of w as a float (an 8-bit code is exact in fp32 and in bf16)
+__device__ __forceinline__ float code_f32(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xffu); }
+
+// One tile of the 8-bit cache.  With x = s (c - z) per token: the score of token j is
+// s_k,j (q.c_j - z_k,j sum(q)), so the K codes go to the MFMA as they are (exact in bf16) and
+// the per-token scale is applied to the 16 scores; the output is
+// sum_j p_j s_v,j c_j - sum_j p_j s_v,j z_v,j, so P is scaled by s_v per token and the second
+// sum is kept per row (o_run, subtracted at the end).
+template <int D, int NRT, bool MASKED>
+__device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, int t_end, const int (&lim)[NRT],
+                                              const bf16x8 (&qb)[NRT][D / 32], const float (&qsum)[NRT],
+                                              float scale_log2, float (&m_run)[NRT], float (&l_run)[NRT],
+                                              float (&o_run)[NRT], f32x4 (&acc)[NRT][D / 16], int g) {
+  constexpr int NKK = D / 32;
+  constexpr int NJT = D / 16;
+  bf16x8 ka[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const uint32_t w0 = t.kc[2 * kk], w1 = t.kc[2 * kk + 1];
+    const uint4 u = make_uint4(pack_bf16(code_f32(w0, 0), code_f32(w0, 1)), pack_bf16(code_f32(w0, 2), code_f32(w0, 3)),
+                               pack_bf16(code_f32(w1, 0), code_f32(w1, 1)), pack_bf16(code_f32(w1, 2), code_f32(w1, 3)));
+    ka[kk] = as_bf16x8(u);
+  }
+  float sv[NRT][4];
+  bool ok[NRT][4];
+  float mx[NRT];
+  bool grow = false;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    f32x4 raw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) raw = mfma16x16x32(ka[kk], qb[rt][kk], raw);
+    float m = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[rt][r] = t.sc[r].x * fmaf(-t.sc[r].y, qsum[rt], raw[r]);
+      if (MASKED) {
+        const int tok = tg + 4 * g + r;
+        ok[rt][r] = (tok < t_end) && (tok <= lim[rt]);
+        m = ok[rt][r] ? fmaxf(m, sv[rt][r]) : m;
+      } else {
+        m = fmaxf(m, sv[rt][r]);
+      }
+    }
+    mx[rt] = row_max4(m) * scale_log2;
+    grow = grow || (mx[rt] > m_run[rt] + kRescaleLog2);
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // uniform branch
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const float m_new = fmaxf(m_run[rt], mx[rt]);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[rt] - m_new);
+      l_run[rt] *= alpha;
+      o_run[rt] *= alpha;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] *= alpha;
+      m_run[rt] = m_new;
+    }
+  }
+  uint2 ph[NRT], pl[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const float ref = (m_run[rt] == kNegInf) ? 0.f : m_run[rt];
+    float pv[4], pw[4];
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = fast_exp2(sv[rt][r] * scale_log2 - ref);
+      pw[r] = pv[r] * t.sc[r].z;
+      float oz = pw[r] * t.sc[r].w;
+      if (MASKED) {
+        pv[r] = ok[rt][r] ? pv[r] : 0.f;
+        pw[r] = ok[rt][r] ? pw[r] : 0.f;
+        oz = ok[rt][r] ? oz : 0.f;
+      }
+      o += oz;
+    }
+    l_run[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    o_run[rt] += o;
+    const uint32_t h01 = pack_bf16(pw[0], pw[1]), h23 = pack_bf16(pw[2], pw[3]);
+    const uint32_t l01 = pack_bf16(pw[0] - __uint_as_float(h01 << 16), pw[1] - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = pack_bf16(pw[2] - __uint_as_float(h23 << 16), pw[3] - __uint_as_float(h23 & 0xffff0000u));
+    ph[rt] = make_uint2(h01, h23);
+    pl[rt] = make_uint2(l01, l23);
+  }
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt) {
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = code_f32(t.vc[r][jt >> 2], jt & 3);
+    const uint2 vt = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      acc[rt][jt] = mfma16x16x16(vt, ph[rt], acc[rt][jt]);
+      acc[rt][jt] = mfma16x16x16(vt, pl[rt], acc[rt][jt]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // one segment: a contiguous block range of one unit
 // ---------------------------------------------------------------------------------------
@@ -367,7 +518,7 @@ __device__ __forceinline__ void unit_rows(const AttnParams& P, int kvh, int rg, 
   }
 }
 
-template <int D, int BS, int NRT>
+template <int D, int BS, int NRT, bool KV8>
 __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, int W, int TB,
                                 int lane, int c, int g, SplitDesc& desc) {
   constexpr int NKK = D / 32;
@@ -382,34 +533,51 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   const long long tok_stride = (long long)P.Hkv * D;
   const uint16_t* kbase = P.kpool + (long long)sg.kvh * D;
   const uint16_t* vbase = P.vpool + (long long)sg.kvh * D;
-  const int vo_k = c * (int)tok_stride * 2 + 16 * g;
-  const int vo_v = 4 * g * (int)tok_stride * 2 + 2 * (D / 16) * c;
+  const int vo_k = KV8 ? c * (int)tok_stride + (D / 4) * g : c * (int)tok_stride * 2 + 16 * g;
+  const int vo_v = KV8 ? 4 * g * (int)tok_stride + (D / 16) * c : 4 * g * (int)tok_stride * 2 + 2 * (D / 16) * c;
   const int jend = sg.ub + sg.seg;
+  // 8-bit cache: codes have the bf16 pool's shape with one byte per element
+  const uint8_t* kbase8 = KV8 ? P.kcodes + (long long)sg.kvh * D : nullptr;
+  const uint8_t* vbase8 = KV8 ? P.vcodes + (long long)sg.kvh * D : nullptr;
+  const float* sbase8 = KV8 ? P.kv_scales + (long long)sg.kvh * BS * 4 : nullptr;
+  const long long sblk = (long long)P.Hkv * BS * 4;
+  const int vo_s = 64 * g;
 
   int out_row[NRT];
   int nrows;
   unit_rows<D, NRT>(P, sg.kvh, sg.rg, sg.Q, sg.qoff, c, out_row, nrows);
 
   // query rows of this unit as B operands: lane holds row rt*16+c, dims 32*kk + 8*g .. +7
+  // (8-bit cache: dims (D/4)*g + 8*kk .. +7, matching the K code layout), and for the 8-bit
+  // cache the row sums of q (the zero points' term of the scores)
   bf16x8 qb[NRT][NKK];
+  float qsum[NRT];
   int lim[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     lim[rt] = sg.L - sg.Q + (row0 + rt * 16 + c) / G;
-    const uint16_t* qp = P.q + (long long)(out_row[rt] >= 0 ? out_row[rt] : 0) * D + 8 * g;
+    const uint16_t* qp = P.q + (long long)(out_row[rt] >= 0 ? out_row[rt] : 0) * D + (KV8 ? (D / 4) * g : 8 * g);
+    float qs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 v = out_row[rt] >= 0 ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      const uint4 v = out_row[rt] >= 0 ? ld16(qp + (KV8 ? 8 * kk : 32 * kk)) : make_uint4(0, 0, 0, 0);
       qb[rt][kk] = as_bf16x8(v);
+      if constexpr (KV8) {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qs += __uint_as_float(wv[e] << 16) + __uint_as_float(wv[e] & 0xffff0000u);
+      }
     }
+    qsum[rt] = KV8 ? row_sum4(qs) : 0.f;
   }
 
-  float m_run[NRT], l_run[NRT];
+  float m_run[NRT], l_run[NRT], o_run[NRT];
   f32x4 acc[NRT][NJT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     m_run[rt] = kNegInf;
     l_run[rt] = 0.f;
+    o_run[rt] = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -438,15 +606,22 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     }
     const int nt = min(kWinTiles, ntiles - wt);
     const int tw0 = t_start + wt * kTile;          // first token of the window
-    auto issue = [&](KVTile<D>& X, int i, bool live) {
+    auto issue = [&](KVTile<D, KV8>& X, int i, bool live) {
       const int ic = min(i, nt - 1);
       const int tg = tw0 + ic * kTile;
-      load_tile<D, BS>(X, kbase, vbase, tok_stride, tg, __builtin_amdgcn_readlane(win, tg / BS - wbase), vo_k, vo_v,
-                       live);
+      const int blk = __builtin_amdgcn_readlane(win, tg / BS - wbase);
+      if constexpr (KV8)
+        load_tile8<D, BS>(X, kbase8, vbase8, sbase8, sblk, (int)tok_stride, tg, blk, vo_k, vo_v, vo_s, live);
+      else
+        load_tile<D, BS>(X, kbase, vbase, tok_stride, tg, blk, vo_k, vo_v, live);
     };
-    auto compute = [&](const KVTile<D>& X, int i, auto masked) {
-      compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, P.scale_log2, m_run,
-                                                    l_run, acc, g);
+    auto compute = [&](const KVTile<D, KV8>& X, int i, auto masked) {
+      if constexpr (KV8)
+        compute_tile8<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, qsum, P.scale_log2,
+                                                       m_run, l_run, o_run, acc, g);
+      else
+        compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, P.scale_log2, m_run,
+                                                      l_run, acc, g);
     };
     // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
     // which would make the compiler keep a second copy of the accumulators.  The unmasked loop
@@ -455,7 +630,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     // compiler never has to drain the load counter at a branch.
     const int nu = min(nt, max(0, n_unmasked - wt));
     if (nu > 0) {
-      KVTile<D> ta, tb;
+      KVTile<D, KV8> ta, tb;
       issue(ta, 0, true);
       int i = 0;
       for (; i + 1 < nu; i += 2) {    // both tiles of a pair are always computed
@@ -471,7 +646,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
       if (i < nu) compute(ta, i, std::false_type{});
     }
     for (int i = nu; i < nt; ++i) {
-      KVTile<D> t0;
+      KVTile<D, KV8> t0;
       issue(t0, i, true);
       compute(t0, i, std::true_type{});
     }
@@ -485,6 +660,11 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     lsum[rt] = l;
+    if constexpr (KV8) {            // subtract the zero points' share from every output dim
+      const float osum = row_sum4(o_run[rt]);
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] -= osum;
+    }
   }
   if (sg.whole) {
     write_rows<D, NRT>(P.out, out_row, acc, lsum, g);
@@ -521,7 +701,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   }
 }
 
-template <int D, int BS, int NRT, bool LDS_PLAN>
+template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
 __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_ATTN_WAVES_2RT) void attn_main_kernel(const AttnParams P) {
   extern __shared__ int s_mem[];
   const int lane = threadIdx.x & 63;
@@ -587,7 +767,7 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
     sg.rg = sg.unit - sg.kvh * nrg;
     sg.whole = (sg.ub == 0) && (sg.seg == sg.nb);
     sg.slot = first ? 0 : 1;
-    process_segment<D, BS, NRT>(P, sg, w, W, TB, lane, c, g, desc);
+    process_segment<D, BS, NRT, KV8>(P, sg, w, W, TB, lane, c, g, desc);
     pos += sg.seg;
     first = false;
   }
@@ -598,10 +778,10 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
   }
 }
 
-template <int D, int BS, int NRT, bool LDS_PLAN>
+template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
 hipError_t launch_main_t(const AttnParams& p, int num_wg, hipStream_t stream) {
   const size_t lds = LDS_PLAN ? attn_main_lds_bytes(p.B) : 0;
-  hipLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN>), dim3(num_wg), dim3(kAttnThreads), lds, stream, p);
+  hipLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(kAttnThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -613,22 +793,30 @@ size_t attn_main_lds_bytes(int B) { return size_t(4 * B + 1) * sizeof(int); }
   X(64, 16, 1) X(64, 16, 2) X(64, 32, 1) X(64, 32, 2) \
   X(128, 16, 1) X(128, 16, 2) X(128, 32, 1) X(128, 32, 2)
 
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int num_wg, hipStream_t stream) {
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream) {
   const bool lds = p.B <= kLdsPlanMaxSeqs;
-#define X(d, bs, nrt)                                                          \
-  if (D == d && BS == bs && NRT == nrt)                                        \
-    return lds ? launch_main_t<d, bs, nrt, true>(p, num_wg, stream)            \
-               : launch_main_t<d, bs, nrt, false>(p, num_wg, stream);
+#define X(d, bs, nrt)                                                                         \
+  if (D == d && BS == bs && NRT == nrt) {                                                     \
+    if (kv8)                                                                                  \
+      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, stream)                   \
+                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, stream);                 \
+    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, stream)                    \
+               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, stream);                  \
+  }
   VAP_ATTN_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
 }
 
-const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan) {
-#define X(d, bs, nrt)                                                                        \
-  if (D == d && BS == bs && NRT == nrt)                                                      \
-    return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true>)     \
-                    : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false>);
+const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8) {
+#define X(d, bs, nrt)                                                                          \
+  if (D == d && BS == bs && NRT == nrt) {                                                      \
+    if (kv8)                                                                                   \
+      return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, true>) \
+                      : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, true>); \
+    return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, false>) \
+                    : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, false>); \
+  }
   VAP_ATTN_VARIANTS(X)
 #undef X
   return nullptr;

@@ -69,6 +69,9 @@ struct AttnParams {
   const uint16_t* q;        // bf16 [T][Hq][D]
   const uint16_t* kpool;    // bf16 [NB][BS][Hkv][D]
   const uint16_t* vpool;    // bf16 [NB][BS][Hkv][D]
+  const uint8_t* kcodes;    // 8-bit cache: uint8 [NB][BS][Hkv][D] codes of K and of V
+  const uint8_t* vcodes;
+  const float* kv_scales;   // 8-bit cache: fp32 [NB][Hkv][BS][4] (k_scale, k_zero, v_scale, v_zero)
   const int32_t* tables;    // [B][MB]
   const int32_t* ctx_lens;  // [B]
   const int32_t* q_lens;    // [B]
@@ -124,9 +127,9 @@ struct VerifyParams {
 
 // launchers (defined in the .hip files); return hipError_t of the launch
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int num_wg, hipStream_t stream);
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
-const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan);
+const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
