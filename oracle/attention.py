@@ -18,6 +18,12 @@ What is computed (the plain definition; paging is only an address translation):
 * Scores use the scale 1/sqrt(head_dim) unless a scale is given; weights are the softmax of the
   scores over the visible keys; the output is the weighted sum of V rows.
 
+* Tree-masked verification [P4 §"4. Tree Attention & Medusa Heads"; P3 §"Draft Model
+  Selection and Tree-Style Variants"]: the draft is a token tree verified in one pass under a
+  tree attention mask.  Read here as: a sequence's Q new rows are the tree's nodes in an order
+  where every node follows its ancestors; node i sees the committed prefix (keys
+  0 .. L - Q - 1) and the nodes j whose bit j is set in its mask (its ancestors and itself).
+  A chain (mask_i = bits 0..i) is the causal verify above.
 * 8-bit KV [P3 §"Quantization and Precision Choices for KV"]: INT8 KV needs per-head or
   per-token scale factors and dequantisation inside the attention kernel, with asymmetric
   quantisation and separate scales for K and V.  Read here as affine uint8 codes with one
@@ -71,12 +77,23 @@ def attend_row(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: f
     return (w @ values) / w.sum()
 
 
+def visible_keys(L: int, Q: int, i: int, tree_mask=None) -> np.ndarray:
+    """Key positions row i of a sequence may attend: the causal range 0 .. L-Q+i, or with a
+    tree mask the prefix 0 .. L-Q-1 plus L-Q+j for every bit j set in tree_mask[i]."""
+    if tree_mask is None:
+        return np.arange(L - Q + i + 1)
+    m = int(tree_mask[i])
+    nodes = [j for j in range(Q) if (m >> j) & 1]
+    return np.concatenate([np.arange(L - Q), L - Q + np.asarray(nodes, dtype=np.int64)]).astype(np.int64)
+
+
 def attention_sequence(q_seq: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
-                       scale: float | None = None, heads=None, rows=None) -> np.ndarray:
+                       scale: float | None = None, heads=None, rows=None, tree_mask=None) -> np.ndarray:
     """Attention for one sequence with contiguous KV.
 
-    q_seq [Q, Hq, D]; k_seq, v_seq [L, Hkv, D] (float64).  Returns [Q, Hq, D] float64
-    (entries not requested through ``rows`` / ``heads`` are left as NaN).
+    q_seq [Q, Hq, D]; k_seq, v_seq [L, Hkv, D] (float64); tree_mask optional [Q] integers
+    (``visible_keys``).  Returns [Q, Hq, D] float64 (entries not requested through ``rows`` /
+    ``heads`` are left as NaN).
     """
     Q, Hq, D = q_seq.shape
     L, Hkv, _ = k_seq.shape
@@ -89,10 +106,13 @@ def attention_sequence(q_seq: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
         scale = 1.0 / np.sqrt(D)
     out = np.full((Q, Hq, D), np.nan)
     for i in (range(Q) if rows is None else rows):
-        visible = L - Q + i + 1          # keys 0 .. L-Q+i
+        if tree_mask is None:
+            sel = slice(0, L - Q + i + 1)    # keys 0 .. L-Q+i
+        else:
+            sel = visible_keys(L, Q, i, tree_mask)
         for h in (range(Hq) if heads is None else heads):
             g = h // G
-            out[i, h] = attend_row(q_seq[i, h], k_seq[:visible, g], v_seq[:visible, g], scale)
+            out[i, h] = attend_row(q_seq[i, h], k_seq[sel, g], v_seq[sel, g], scale)
     return out
 
 
@@ -136,9 +156,9 @@ def gather_sequence_kv_u8(codes: np.ndarray, kv_scales: np.ndarray, table_row: n
     return dequantize_u8(kc, s[..., 0], s[..., 1]), dequantize_u8(vc, s[..., 2], s[..., 3])
 
 
-def _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv) -> dict:
+def _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask=None) -> dict:
     """Attention of the requested (packed row, head) pairs; ``sequence_kv(s, L)`` returns the
-    float64 [L, Hkv, D] keys and values of sequence s."""
+    float64 [L, Hkv, D] keys and values of sequence s; ``tree_mask`` [T] per packed row."""
     T, Hq, D = q_bits.shape
     starts = np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))])
     wanted = None
@@ -154,20 +174,21 @@ def _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv) -> dict:
         L, Q, r0 = int(ctx_lens[s]), int(q_lens[s]), int(starts[s])
         ks, vs = sequence_kv(s, L)
         qs = bf16_bits_to_f64(q_bits[r0:r0 + Q])
+        tm = None if tree_mask is None else np.asarray(tree_mask)[r0:r0 + Q]
         if wanted is None:
-            o = attention_sequence(qs, ks, vs, scale)
+            o = attention_sequence(qs, ks, vs, scale, tree_mask=tm)
             for i in range(Q):
                 for h in range(Hq):
                     result[(r0 + i, h)] = o[i, h]
         else:
             for t, h in wanted[s]:
-                o = attention_sequence(qs, ks, vs, scale, heads=[h], rows=[t - r0])
+                o = attention_sequence(qs, ks, vs, scale, heads=[h], rows=[t - r0], tree_mask=tm)
                 result[(t, h)] = o[t - r0, h]
     return result
 
 
 def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables: np.ndarray,
-                         ctx_lens, q_lens, scale: float | None = None, rows=None) -> dict:
+                         ctx_lens, q_lens, scale: float | None = None, rows=None, tree_mask=None) -> dict:
     """Same as ``paged_attention`` from bf16 bit patterns, converting only what is read.
 
     q_bits [T, Hq, D] uint16; pool_bits [2, NB, bs, Hkv, D] uint16.  ``rows`` optionally
@@ -177,14 +198,14 @@ def paged_attention_bf16(q_bits: np.ndarray, pool_bits: np.ndarray, block_tables
     def sequence_kv(s, L):
         return (bf16_bits_to_f64(gather_sequence_kv(pool_bits[0], block_tables[s], L)),
                 bf16_bits_to_f64(gather_sequence_kv(pool_bits[1], block_tables[s], L)))
-    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv)
+    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask)
 
 
 def paged_attention_u8(q_bits: np.ndarray, codes: np.ndarray, kv_scales: np.ndarray,
                        block_tables: np.ndarray, ctx_lens, q_lens, scale: float | None = None,
-                       rows=None) -> dict:
+                       rows=None, tree_mask=None) -> dict:
     """``paged_attention_bf16`` over an 8-bit KV cache: codes [2, NB, bs, Hkv, D] uint8 and
     kv_scales [NB, Hkv, bs, 4] float32, dequantised (``dequantize_u8``) as they are read."""
     def sequence_kv(s, L):
         return gather_sequence_kv_u8(codes, kv_scales, block_tables[s], L)
-    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv)
+    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask)

@@ -13,6 +13,7 @@ from oracle import spec_verify as S
 import tests.test_oracle_attention as TA
 import tests.test_oracle_kv8 as TK
 import tests.test_oracle_spec_verify as TS
+import tests.test_oracle_tree as TT
 
 GOLDEN = TA.os.path.join(TA.os.path.dirname(TA.os.path.abspath(TA.__file__)), "golden")
 
@@ -29,8 +30,8 @@ ATTN_PINS = [
 ]
 
 
-def _seq_variant(scale_fn=None, visible_fn=None, head_fn=None, row_fn=None):
-    def attention_sequence(q_seq, k_seq, v_seq, scale=None, heads=None, rows=None):
+def _seq_variant(scale_fn=None, visible_fn=None, head_fn=None, row_fn=None, tree_fn=None):
+    def attention_sequence(q_seq, k_seq, v_seq, scale=None, heads=None, rows=None, tree_mask=None):
         Q, Hq, D = q_seq.shape
         L, Hkv, _ = k_seq.shape
         if Hq % Hkv or not 1 <= Q <= L:
@@ -40,12 +41,15 @@ def _seq_variant(scale_fn=None, visible_fn=None, head_fn=None, row_fn=None):
             scale = scale_fn(D) if scale_fn else 1.0 / np.sqrt(D)
         out = np.full((Q, Hq, D), np.nan)
         for i in (range(Q) if rows is None else rows):
-            vis = visible_fn(L, Q, i) if visible_fn else L - Q + i + 1
-            vis = max(1, min(L, vis))
+            if tree_mask is None:
+                vis = visible_fn(L, Q, i) if visible_fn else L - Q + i + 1
+                sel = slice(0, max(1, min(L, vis)))
+            else:
+                sel = tree_fn(L, Q, i, tree_mask) if tree_fn else A.visible_keys(L, Q, i, tree_mask)
             for h in (range(Hq) if heads is None else heads):
                 g = head_fn(h, G, Hkv) if head_fn else h // G
                 f = row_fn or A.attend_row
-                out[i, h] = f(q_seq[i, h], k_seq[:vis, g], v_seq[:vis, g], scale)
+                out[i, h] = f(q_seq[i, h], k_seq[sel, g], v_seq[sel, g], scale)
         return out
     return attention_sequence
 
@@ -125,6 +129,30 @@ KV8_MUTANTS = {
 }
 
 
+TREE_PINS = [
+    lambda: TT.test_chain_mask_is_the_causal_verify(5),
+    lambda: TT.test_each_node_equals_the_causal_verify_of_its_path(0),
+    lambda: TT.test_each_node_equals_the_causal_verify_of_its_path(1),
+    TT.test_single_node_tree_is_a_decode_row,
+]
+
+
+def _tree_nodes(L, Q, i, tree_mask, shift=0, self_bit=True):
+    m = int(tree_mask[i])
+    if not self_bit:
+        m &= ~(1 << i)
+    return [j for j in range(Q) if (m >> (j + shift)) & 1]
+
+
+TREE_MUTANTS = {
+    "tree: node does not see itself": lambda L, Q, i, tm: np.concatenate(
+        [np.arange(L - Q), L - Q + np.array(_tree_nodes(L, Q, i, tm, self_bit=False), dtype=np.int64)]).astype(np.int64),
+    "tree: prefix dropped": lambda L, Q, i, tm: (L - Q + np.array(_tree_nodes(L, Q, i, tm), dtype=np.int64)),
+    "tree: mask bits off by one": lambda L, Q, i, tm: np.concatenate(
+        [np.arange(L - Q), L - Q + np.array(_tree_nodes(L, Q, i, tm, shift=1), dtype=np.int64)]).astype(np.int64),
+}
+
+
 def _any_pin_fails(pins):
     for pin in pins:
         try:
@@ -140,6 +168,12 @@ def test_attention_mutant_is_caught(name, monkeypatch):
     attr, fn = ATTN_MUTANTS[name]
     monkeypatch.setattr(A, attr, fn)
     assert _any_pin_fails(ATTN_PINS), f"no attention pin caught: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(TREE_MUTANTS))
+def test_tree_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(A, "attention_sequence", _seq_variant(tree_fn=TREE_MUTANTS[name]))
+    assert _any_pin_fails(TREE_PINS), f"no tree pin caught: {name}"
 
 
 @pytest.mark.parametrize("name", sorted(KV8_MUTANTS))
@@ -238,3 +272,4 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     assert not _any_pin_fails(ATTN_PINS)
     assert not _any_pin_fails(SPEC_PINS)
     assert not _any_pin_fails(KV8_PINS)
+    assert not _any_pin_fails(TREE_PINS)

@@ -8,7 +8,8 @@ rejection-sampling arithmetic, so both the CPU oracle (``oracle/``) and the HIP 
 Shapes and distributions follow the workloads described for continuous-batching serving
 steps: long-tailed (lognormal / Pareto) context lengths, 16- or 32-token KV blocks placed at
 non-contiguous pool slots through a per-sequence block table, GQA head groups, and
-speculative drafts of k tokens verified with k+1 query rows.
+speculative drafts of k tokens verified with k+1 query rows, or token trees verified under
+their ancestor masks.
 """
 
 from .generate import (  # noqa: F401
@@ -22,4 +23,6 @@ from .generate import (  # noqa: F401
     DEFAULT_SEEDS,
     verify_config,
     open_uniforms,
+    random_tree_parents,
+    tree_masks,
 )

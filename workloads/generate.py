@@ -36,7 +36,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-CONFIG_NAMES = ("tiny", "llama3_8b_decode", "spec_verify_step", "llama70b_share", "mixed_step")
+CONFIG_NAMES = ("tiny", "llama3_8b_decode", "spec_verify_step", "llama70b_share", "mixed_step",
+                "tree_verify_step")
 DEFAULT_SEEDS = {name: 1001 + i for i, name in enumerate(CONFIG_NAMES)}
 
 _CHUNK = 1 << 24  # values drawn per numpy call when filling large pools
@@ -50,6 +51,8 @@ class AttnInputs:
     kv_pool      bf16  [2, NB, bs, Hkv, D]   plane 0 = K, plane 1 = V
                  (uint8 codes of the same shape when kv_scales is set)
     kv_scales    None, or fp32 [NB, Hkv, bs, 4] = (k_scale, k_zero, v_scale, v_zero) per token
+    tree_mask    None, or int64 [T] (the bits of a uint64): bit j of a sequence's row i set when
+                 row i may attend the sequence's new row j (tree verification)
     block_tables int32 [B, MB]        logical block -> physical block, -1 padded
     ctx_lens     int32 [B]            L_s, counting this step's Q_s new tokens
     q_lens       int32 [B]            Q_s (1 = decode, k+1 = verify, chunk = prefill)
@@ -67,6 +70,7 @@ class AttnInputs:
     head_dim: int
     block_size: int
     kv_scales: torch.Tensor | None = None
+    tree_mask: torch.Tensor | None = None
 
     @property
     def kv_format(self) -> str:
@@ -158,6 +162,27 @@ def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
     """Uniforms in the open interval (0, 1): (j + 1/2) / 2^24, exactly representable in fp32."""
     j = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
     return ((j.astype(np.float64) + 0.5) / float(1 << 24)).astype(np.float32)
+
+
+def random_tree_parents(rng: np.random.Generator, n: int) -> np.ndarray:
+    """A random recursive tree of n nodes in topological order: node 0 is the root (parent -1),
+    node i > 0 hangs under a parent drawn uniformly from 0 .. i-1."""
+    par = np.full(n, -1, dtype=np.int64)
+    for i in range(1, n):
+        par[i] = rng.integers(0, i)
+    return par
+
+
+def tree_masks(parents) -> np.ndarray:
+    """Ancestor masks of a tree in topological order: bit j of entry i is set when node j is
+    node i or one of its ancestors.  Returned as int64 holding the uint64 bit pattern."""
+    par = np.asarray(parents, dtype=np.int64)
+    n = par.size
+    assert n <= 64 and all(par[i] < i for i in range(n))
+    masks = [0] * n
+    for i in range(n):
+        masks[i] = (1 << i) | (masks[par[i]] if par[i] >= 0 else 0)
+    return np.array(masks, dtype=np.uint64).view(np.int64)
 
 
 def _lognormal_lengths(rng, n, median, sigma, lo, hi):
@@ -272,6 +297,7 @@ _ATTN_SHAPES = {
     "spec_verify_step": (32, 8, 128, 16, 4096),
     "llama70b_share": (64, 8, 128, 16, 32768),
     "mixed_step": (32, 8, 128, 32, 4096),
+    "tree_verify_step": (32, 8, 128, 16, 4096),
 }
 
 
@@ -293,6 +319,8 @@ def _config_lengths(name: str, rng: np.random.Generator):
         Q = np.concatenate([np.ones(128, np.int64), np.full(32, 5, np.int64), np.full(4, 256, np.int64)])
         order = rng.permutation(L.size)
         return L[order], Q[order]
+    if name == "tree_verify_step":
+        return rng.integers(512, 4096, size=16, endpoint=True), np.full(16, 16, np.int64)
     raise KeyError(name)
 
 
@@ -313,6 +341,8 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
     llama3_8b_decode  64 decode seqs, L lognormal(median 1024, sigma 1) clipped [16, 8192],
                       32 q / 8 kv heads, D 128, bs 16, pool 1.2x live blocks
     spec_verify_step  16 verify seqs (q_len 5), L uniform in [512, 4096], 32/8 heads, D 128
+    tree_verify_step  16 seqs verifying 16-node token trees (random recursive trees, drawn after
+                      the pool), L uniform in [512, 4096], 32/8 heads, D 128
     llama70b_share    256 decode seqs, L Pareto(alpha 1.5, min 128) capped at 32768,
                       64 q / 8 kv heads, D 128, bs 16
     mixed_step        128 decode + 32 verify (q_len 5) + 4 prefill chunks (q_len 256);
@@ -330,10 +360,14 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
     if name == "mixed_step":
         live = int(((L + bs - 1) // bs).sum())
         pool_blocks = int(math.ceil(live / 0.95))
-    return make_attention_inputs(seed, ctx_lens=L, q_lens=Q, num_q_heads=Hq, num_kv_heads=Hkv,
-                                 head_dim=D, block_size=bs, max_ctx=max_ctx,
-                                 pool_blocks=pool_blocks, poison=poison, rng=rng, name=name,
-                                 kv_format=kv_format)
+    inp = make_attention_inputs(seed, ctx_lens=L, q_lens=Q, num_q_heads=Hq, num_kv_heads=Hkv,
+                                head_dim=D, block_size=bs, max_ctx=max_ctx,
+                                pool_blocks=pool_blocks, poison=poison, rng=rng, name=name,
+                                kv_format=kv_format)
+    if name == "tree_verify_step":
+        inp.tree_mask = torch.from_numpy(np.concatenate([tree_masks(random_tree_parents(rng, int(q)))
+                                                         for q in Q]))
+    return inp
 
 
 # ----------------------------------------------------------------------------------------
