@@ -141,6 +141,7 @@ def setup_attention(name, dev, kv_format="bf16"):
     nbytes = size(inp.ctx_lens.tolist(), inp.q_lens.tolist(), inp.num_q_heads, inp.num_kv_heads,
                   inp.head_dim, inp.block_size)
     d["scales"] = scales
+    d["tree_mask"] = inp.tree_mask.to(dev) if inp.tree_mask is not None else None
     return inp, d, pools, out, ws, nbytes
 
 
@@ -210,7 +211,8 @@ def run_attention_only(args, dev, name):
     sc = d["scales"]
     step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
                                          d["q_lens"], out=out, workspace=ws,
-                                         kv_scales=None if sc is None else sc[i % len(pools)])
+                                         kv_scales=None if sc is None else sc[i % len(pools)],
+                                         tree_mask=d["tree_mask"])
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)

@@ -63,6 +63,9 @@ extern "C" {
 #define VAP_DERR_TOTAL_Q 0x4   /* sum of q_lens differs from total_q                          */
 #define VAP_DERR_DRAFT_ID 0x8  /* draft id outside [0, vocab)                                  */
 #define VAP_DERR_EMPTY_ROW 0x10 /* the row to sample from has no positive weight              */
+#define VAP_DERR_TREE 0x20      /* tree mask without the row's own bit or with bits past it, or
+                                   a tree of more than 64 rows (the row is then repaired: own
+                                   bit set, later bits cleared; or kept causal)              */
 
 /*
  * Shape of one attention step.
@@ -135,6 +138,28 @@ int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scal
                        const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
                        float* out, const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * paged_attn_step_tree -- paged_attn_step where each sequence's q_len new rows are the nodes of
+ * a draft token tree verified in one pass under a tree attention mask (neuralmasteryai.com
+ * "Continuous Batching & Speculative Decoding", section "4. Tree Attention & Medusa Heads").
+ *
+ *   tree_mask  uint64 [total_q], 8-byte aligned.  Nodes are numbered 0 .. q_len-1 within their
+ *              sequence in an order where ancestors come first; node i sits at position
+ *              L - q_len + i.  Bit j of node i's mask is set when node i attends node j: its
+ *              ancestors and itself (so only bits 0 .. i).  Every node also attends the whole
+ *              committed prefix, positions 0 .. L - q_len - 1.  A chain (mask of node i =
+ *              bits 0 .. i) is the causal verify of paged_attn_step.  q_len <= 64.
+ *   kv, kv_scales  a bf16 pool as for paged_attn_step when kv_scales is NULL, else 8-bit codes
+ *              and their scales as for paged_attn_step_u8.
+ *
+ * A mask without its own bit or with bits past its node, or a sequence of more than 64 rows,
+ * sets VAP_DERR_TREE; the row then uses its mask with its own bit set and later bits cleared
+ * (or stays causal past 64 rows).  Everything else is as for paged_attn_step.
+ */
+int paged_attn_step_tree(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,
+                         const int32_t* ctx_lens, const int32_t* q_lens, const uint64_t* tree_mask, float* out,
+                         const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes spec_verify needs (0 on bad sizes). */
 size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);

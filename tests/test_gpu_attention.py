@@ -160,6 +160,18 @@ def test_bad_block_id_sets_error_without_fault():
     assert vap.get_device_error(ws) == 0
 
 
+def test_bad_block_id_deep_in_a_long_context_is_reported():
+    """The error is flagged whichever lane of a wave reads the bad table entry."""
+    inp = _case(14, [2000, 900], [1, 1], 8, 2, 64, 16)
+    d = H.to_device(inp)
+    d["block_tables"][0, 77] = -3                       # negative: outside the pool
+    ws = vap.attn_workspace(vap.attn_shape(d["q"], d["kv_pool"], d["block_tables"]), H.device())
+    out = vap.paged_attn_step(d["q"], d["kv_pool"], d["block_tables"], d["ctx_lens"], d["q_lens"], workspace=ws)
+    assert vap.get_device_error(ws, clear=True) & vap.DERR_BLOCK_ID
+    H.assert_close_rows(out[1:], {(t - 1, h): v for (t, h), v in H.oracle_rows(inp).items() if t == 1},
+                        "untouched seq")
+
+
 def test_bad_lengths_set_error_and_spare_other_sequences():
     inp = _case(13, [40, 40, 40], [1, 1, 1], 8, 2, 64, 16)
     d = H.to_device(inp)

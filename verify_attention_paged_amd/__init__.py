@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     DERR_TOTAL_Q,
     DERR_DRAFT_ID,
     DERR_EMPTY_ROW,
+    DERR_TREE,
     TIMER_ATTENTION,
     TIMER_VERIFY,
     attn_shape,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libv
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vap.h")
 
 VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
-DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW = 0x1, 0x2, 0x4, 0x8, 0x10
+DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 TIMER_ATTENTION, TIMER_VERIFY = 0, 1
 
 
@@ -50,6 +50,7 @@ SIGNATURES = {
     "vap_attn_workspace_min_bytes": (_sz, [_pshape]),
     "paged_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "paged_attn_step_u8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
+    "paged_attn_step_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
@@ -142,12 +143,14 @@ def attn_workspace(shape: AttnShape, device=None) -> torch.Tensor:
 
 
 def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale: float = 0.0,
-                    workspace: torch.Tensor | None = None, stream=None, kv_scales=None) -> torch.Tensor:
+                    workspace: torch.Tensor | None = None, stream=None, kv_scales=None,
+                    tree_mask=None) -> torch.Tensor:
     """Paged attention for one ragged batch; see ``paged_attn_step`` in include/vap.h.
 
     q bf16 [T, Hq, D]; kv_pool bf16 [2, NB, bs, Hkv, D]; block_tables int32 [B, MB];
     ctx_lens, q_lens int32 [B]; returns out fp32 [T, Hq, D].  With ``kv_scales`` (fp32
-    [NB, Hkv, bs, 4]) the pool holds uint8 codes and ``paged_attn_step_u8`` is called.
+    [NB, Hkv, bs, 4]) the pool holds uint8 codes and ``paged_attn_step_u8`` is called.  With
+    ``tree_mask`` (int64 [T] holding uint64 ancestor masks) ``paged_attn_step_tree`` is called.
     """
     lib = load_library()
     dev = q.device
@@ -164,6 +167,10 @@ def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, sca
             raise ValueError("kv_scales must be [num_blocks, Hkv, block_size, 4]")
     if ctx_lens.numel() != shape.num_seqs or q_lens.numel() != shape.num_seqs:
         raise ValueError("ctx_lens and q_lens need one entry per block-table row")
+    if tree_mask is not None:
+        _need(tree_mask, "tree_mask", torch.int64, 1, dev)
+        if tree_mask.numel() != shape.total_q:
+            raise ValueError("tree_mask needs one entry per query row")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, 3, dev)
@@ -173,7 +180,12 @@ def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, sca
         workspace = attn_workspace(shape, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
     with torch.cuda.device(dev):
-        if kv8:
+        if tree_mask is not None:
+            rc = lib.paged_attn_step_tree(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr() if kv8 else None,
+                                          block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
+                                          tree_mask.data_ptr(), out.data_ptr(), ctypes.byref(shape),
+                                          workspace.data_ptr(), workspace.numel(), _stream(stream))
+        elif kv8:
             rc = lib.paged_attn_step_u8(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr(),
                                         block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
                                         out.data_ptr(), ctypes.byref(shape), workspace.data_ptr(),

@@ -198,8 +198,8 @@ namespace {
 
 // Shared body of the bf16 and 8-bit entry points: kv_scales == nullptr selects the bf16 pool.
 int attn_step(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,
-              const int32_t* ctx_lens, const int32_t* q_lens, float* out, const vap_attn_shape* shape,
-              void* workspace, size_t workspace_bytes, void* stream_, bool kv8) {
+              const int32_t* ctx_lens, const int32_t* q_lens, const uint64_t* tree_mask, float* out,
+              const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream_, bool kv8) {
   AttnPlanChoice c;
   int rc = check_attn_shape(shape, &c);
   if (rc != VAP_OK) return rc;
@@ -242,6 +242,7 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
   P.kcodes = kv8 ? static_cast<const uint8_t*>(kv) : nullptr;
   P.vcodes = kv8 ? P.kcodes + plane : nullptr;
   P.kv_scales = kv8 ? kv_scales : nullptr;
+  P.tree_mask = tree_mask;
   P.tables = block_tables;
   P.ctx_lens = ctx_lens;
   P.q_lens = q_lens;
@@ -292,7 +293,7 @@ int paged_attn_step(const void* q, const void* kv_pool, const int32_t* block_tab
                     const int32_t* ctx_lens, const int32_t* q_lens, float* out,
                     const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return attn_step(q, kv_pool, nullptr, block_tables, ctx_lens, q_lens, out, shape, workspace,
+  return attn_step(q, kv_pool, nullptr, block_tables, ctx_lens, q_lens, nullptr, out, shape, workspace,
                    workspace_bytes, stream, false);
 }
 
@@ -300,8 +301,17 @@ int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scal
                        const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
                        float* out, const vap_attn_shape* shape, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return attn_step(q, kv_codes, kv_scales, block_tables, ctx_lens, q_lens, out, shape, workspace,
+  return attn_step(q, kv_codes, kv_scales, block_tables, ctx_lens, q_lens, nullptr, out, shape, workspace,
                    workspace_bytes, stream, true);
+}
+
+int paged_attn_step_tree(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,
+                         const int32_t* ctx_lens, const int32_t* q_lens, const uint64_t* tree_mask, float* out,
+                         const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  if (shape != nullptr && shape->num_seqs > 0 && tree_mask == nullptr) return fail(VAP_EINVAL, "NULL tree_mask");
+  if (reinterpret_cast<uintptr_t>(tree_mask) & 7) return fail(VAP_EINVAL, "tree_mask must be 8-byte aligned");
+  return attn_step(q, kv, kv_scales, block_tables, ctx_lens, q_lens, tree_mask, out, shape, workspace,
+                   workspace_bytes, stream, kv_scales != nullptr);
 }
 
 size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {

@@ -257,6 +257,19 @@ __device__ __forceinline__ void load_tile8(KVTile<D, true>& t, const uint8_t* kb
     t.sc[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_s, 16 * r, 0));
 }
 
+// Which keys a lane's rows may see: key positions up to lim (L - Q + the row's node index), and
+// of the new rows (positions >= base = L - Q) only those set in the row's tree mask (all ones
+// for causal rows).
+template <int NRT>
+struct RowVis {
+  int lim[NRT];
+  uint64_t tmask[NRT];
+  int base;
+  __device__ __forceinline__ bool sees(int rt, int tok) const {
+    return tok <= lim[rt] && (tok < base || ((tmask[rt] >> ((tok - base) & 63)) & 1ull));
+  }
+};
+
 // Max over the four lanes {c, c+16, c+32, c+48} holding one row: two lane swaps (odd/even
 // 16-lane rows, then the two 32-lane halves), no LDS round trip.
 __device__ __forceinline__ float row_max4(float x) {
@@ -279,7 +292,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int NRT, bool MASKED>
-__device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, int t_end, const int (&lim)[NRT],
+__device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, int t_end, const RowVis<NRT>& vis,
                                              const bf16x8 (&qb)[NRT][D / 32], float scale_log2,
                                              float (&m_run)[NRT], float (&l_run)[NRT],
                                              f32x4 (&acc)[NRT][D / 16], int g) {
@@ -299,7 +312,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, 
     for (int r = 0; r < 4; ++r) {
       if (MASKED) {
         const int tok = tg + 4 * g + r;
-        ok[rt][r] = (tok < t_end) && (tok <= lim[rt]);
+        ok[rt][r] = (tok < t_end) && vis.sees(rt, tok);
         m = ok[rt][r] ? fmaxf(m, sc[rt][r]) : m;
       } else {
         m = fmaxf(m, sc[rt][r]);
@@ -372,7 +385,7 @@ __device__ __forceinline__ float code_f32(uint32_t w, int i) { return (float)((w
 // sum_j p_j s_v,j c_j - sum_j p_j s_v,j z_v,j, so P is scaled by s_v per token and the second
 // sum is kept per row (o_run, subtracted at the end).
 template <int D, int NRT, bool MASKED>
-__device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, int t_end, const int (&lim)[NRT],
+__device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, int t_end, const RowVis<NRT>& vis,
                                               const bf16x8 (&qb)[NRT][D / 32], const float (&qsum)[NRT],
                                               float scale_log2, float (&m_run)[NRT], float (&l_run)[NRT],
                                               float (&o_run)[NRT], f32x4 (&acc)[NRT][D / 16], int g) {
@@ -401,7 +414,7 @@ __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, 
       sv[rt][r] = t.sc[r].x * fmaf(-t.sc[r].y, qsum[rt], raw[r]);
       if (MASKED) {
         const int tok = tg + 4 * g + r;
-        ok[rt][r] = (tok < t_end) && (tok <= lim[rt]);
+        ok[rt][r] = (tok < t_end) && vis.sees(rt, tok);
         m = ok[rt][r] ? fmaxf(m, sv[rt][r]) : m;
       } else {
         m = fmaxf(m, sv[rt][r]);
@@ -528,7 +541,8 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   const int row0 = sg.rg * RG;
   const int t_start = sg.ub * BS;
   const int t_end = min(sg.L, (sg.ub + sg.seg) * BS);
-  const int full_until = sg.L - sg.Q;   // tokens <= this are visible to every row
+  // tokens <= full_until are visible to every row (tree rows: the committed prefix only)
+  const int full_until = P.tree_mask ? sg.L - sg.Q - 1 : sg.L - sg.Q;
   const int32_t* trow = P.tables + (long long)sg.s * P.MB;
   const long long tok_stride = (long long)P.Hkv * D;
   const uint16_t* kbase = P.kpool + (long long)sg.kvh * D;
@@ -552,10 +566,25 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   // cache the row sums of q (the zero points' term of the scores)
   bf16x8 qb[NRT][NKK];
   float qsum[NRT];
-  int lim[NRT];
+  RowVis<NRT> vis;
+  vis.base = sg.L - sg.Q;
+  int derr = 0;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    lim[rt] = sg.L - sg.Q + (row0 + rt * 16 + c) / G;
+    const int node = (row0 + rt * 16 + c) / G;
+    vis.lim[rt] = sg.L - sg.Q + node;
+    vis.tmask[rt] = ~0ull;
+    if (P.tree_mask != nullptr && out_row[rt] >= 0) {
+      // a tree row sees itself and nodes before it only (topological order, at most 64 nodes)
+      const uint64_t m = P.tree_mask[sg.qoff + node];
+      const uint64_t allowed = (node >= 63) ? ~0ull : ((2ull << node) - 1);
+      if (sg.Q > 64) {
+        derr |= VAP_DERR_TREE;                 // cannot be a tree: keep the row causal
+      } else {
+        if (!((m >> node) & 1ull) || (m & ~allowed)) derr |= VAP_DERR_TREE;
+        vis.tmask[rt] = (m & allowed) | (1ull << node);
+      }
+    }
     const uint16_t* qp = P.q + (long long)(out_row[rt] >= 0 ? out_row[rt] : 0) * D + (KV8 ? (D / 4) * g : 8 * g);
     float qs = 0.f;
 #pragma unroll
@@ -585,7 +614,6 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   // The tile loop walks the segment in windows of 64 KV blocks.  A window's pool block ids are
   // loaded once (one per lane) before its tiles, so no vector load inside the tile loop depends
   // on a branch.
-  int derr = 0;
   constexpr int kWinBlocks = 64;
   constexpr int kWinTiles = kWinBlocks * BS / kTile;
   const int ntiles = (t_end - t_start + kTile - 1) / kTile;
@@ -600,7 +628,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
       const int j = wbase + lane;
       win = (j < jend) ? trow[j] : 0;
       if (j < jend && (unsigned)win >= (unsigned)P.num_blocks) {
-        derr = VAP_DERR_BLOCK_ID;
+        derr |= VAP_DERR_BLOCK_ID;
         win = 0;
       }
     }
@@ -617,10 +645,10 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     };
     auto compute = [&](const KVTile<D, KV8>& X, int i, auto masked) {
       if constexpr (KV8)
-        compute_tile8<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, qsum, P.scale_log2,
+        compute_tile8<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, qsum, P.scale_log2,
                                                        m_run, l_run, o_run, acc, g);
       else
-        compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, lim, qb, P.scale_log2, m_run,
+        compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, P.scale_log2, m_run,
                                                       l_run, acc, g);
     };
     // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
@@ -651,7 +679,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
       compute(t0, i, std::true_type{});
     }
   }
-  if (derr && lane == 0) atomicOr(&P.hdr->err, derr);
+  if (derr) atomicOr(&P.hdr->err, derr);      // any lane: errors are per table entry / row
 
   float lsum[NRT];
 #pragma unroll

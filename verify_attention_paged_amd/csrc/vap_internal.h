@@ -72,6 +72,7 @@ struct AttnParams {
   const uint8_t* kcodes;    // 8-bit cache: uint8 [NB][BS][Hkv][D] codes of K and of V
   const uint8_t* vcodes;
   const float* kv_scales;   // 8-bit cache: fp32 [NB][Hkv][BS][4] (k_scale, k_zero, v_scale, v_zero)
+  const uint64_t* tree_mask;   // [T] ancestor masks of tree rows, or nullptr (causal rows)
   const int32_t* tables;    // [B][MB]
   const int32_t* ctx_lens;  // [B]
   const int32_t* q_lens;    // [B]
