@@ -14,6 +14,8 @@ import tests.test_oracle_attention as TA
 import tests.test_oracle_kv8 as TK
 import tests.test_oracle_spec_verify as TS
 import tests.test_oracle_tree as TT
+import tests.test_oracle_tree_verify as TV
+from oracle import tree_verify as TVO
 
 GOLDEN = TA.os.path.join(TA.os.path.dirname(TA.os.path.abspath(TA.__file__)), "golden")
 
@@ -153,6 +155,63 @@ TREE_MUTANTS = {
 }
 
 
+TREE_VERIFY_PINS = [
+    lambda: TV.test_golden_worked_cases(GOLDEN),
+    lambda: [TV.test_chain_tree_is_the_chain_verifier(s) for s in range(6)],
+    lambda: TV.test_root_only_is_numpy_inverse_cdf(0),
+    TV.test_lossless_monte_carlo_on_a_two_level_tree,
+]
+
+
+def _tree_verify_variant(update="normalised", q_of="parent", order=1, final="current", final_u=0):
+    def tree_verify_sequence(p_rows, q_rows, parents, tokens, uniforms):
+        p_rows = np.asarray(p_rows, dtype=np.float64)
+        q_rows = np.asarray(q_rows, dtype=np.float64)
+        N, V = p_rows.shape
+        kids = TVO.tree_children(parents)
+        ids, path = [], []
+        u, p_cur = 0, p_rows[0]
+        while True:
+            accepted = None
+            for c in kids[u][::order]:
+                x = int(tokens[c])
+                inside = 0 <= x < V
+                qrow = q_rows[u] if q_of == "parent" else q_rows[c]
+                P = p_cur[x] if inside else 0.0
+                Qx = qrow[x] if inside else 0.0
+                if S.accept_draft(P, Qx, uniforms[c]):
+                    accepted = c
+                    break
+                if update == "normalised":
+                    p_cur = TVO.residual(p_cur, qrow)
+                elif update == "raw":
+                    p_cur = np.maximum(0.0, p_cur - qrow)
+            if accepted is None:
+                row = p_cur if final == "current" else p_rows[u]
+                y = S.sample_inverse_cdf(row, uniforms[final_u])
+                ids.append(max(y, 0))
+                break
+            path.append(accepted)
+            ids.append(int(tokens[accepted]))
+            u, p_cur = accepted, p_rows[accepted]
+        out = np.full(N, -1, dtype=np.int64)
+        out[:len(ids)] = ids
+        nodes = np.full(N, -1, dtype=np.int64)
+        nodes[:len(path)] = path
+        return out, nodes, len(path)
+    return tree_verify_sequence
+
+
+TREE_VERIFY_MUTANTS = {
+    "no residual after a rejection": _tree_verify_variant(update="none"),
+    "residual not normalised": _tree_verify_variant(update="raw"),
+    "residual against the child's q row": _tree_verify_variant(q_of="child"),
+    "children tested in reverse order": _tree_verify_variant(order=-1),
+    "final draw ignores the residual": _tree_verify_variant(final="fresh"),
+    "final draw uses the last node's uniform": _tree_verify_variant(final_u=-1),
+}
+
+
 def _any_pin_fails(pins):
     for pin in pins:
         try:
@@ -174,6 +233,12 @@ def test_attention_mutant_is_caught(name, monkeypatch):
 def test_tree_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(A, "attention_sequence", _seq_variant(tree_fn=TREE_MUTANTS[name]))
     assert _any_pin_fails(TREE_PINS), f"no tree pin caught: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(TREE_VERIFY_MUTANTS))
+def test_tree_verify_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(TVO, "tree_verify_sequence", TREE_VERIFY_MUTANTS[name])
+    assert _any_pin_fails(TREE_VERIFY_PINS), f"no tree-verification pin caught: {name}"
 
 
 @pytest.mark.parametrize("name", sorted(KV8_MUTANTS))
@@ -273,3 +338,5 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     assert not _any_pin_fails(SPEC_PINS)
     assert not _any_pin_fails(KV8_PINS)
     assert not _any_pin_fails(TREE_PINS)
+    monkeypatch.setattr(TVO, "tree_verify_sequence", _tree_verify_variant())
+    assert not _any_pin_fails(TREE_VERIFY_PINS)

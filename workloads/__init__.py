@@ -25,4 +25,7 @@ from .generate import (  # noqa: F401
     open_uniforms,
     random_tree_parents,
     tree_masks,
+    TreeVerifyInputs,
+    make_tree_verify_from_probs,
+    tree_verify_config,
 )

@@ -433,3 +433,84 @@ def verify_config(name: str, seed: int | None = None, batch: int | None = None) 
     else:
         raise KeyError(name)
     return make_verify_inputs(seed, p_logits=pl, q_logits=ql, rng=rng, name=name)
+
+
+# ----------------------------------------------------------------------------------------
+# tree verification inputs
+# ----------------------------------------------------------------------------------------
+
+@dataclass
+class TreeVerifyInputs:
+    """One batch for verifying draft token trees (CPU tensors).
+
+    p         fp32  [B, N, V]   target next-token distribution after each node
+    q         fp32  [B, N, V]   draft distribution each node's children were drawn from
+    parents   int32 [B, N]      parent of each node (-1 for the root, node 0); parents first
+    tokens    int32 [B, N]      draft token of each node (entry 0, the root, unused: -1)
+    uniforms  fp32  [B, N]      u[:, i] the accept test of node i > 0, u[:, 0] the final draw
+    """
+
+    name: str
+    seed: int
+    p: torch.Tensor
+    q: torch.Tensor
+    parents: torch.Tensor
+    tokens: torch.Tensor
+    uniforms: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.p.shape[0])
+
+    @property
+    def num_nodes(self) -> int:
+        return int(self.p.shape[1])
+
+    @property
+    def vocab(self) -> int:
+        return int(self.p.shape[2])
+
+
+def make_tree_verify_from_probs(seed: int, p32: np.ndarray, q32: np.ndarray, parents: np.ndarray,
+                                rng: np.random.Generator | None = None, name: str = "custom") -> TreeVerifyInputs:
+    """Children's tokens drawn independently from their parent's draft row, then uniforms."""
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    B, N, V = p32.shape
+    parents = np.asarray(parents, dtype=np.int64).reshape(B, N)
+    tokens = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            w = q32[b, int(parents[b, i])].astype(np.float64)
+            tokens[b, i] = rng.choice(V, p=w / w.sum())
+    u = open_uniforms(rng, (B, N))
+    return TreeVerifyInputs(name=name, seed=seed, p=torch.from_numpy(np.ascontiguousarray(p32)),
+                            q=torch.from_numpy(np.ascontiguousarray(q32)),
+                            parents=torch.from_numpy(parents.astype(np.int32)),
+                            tokens=torch.from_numpy(tokens), uniforms=torch.from_numpy(u))
+
+
+def tree_verify_config(name: str, seed: int | None = None, batch: int | None = None) -> TreeVerifyInputs:
+    """Named tree-verification workloads (trees are random recursive trees, node 0 the root).
+
+    tiny_tree         B 4, N 9, V 1000; target and draft logits independent N(0, 2)
+    tree_verify_step  B 16, N 16, V 128256; target logits N(0, 3) per node; draft logits =
+                      target logits + N(0, 0.7)
+    """
+    if seed is None:
+        seed = DEFAULT_SEEDS.get(name, 2001)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if name == "tiny_tree":
+        B, N, V = batch or 4, 9, 1000
+        pl = 2.0 * rng.standard_normal((B, N, V))
+        ql = 2.0 * rng.standard_normal((B, N, V))
+    elif name == "tree_verify_step":
+        B, N, V = batch or 16, 16, 128256
+        pl = 3.0 * rng.standard_normal((B, N, V))
+        ql = pl + 0.7 * rng.standard_normal((B, N, V))
+    else:
+        raise KeyError(name)
+    parents = np.stack([random_tree_parents(rng, N) for _ in range(B)])
+    p32 = _softmax_rows_f64(pl).astype(np.float32)
+    q32 = _softmax_rows_f64(ql).astype(np.float32)
+    return make_tree_verify_from_probs(seed, p32, q32, parents, rng=rng, name=name)
