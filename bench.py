@@ -87,6 +87,29 @@ def code_only(text: str) -> str:
     return "\n".join(ln for ln in lines if ln)
 
 
+def tree_verify_bytes(parents, path, n_accepted, V) -> int:
+    """Rows the tree walk must read: at every visited node where a child was rejected, its
+    target and draft rows (8V); at the final node without a rejection, its target row (4V);
+    plus the two gathered values per accept test, the tree, the uniforms and the outputs."""
+    total = 0
+    for par, pth, n in zip(parents, path, n_accepted):
+        par = list(par)
+        N = len(par)
+        visited = [0] + [int(x) for x in pth[:int(n)]]
+        tests = 0
+        for i, u in enumerate(visited):
+            kids = [c for c in range(1, N) if par[c] == u]
+            if i < len(visited) - 1:
+                rejected = sum(1 for c in kids if c < visited[i + 1])
+                tests += rejected + 1
+            else:
+                rejected = len(kids)
+                tests += rejected
+            total += 8 * V if rejected else (4 * V if i == len(visited) - 1 else 0)
+        total += 8 * tests + 12 * N + 8 * N + 4
+    return total
+
+
 def kernel_source_hash() -> str:
     """Fingerprint of the attention kernel's code (comments ignored); the committed counter
     summary is valid only for the fingerprint it records."""
@@ -284,6 +307,41 @@ def run_default(args, dev):
         f"-> {sv_bytes / (sv_kernel_ms * 1e-3) / 1e9:.1f} GB/s; verify attention kernel "
         f"{vattn_ms / max(1, c0) * 1e3:.1f} us -> {vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9:.1f} GB/s")
 
+    # ---- tree verify step: tree-masked attention (16 x 16-node trees) + spec_verify_tree
+    tinp, td, tpools, tout, tws, tnbytes = setup_attention("tree_verify_step", dev)
+    tver = workloads.tree_verify_config("tree_verify_step")
+    tmask = torch.from_numpy(np.concatenate([workloads.tree_masks(pr) for pr in tver.parents.numpy()])).to(dev)
+    tps = rotating_copies(tver.p.to(dev), 768 << 20)
+    tqs = [tver.q.to(dev) for _ in range(len(tps))]
+    tpar, ttok, tuni = tver.parents.to(dev), tver.tokens.to(dev), tver.uniforms.to(dev)
+    t_ids = torch.empty((tver.num_seqs, tver.num_nodes), dtype=torch.int32, device=dev)
+    t_path = torch.empty_like(t_ids)
+    t_n = torch.empty((tver.num_seqs,), dtype=torch.int32, device=dev)
+    tvws = vap.tree_verify_workspace(dev)
+
+    def tstep(i):
+        vap.paged_attn_step(td["q"], tpools[i % len(tpools)], td["block_tables"], td["ctx_lens"], td["q_lens"],
+                            out=tout, workspace=tws, tree_mask=tmask)
+        vap.spec_verify_tree(tps[i % len(tps)], tqs[i % len(tqs)], tpar, ttok, tuni, t_ids, t_path, t_n,
+                             workspace=tvws)
+
+    vap.timer_enable(True)
+    time_loop(tstep, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
+    tms, _ = time_loop(tstep, args.steps, 0)
+    tattn_ms, tc0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    tsv_ms, tc1 = vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
+    vap.timer_enable(False)
+    tn_host = t_n.cpu().numpy()
+    t_emitted = int((tn_host + 1).sum())
+    tsv_bytes = tree_verify_bytes(tver.parents.numpy(), t_path.cpu().numpy(), tn_host, tver.vocab)
+    tsv_kernel_ms = tsv_ms / max(1, tc1)
+    tree_tok_s = t_emitted / (tms * 1e-3)
+    log(f"tree verify step {tms * 1e3:.1f} us ({t_emitted} tokens emitted, {tn_host.mean():.2f} accepted per "
+        f"sequence); tree attention kernel {tattn_ms / max(1, tc0) * 1e3:.1f} us; spec_verify_tree kernel "
+        f"{tsv_kernel_ms * 1e3:.1f} us -> {tsv_bytes / (tsv_kernel_ms * 1e-3) / 1e9:.1f} GB/s")
+
     # ---- decode step over an 8-bit KV cache (same lengths and shapes)
     qinp, qd, qpools, qout, qws, qnbytes = setup_attention("llama3_8b_decode", dev, kv_format="u8")
     qstep = lambda i: vap.paged_attn_step(qd["q"], qpools[i % len(qpools)], qd["block_tables"], qd["ctx_lens"],
@@ -335,6 +393,15 @@ def run_default(args, dev):
                         "spec_verify_kernel_ms": round(sv_kernel_ms, 5),
                         "spec_verify_GB_per_s": round(sv_bytes / (sv_kernel_ms * 1e-3) / 1e9, 2),
                         "spec_verify_bytes": sv_bytes},
+        "tree_verify_step": {"workload": "tree_verify_step: 16 seqs verifying 16-node random token trees "
+                                         "(tree-masked attention, 32/8 heads, head_dim 128, ctx uniform "
+                                         "[512, 4096]) then spec_verify_tree over vocab 128256",
+                             "ms_per_step": round(tms, 5), "tokens_emitted": t_emitted,
+                             "mean_accepted": round(float(tn_host.mean()), 3),
+                             "verified_tokens_per_s": round(tree_tok_s, 1),
+                             "attention_kernel_ms": round(tattn_ms / max(1, tc0), 5),
+                             "spec_verify_tree_kernel_ms": round(tsv_kernel_ms, 5),
+                             "spec_verify_tree_bytes": tsv_bytes},
         "kv8_decode_step": {"workload": "llama3_8b_decode with uint8 K/V codes and per-token (scale, zero) "
                                         "pairs, dequantised in the kernel",
                             "ms_per_step": round(qms, 5), "bytes_per_step": qnbytes,

@@ -203,8 +203,43 @@ const char* vap_last_error_message(void);
 
 /* ---- measurement helpers (not part of the step) ------------------------------------------ */
 
+/* Workspace bytes spec_verify_tree needs (its sticky error word). */
+size_t vap_tree_verify_workspace_bytes(void);
+
+/*
+ * spec_verify_tree -- verify a draft token tree per sequence (modified rejection sampling,
+ * neuralmasteryai.com "Continuous Batching & Speculative Decoding", sections "The Modified
+ * Rejection Sampling Algorithm" and "4. Tree Attention & Medusa Heads").
+ *
+ *   p          fp32 [B][N][V]  target next-token distribution after each node
+ *   q          fp32 [B][N][V]  draft distribution each node's children were drawn from
+ *   parents    int32 [B][N]    parent of each node: -1 for node 0 (the last committed token),
+ *                              0 <= parent[i] < i otherwise
+ *   tokens     int32 [B][N]    draft token of each node (entry 0 unused)
+ *   uniforms   fp32 [B][N]     in (0,1): uniforms[i] decides node i's accept test (i > 0),
+ *                              uniforms[0] the final draw
+ *   out_ids    int32 [B][N]    accepted tokens along the path, then the drawn token, then -1
+ *   out_path   int32 [B][N]    accepted node indices along the path, then -1
+ *   n_accepted int32 [B]       number of accepted draft nodes
+ *   1 <= N <= 64, 1 <= V <= 2^24.
+ *
+ * Per sequence: at the current node, its children are tested in index order; child c with
+ * token x passes when p_cur(x) > 0 and uniforms[c] * q(x) <= p_cur(x) (q = the current node's
+ * draft row, decided in fp64).  After a rejection p_cur becomes max(0, p_cur - q), normalised
+ * (unchanged when it sums to 0).  The first child that passes is accepted and the walk moves to
+ * it with p_cur = its target row.  With no child left, one token is drawn from p_cur (inverse
+ * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
+ * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
+ * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  One workgroup per sequence.
+ */
+int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
+                     const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,
+                     int32_t num_seqs, int32_t num_nodes, int32_t vocab, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Kernel timer.  While enabled, every paged_attn_step records a hipEvent pair around its
- * attention kernel (kind 0) and every spec_verify around its kernel (kind 1), on the caller's
+ * attention kernel (kind 0), every spec_verify around its kernel (kind 1) and every
+ * spec_verify_tree around its kernel (kind 2), on the caller's
  * stream, into a ring of 4096 pairs per kind.  vap_timer_read synchronises on the recorded
  * events, returns the summed milliseconds and the number of pairs, and resets the ring when
  * `reset` is nonzero. */

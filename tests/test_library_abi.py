@@ -20,7 +20,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = vap.header_functions()
-    assert {"paged_attn_step", "paged_attn_step_u8", "spec_verify", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
+    assert {"paged_attn_step", "paged_attn_step_u8", "paged_attn_step_tree", "spec_verify", "spec_verify_tree", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
             "vap_get_device_error", "vap_strerror"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -70,6 +70,16 @@ def test_u8_attention_null_pointers_and_empty_batch(lib):
     assert lib.paged_attn_step_u8(fake, fake, None, fake, fake, fake, fake, ctypes.byref(s), fake, 1 << 20, None) == B.VAP_EINVAL
     empty = B.AttnShape(0, 8, 2, 64, 16, 35, 16, 0, 0.0)
     assert lib.paged_attn_step_u8(None, None, None, None, None, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
+
+
+def test_tree_verify_rejected_on_host(lib):
+    ws = lib.vap_tree_verify_workspace_bytes()
+    assert ws >= 4
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 65, 10, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 0, 10, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 0, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 10, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 0, 8, 10, None, 0, None) == B.VAP_OK
 
 
 def test_workspace_sizes_are_consistent(lib):

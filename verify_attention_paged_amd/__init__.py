@@ -6,6 +6,8 @@ memory and streams only.
 
     paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale=0.0)
     spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None)
+    spec_verify_tree(p, q, parents, tokens, uniforms)
+    (paged_attn_step also takes kv_scales= for an 8-bit cache and tree_mask= for token trees)
 """
 
 from ._binding import (  # noqa: F401
@@ -20,6 +22,7 @@ from ._binding import (  # noqa: F401
     DERR_TREE,
     TIMER_ATTENTION,
     TIMER_VERIFY,
+    TIMER_TREE_VERIFY,
     attn_shape,
     attn_workspace,
     device_info,
@@ -28,6 +31,8 @@ from ._binding import (  # noqa: F401
     load_library,
     paged_attn_step,
     spec_verify,
+    spec_verify_tree,
+    tree_verify_workspace,
     stream_copy,
     stream_read,
     timer_enable,

@@ -19,7 +19,7 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
 
 VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
 DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
-TIMER_ATTENTION, TIMER_VERIFY = 0, 1
+TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY = 0, 1, 2
 
 
 class VapError(RuntimeError):
@@ -53,6 +53,8 @@ SIGNATURES = {
     "paged_attn_step_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "vap_tree_verify_workspace_bytes": (_sz, []),
+    "spec_verify_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "vap_get_device_error": (ctypes.c_int, [_vp, _vp, _pi32, ctypes.c_int]),
     "vap_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -248,6 +250,51 @@ def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
                              workspace.numel(), _stream(stream))
     _check(rc)
     return out_ids, n_accepted
+
+
+def tree_verify_workspace(device=None) -> torch.Tensor:
+    n = load_library().vap_tree_verify_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
+
+
+def spec_verify_tree(p, q, parents, tokens, uniforms, out_ids=None, out_path=None, n_accepted=None, *,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """Verification of draft token trees; see ``spec_verify_tree`` in include/vap.h.
+
+    p, q fp32 [B, N, V]; parents, tokens int32 [B, N]; uniforms fp32 [B, N].
+    Returns (out_ids int32 [B, N], out_path int32 [B, N], n_accepted int32 [B]).
+    """
+    lib = load_library()
+    dev = p.device
+    _need(p, "p", torch.float32, 3)
+    B, N, V = p.shape
+    _need(q, "q", torch.float32, 3, dev)
+    if tuple(q.shape) != (B, N, V):
+        raise ValueError("q must have the shape of p")
+    for t, name, dt in ((parents, "parents", torch.int32), (tokens, "tokens", torch.int32),
+                        (uniforms, "uniforms", torch.float32)):
+        _need(t, name, dt, 2, dev)
+        if tuple(t.shape) != (B, N):
+            raise ValueError(f"{name} must be [B, N]")
+    if out_ids is None:
+        out_ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_path is None:
+        out_path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    for t, name in ((out_ids, "out_ids"), (out_path, "out_path")):
+        _need(t, name, torch.int32, 2, dev)
+    _need(n_accepted, "n_accepted", torch.int32, 1, dev)
+    if workspace is None:
+        workspace = tree_verify_workspace(dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_tree(p.data_ptr(), q.data_ptr(), parents.data_ptr(), tokens.data_ptr(),
+                                  uniforms.data_ptr(), out_ids.data_ptr(), out_path.data_ptr(),
+                                  n_accepted.data_ptr(), B, N, V, workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream))
+    _check(rc)
+    return out_ids, out_path, n_accepted
 
 
 # ---------------------------------------------------------------------------------------

@@ -81,9 +81,9 @@ constexpr int kTimerSlots = 4096;
 struct Timer {
   bool on = false;
   bool created = false;
-  hipEvent_t start[2][kTimerSlots];
-  hipEvent_t stop[2][kTimerSlots];
-  int count[2] = {0, 0};
+  hipEvent_t start[3][kTimerSlots];
+  hipEvent_t stop[3][kTimerSlots];
+  int count[3] = {0, 0, 0};
 };
 Timer g_timer;
 
@@ -374,6 +374,47 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
   return ok();
 }
 
+size_t vap_tree_verify_workspace_bytes(void) { return 256; }
+
+int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
+                     const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,
+                     int32_t num_seqs, int32_t num_nodes, int32_t vocab, void* workspace,
+                     size_t workspace_bytes, void* stream_) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs)
+    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
+  if (num_nodes < 1 || num_nodes > kMaxTreeNodes)
+    return fail(VAP_EINVAL, "num_nodes=%d outside [1, %d]", num_nodes, kMaxTreeNodes);
+  if (vocab < 1 || vocab > (1 << 24)) return fail(VAP_EINVAL, "vocab=%d outside [1, 2^24]", vocab);
+  if (num_seqs == 0) return ok();
+  if (!p || !q || !parents || !tokens || !uniforms || !out_ids || !out_path || !n_accepted || !workspace)
+    return fail(VAP_EINVAL, "NULL data pointer");
+  if (workspace_bytes < vap_tree_verify_workspace_bytes())
+    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes, vap_tree_verify_workspace_bytes());
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
+  const DevInfo* d = device_info();
+  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+  TreeVerifyParams P;
+  P.p = p;
+  P.q = q;
+  P.parents = parents;
+  P.tokens = tokens;
+  P.uniforms = uniforms;
+  P.out_ids = out_ids;
+  P.out_path = out_path;
+  P.n_accepted = n_accepted;
+  P.B = num_seqs;
+  P.N = num_nodes;
+  P.V = vocab;
+  P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
+  P.err = static_cast<int32_t*>(workspace);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  timer_begin(2, stream);
+  const hipError_t e = launch_tree_verify(P, stream);
+  timer_end(2, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "tree verify launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int vap_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return fail(VAP_EINVAL, "NULL workspace");
   if (bytes == 0) return ok();
@@ -398,7 +439,7 @@ int vap_get_device_error(void* workspace, void* stream_, int32_t* err_out, int c
 int vap_timer_enable(int on) {
   std::lock_guard<std::mutex> lock(g_mu);
   if (on && !g_timer.created) {
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 3; ++k)
       for (int i = 0; i < kTimerSlots; ++i) {
         if (hipEventCreate(&g_timer.start[k][i]) != hipSuccess || hipEventCreate(&g_timer.stop[k][i]) != hipSuccess)
           return fail(VAP_EHIP, "hipEventCreate failed");
@@ -410,7 +451,7 @@ int vap_timer_enable(int on) {
 }
 
 int vap_timer_read(int kind, double* total_ms, int32_t* count, int reset) {
-  if (kind < 0 || kind > 1 || !total_ms || !count) return fail(VAP_EINVAL, "bad timer arguments");
+  if (kind < 0 || kind > 2 || !total_ms || !count) return fail(VAP_EINVAL, "bad timer arguments");
   double sum = 0.0;
   const int n = g_timer.count[kind];
   for (int i = 0; i < n; ++i) {

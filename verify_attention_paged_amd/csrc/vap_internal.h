@@ -137,4 +137,25 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
+// ---------------------------------------------------------------------------------------
+// Tree verification: one workgroup per sequence, no workspace beyond the error word.
+// ---------------------------------------------------------------------------------------
+constexpr int kMaxTreeNodes = 64;
+
+struct TreeVerifyParams {
+  const float* p;           // [B][N][V] target rows per node
+  const float* q;           // [B][N][V] draft rows per node (the children's proposal)
+  const int32_t* parents;   // [B][N]
+  const int32_t* tokens;    // [B][N]
+  const float* uniforms;    // [B][N]
+  int32_t* out_ids;         // [B][N]
+  int32_t* out_path;        // [B][N]
+  int32_t* n_accepted;      // [B]
+  int32_t B, N, V;
+  bool vec4;                // V % 4 == 0 and p, q 16-byte aligned
+  int32_t* err;
+};
+
+hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream);
+
 }  // namespace vap
