@@ -20,9 +20,11 @@ Modules:
   attention    -- paged KV address translation and causal softmax attention (fp64)
   spec_verify  -- sequential modified rejection sampling with residual resampling (fp64)
   tree_verify  -- the same rule walked over a draft token tree (fp64)
+  kv_cache     -- writing new K/V rows into the paged pool (bf16 copy, 8-bit per-token
+                  quantisation in fp32) and committing accepted draft tokens
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants the
 pages fix, library routines and hand-worked fixtures under ``tests/golden/``.
 """
 
-from . import attention, spec_verify, tree_verify  # noqa: F401
+from . import attention, kv_cache, spec_verify, tree_verify  # noqa: F401

@@ -12,6 +12,8 @@ from oracle import attention as A
 from oracle import spec_verify as S
 import tests.test_oracle_attention as TA
 import tests.test_oracle_kv8 as TK
+import tests.test_oracle_kv_cache as TC
+from oracle import kv_cache as KC
 import tests.test_oracle_spec_verify as TS
 import tests.test_oracle_tree as TT
 import tests.test_oracle_tree_verify as TV
@@ -212,6 +214,80 @@ TREE_VERIFY_MUTANTS = {
 }
 
 
+KV_CACHE_PINS = [
+    lambda: TC.test_quantiser_equals_torch_per_channel_minmax(0),
+    TC.test_append_writes_exactly_the_new_positions,
+    TC.test_append_u8_quantises_each_row_and_touches_nothing_else,
+    TC.test_chain_commit_only_shortens,
+    lambda: TC.test_tree_commit_then_decode_equals_tree_attention_of_the_last_node("bf16"),
+    lambda: TC.test_tree_commit_then_decode_equals_tree_attention_of_the_last_node("u8"),
+]
+
+
+def _quantize_variant(clamp_lo=True, eps=True, levels=255, zero_round=np.rint, divide=False):
+    def quantize_rows_u8(x):
+        x = np.asarray(x, dtype=np.float32)
+        lo = x.min(axis=-1)
+        if clamp_lo:
+            lo = np.minimum(lo, np.float32(0))
+        hi = np.maximum(x.max(axis=-1), np.float32(0))
+        scale = ((hi - lo) / np.float32(levels)).astype(np.float32)
+        if eps:
+            scale = np.maximum(scale, KC.FP32_EPS).astype(np.float32)
+        zero = np.clip(zero_round(-lo / scale), 0, 255).astype(np.float32)
+        if divide:
+            y = x / scale[..., None]
+        else:
+            y = x * (np.float32(1) / scale).astype(np.float32)[..., None]
+        codes = np.clip(np.rint(y) + zero[..., None], 0, 255).astype(np.uint8)
+        return codes, scale, zero
+    return quantize_rows_u8
+
+
+def _new_slots_variant(offset=True):
+    def _new_slots(table_row, L, Q, bs):
+        start = L - Q if offset else 0
+        return A.physical_slots(table_row, L, bs)[start:start + Q]
+    return _new_slots
+
+
+def _commit_variant(src_shift=0, dst_start=1, move_scales=True, keep_root=1, gather_first=True):
+    def kv_commit_tree(pool, block_tables, ctx_lens, q_lens, path, n_accepted, kv_scales=None):
+        pool = np.array(pool, copy=True)
+        scales = None if kv_scales is None else np.array(kv_scales, copy=True)
+        NB, bs = pool.shape[1], pool.shape[2]
+        flat = pool.reshape(2, NB * bs, *pool.shape[3:])
+        for s in range(len(ctx_lens)):
+            L, Q, n = int(ctx_lens[s]), int(q_lens[s]), int(n_accepted[s])
+            slots = A.physical_slots(block_tables[s], L, bs)
+            src = slots[L - Q + src_shift + np.asarray(path[s][:n], dtype=np.int64)]
+            dst = slots[L - Q + dst_start + np.arange(n)]
+            if gather_first:
+                flat[:, dst] = flat[:, src].copy()
+            else:
+                for a, b in zip(src, dst):
+                    flat[:, b] = flat[:, a]
+            if scales is not None and move_scales:
+                scales[dst // bs, :, dst % bs] = scales[src // bs, :, src % bs].copy()
+        L2 = (np.asarray(ctx_lens) - np.asarray(q_lens) + keep_root + np.asarray(n_accepted)).astype(np.int64)
+        return pool, scales, L2
+    return kv_commit_tree
+
+
+KV_CACHE_MUTANTS = {
+    "quantiser: lower end not clamped to 0": ("quantize_rows_u8", _quantize_variant(clamp_lo=False)),
+    "quantiser: 256 levels": ("quantize_rows_u8", _quantize_variant(levels=256)),
+    "quantiser: zero point floored": ("quantize_rows_u8", _quantize_variant(zero_round=np.floor)),
+    "quantiser: no eps floor on the scale": ("quantize_rows_u8", _quantize_variant(eps=False)),
+    "quantiser: divides instead of multiplying by 1/scale": ("quantize_rows_u8", _quantize_variant(divide=True)),
+    "append: written from position 0": ("_new_slots", _new_slots_variant(offset=False)),
+    "commit: source node off by one": ("kv_commit_tree", _commit_variant(src_shift=-1)),
+    "commit: overwrites the root": ("kv_commit_tree", _commit_variant(dst_start=0)),
+    "commit: scales left behind": ("kv_commit_tree", _commit_variant(move_scales=False)),
+    "commit: root not kept in the length": ("kv_commit_tree", _commit_variant(keep_root=0)),
+}
+
+
 def _any_pin_fails(pins):
     for pin in pins:
         try:
@@ -321,6 +397,13 @@ SPEC_MUTANTS = {
 }
 
 
+@pytest.mark.parametrize("name", sorted(KV_CACHE_MUTANTS))
+def test_kv_cache_mutant_is_caught(name, monkeypatch):
+    attr, fn = KV_CACHE_MUTANTS[name]
+    monkeypatch.setattr(KC, attr, fn)
+    assert _any_pin_fails(KV_CACHE_PINS), f"no KV-cache pin caught: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(SPEC_MUTANTS))
 def test_spec_verify_mutant_is_caught(name, monkeypatch):
     attr, fn = SPEC_MUTANTS[name]
@@ -340,3 +423,7 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     assert not _any_pin_fails(TREE_PINS)
     monkeypatch.setattr(TVO, "tree_verify_sequence", _tree_verify_variant())
     assert not _any_pin_fails(TREE_VERIFY_PINS)
+    monkeypatch.setattr(KC, "quantize_rows_u8", _quantize_variant())
+    monkeypatch.setattr(KC, "_new_slots", _new_slots_variant())
+    monkeypatch.setattr(KC, "kv_commit_tree", _commit_variant())
+    assert not _any_pin_fails(KV_CACHE_PINS)
