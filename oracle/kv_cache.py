@@ -11,8 +11,9 @@ What is computed:
   K and of V is quantised on its own (per-token scales, separate for K and V, asymmetric).
   Reading taken: the usual affine uint8 min/max rule, in float32 --
       lo = min(0, min x), hi = max(0, max x), scale = max((hi - lo) / 255, eps_fp32),
-      zero = clip(round(-lo / scale), 0, 255), code = clip(round(x * (1/scale)) + zero, 0, 255)
-  with round-half-even; value = scale * (code - zero).  (0 is exactly representable.)
+      zero = clip(round((0 - lo) / scale), 0, 255), code = clip(round(x * (1/scale)) + zero, 0, 255)
+  with round-half-even; value = scale * (code - zero).  (0 is exactly representable.)  The zero
+  point is an integer, stored as float +0 .. 255 (0 - lo, not -lo, so that lo = 0 gives +0).
 * Commit [P3 §"Speculative Decoding: Turning Verification Parallelism into Latency Wins":
   rollback of the KV of rejected tokens; P2 §"Speculative Decoding: Draft Fast, Verify Cheap"]:
   after verifying Q = k + 1 rows (the last committed token and k drafts) with n accepted, the
@@ -39,7 +40,7 @@ def quantize_rows_u8(x: np.ndarray):
     lo = np.minimum(x.min(axis=-1), np.float32(0))
     hi = np.maximum(x.max(axis=-1), np.float32(0))
     scale = np.maximum((hi - lo) / np.float32(255), FP32_EPS).astype(np.float32)
-    zero = np.clip(np.rint(-lo / scale), 0, 255).astype(np.float32)
+    zero = np.clip(np.rint((np.float32(0) - lo) / scale), 0, 255).astype(np.float32)   # +0, never -0
     inv = (np.float32(1) / scale).astype(np.float32)
     codes = np.clip(np.rint(x * inv[..., None]) + zero[..., None], 0, 255).astype(np.uint8)
     return codes, scale, zero

@@ -42,7 +42,7 @@ def test_quantiser_equals_torch_per_channel_minmax(seed):
     codes, sc, z = K.quantize_rows_u8(x)
     tc, tsc, tz = _torch_quantize(x)
     np.testing.assert_array_equal(sc, tsc)
-    np.testing.assert_array_equal(z, tz)
+    np.testing.assert_array_equal(z.view(np.uint32), tz.view(np.uint32))   # integer zero points: +0, never -0
     np.testing.assert_array_equal(codes, tc)
     deq = sc[:, None].astype(np.float64) * (codes.astype(np.float64) - z[:, None])
     assert np.all(np.abs(deq - x) <= 0.5 * sc[:, None].astype(np.float64) * (1 + 1e-5) + 1e-7)

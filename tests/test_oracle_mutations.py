@@ -224,7 +224,7 @@ KV_CACHE_PINS = [
 ]
 
 
-def _quantize_variant(clamp_lo=True, eps=True, levels=255, zero_round=np.rint, divide=False):
+def _quantize_variant(clamp_lo=True, eps=True, levels=255, zero_round=np.rint, divide=False, neg_lo=False):
     def quantize_rows_u8(x):
         x = np.asarray(x, dtype=np.float32)
         lo = x.min(axis=-1)
@@ -234,7 +234,8 @@ def _quantize_variant(clamp_lo=True, eps=True, levels=255, zero_round=np.rint, d
         scale = ((hi - lo) / np.float32(levels)).astype(np.float32)
         if eps:
             scale = np.maximum(scale, KC.FP32_EPS).astype(np.float32)
-        zero = np.clip(zero_round(-lo / scale), 0, 255).astype(np.float32)
+        num = -lo if neg_lo else np.float32(0) - lo
+        zero = np.clip(zero_round(num / scale), 0, 255).astype(np.float32)
         if divide:
             y = x / scale[..., None]
         else:
@@ -280,6 +281,7 @@ KV_CACHE_MUTANTS = {
     "quantiser: zero point floored": ("quantize_rows_u8", _quantize_variant(zero_round=np.floor)),
     "quantiser: no eps floor on the scale": ("quantize_rows_u8", _quantize_variant(eps=False)),
     "quantiser: divides instead of multiplying by 1/scale": ("quantize_rows_u8", _quantize_variant(divide=True)),
+    "quantiser: zero point -0 for rows without negatives": ("quantize_rows_u8", _quantize_variant(neg_lo=True)),
     "append: written from position 0": ("_new_slots", _new_slots_variant(offset=False)),
     "commit: source node off by one": ("kv_commit_tree", _commit_variant(src_shift=-1)),
     "commit: overwrites the root": ("kv_commit_tree", _commit_variant(dst_start=0)),
