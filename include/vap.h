@@ -22,6 +22,10 @@
  *                    Batching & Speculative Decoding", section "The Modified Rejection Sampling
  *                    Algorithm"; syslabs.in, section "The core idea").
  *
+ * Around them, kv_append writes the step's new K/V rows into the cache before the attention,
+ * and kv_commit keeps the accepted draft tokens' rows (moving a tree's accepted path into
+ * place) and sets the committed lengths after verification.
+ *
  * Conventions shared by every entry point:
  *   - Data pointers are DEVICE pointers owned by the caller.  The library never allocates,
  *     frees or synchronises device memory on these paths (vap_get_device_error is the only
@@ -38,7 +42,8 @@
  *   - A workspace must be zero-filled before its first use (vap_workspace_init, or any
  *     zero-filled allocation); every call leaves it reusable.  Calls that share a workspace
  *     must be ordered (same stream, or synchronised).  A workspace serves one kind of call:
- *     either paged_attn_step or spec_verify, never both.
+ *     either paged_attn_step or spec_verify, never both; kv_append and kv_commit touch only the
+ *     sticky error word and may share either.
  */
 #ifndef VAP_H_
 #define VAP_H_
@@ -201,8 +206,6 @@ const char* vap_strerror(int code);
 /* Detail of the calling thread's last host-side error ("" if none). */
 const char* vap_last_error_message(void);
 
-/* ---- measurement helpers (not part of the step) ------------------------------------------ */
-
 /* Workspace bytes spec_verify_tree needs (its sticky error word). */
 size_t vap_tree_verify_workspace_bytes(void);
 
@@ -237,10 +240,71 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
                      int32_t num_seqs, int32_t num_nodes, int32_t vocab, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Workspace bytes kv_append and kv_commit need: they use only the sticky error word at its
+ * start, so the workspace of the step's paged_attn_step (used in stream order) serves too. */
+size_t vap_kv_workspace_bytes(void);
+
+/*
+ * kv_append -- write one step's new K and V rows into the paged cache (tempatgunting.com
+ * article, section "Anatomy of the KV Cache: Memory Layout, Paging and Quantization
+ * Trade-offs"), before paged_attn_step reads them.
+ *
+ *   k_new, v_new  bf16 [total_q][Hkv][D], 16-byte aligned; rows packed by sequence exactly as
+ *                 the query rows of paged_attn_step (sequence s owns q_lens[s] rows).
+ *   kv            the pool, written in place: bf16 [2][num_blocks][block_size][Hkv][D] when
+ *                 kv_scales is NULL, else uint8 codes of the same shape.
+ *   kv_scales     NULL, or fp32 [num_blocks][Hkv][block_size][4] written in place (as for
+ *                 paged_attn_step_u8).
+ *   block_tables, ctx_lens, q_lens, shape  as for paged_attn_step: ctx_lens already count the
+ *                 new rows, so row i of sequence s goes to position ctx_len - q_len + i.
+ *
+ * The 8-bit cache stores each (token, KV head) row of K and of V on its own (tempatgunting.com
+ * article, section "Quantization and Precision Choices for KV": per-token, asymmetric, separate
+ * for K and V), computed in fp32 from the bf16 input x (D values):
+ *   lo = min(0, min x), hi = max(0, max x), scale = max((hi - lo) / 255, FLT_EPSILON),
+ *   zero = clamp(rint((0 - lo) / scale), 0, 255), code = clamp(rint(x * (1 / scale)) + zero, 0, 255)
+ * with IEEE division and round-half-even; inputs must be finite.  Nothing but the new rows'
+ * entries (and their scales) is written.  Rows whose sequence has inconsistent lengths
+ * (VAP_DERR_LENS) or a block id outside the pool (VAP_DERR_BLOCK_ID) are skipped; a sum of
+ * q_lens other than total_q sets VAP_DERR_TOTAL_Q.  Rows of different sequences must not map to
+ * the same slot.  One kernel on `stream`.
+ */
+int kv_append(const void* k_new, const void* v_new, void* kv, float* kv_scales, const int32_t* block_tables,
+              const int32_t* ctx_lens, const int32_t* q_lens, const vap_attn_shape* shape, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * kv_commit -- keep the accepted draft tokens of a verified step and drop the rest
+ * (tempatgunting.com article, section "Speculative Decoding: Turning Verification Parallelism
+ * into Latency Wins": the rejected tokens' KV is rolled back).
+ *
+ *   kv, kv_scales  the pool as for kv_append, updated in place.
+ *   block_tables, ctx_lens, q_lens, shape  those of the verified step (the q_len rows are the
+ *                  last committed token and the drafts, at positions ctx_len - q_len ...).
+ *   path           NULL for a chain of drafts (nothing moves), or int32 [num_seqs][path_stride]:
+ *                  the accepted tree nodes a_1 < a_2 < ... < a_n (node i at position
+ *                  ctx_len - q_len + i; spec_verify_tree's out_path).  Node a_i's K, V (and
+ *                  scales) move to position ctx_len - q_len + i, so the kept tokens are
+ *                  contiguous.  With a path, n <= min(63, path_stride).
+ *   n_accepted     int32 [num_seqs], n in [0, q_len - 1].
+ *   out_ctx_lens   int32 [num_seqs] = ctx_len - q_len + 1 + n: the committed length (the last
+ *                  committed token and the n accepted drafts).  May be ctx_lens itself.
+ *
+ * Slots past the committed length keep stale entries; they are never read.  A sequence with
+ * inconsistent lengths or n (VAP_DERR_LENS), a path that is not increasing within [1, q_len - 1]
+ * (VAP_DERR_TREE) or a block id outside the pool (VAP_DERR_BLOCK_ID) is left unchanged with
+ * out_ctx_len = ctx_len.  One workgroup per sequence on `stream`.
+ */
+int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
+              const int32_t* path, int32_t path_stride, const int32_t* n_accepted, int32_t* out_ctx_lens,
+              const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- measurement helpers (not part of the step) ------------------------------------------ */
+
 /* Kernel timer.  While enabled, every paged_attn_step records a hipEvent pair around its
- * attention kernel (kind 0), every spec_verify around its kernel (kind 1) and every
- * spec_verify_tree around its kernel (kind 2), on the caller's
- * stream, into a ring of 4096 pairs per kind.  vap_timer_read synchronises on the recorded
+ * attention kernel (kind 0), every spec_verify around its kernel (kind 1), every
+ * spec_verify_tree (kind 2), kv_append (kind 3) and kv_commit (kind 4) around theirs, on the
+ * caller's stream, into a ring of 4096 pairs per kind.  vap_timer_read synchronises on the recorded
  * events, returns the summed milliseconds and the number of pairs, and resets the ring when
  * `reset` is nonzero. */
 int vap_timer_enable(int on);

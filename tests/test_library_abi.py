@@ -20,7 +20,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = vap.header_functions()
-    assert {"paged_attn_step", "paged_attn_step_u8", "paged_attn_step_tree", "spec_verify", "spec_verify_tree", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
+    assert {"paged_attn_step", "paged_attn_step_u8", "paged_attn_step_tree", "spec_verify", "spec_verify_tree", "kv_append", "kv_commit", "vap_attn_workspace_bytes", "vap_verify_workspace_bytes",
             "vap_get_device_error", "vap_strerror"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,6 +80,31 @@ def test_tree_verify_rejected_on_host(lib):
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 0, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 10, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 0, 8, 10, None, 0, None) == B.VAP_OK
+
+
+def test_kv_append_and_commit_rejected_on_host(lib):
+    s = B.AttnShape(4, 8, 2, 64, 16, 35, 16, 4, 0.0)
+    fake = ctypes.c_void_p(256)       # never dereferenced: the host check fails first
+    ws = lib.vap_kv_workspace_bytes()
+    assert ws >= 4
+    append = lambda *a: lib.kv_append(*a)
+    # NULL pool / workspace, small workspace, misaligned new rows, bad shape
+    assert append(fake, fake, None, None, fake, fake, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    assert append(fake, fake, fake, None, fake, fake, fake, ctypes.byref(s), fake, 2, None) == B.VAP_ENOSPC
+    assert append(ctypes.c_void_p(258), fake, fake, None, fake, fake, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    assert append(fake, fake, fake, None, None, fake, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    bad = B.AttnShape(4, 8, 2, 96, 16, 35, 16, 4, 0.0)
+    assert append(fake, fake, fake, None, fake, fake, fake, ctypes.byref(bad), fake, ws, None) == B.VAP_EINVAL
+    empty = B.AttnShape(0, 8, 2, 64, 16, 35, 16, 0, 0.0)
+    assert append(None, None, None, None, None, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
+    bad_empty = B.AttnShape(0, 8, 2, 64, 16, 35, 16, 3, 0.0)
+    assert append(None, None, None, None, None, None, None, ctypes.byref(bad_empty), None, 0, None) == B.VAP_EINVAL
+    commit = lambda *a: lib.kv_commit(*a)
+    assert commit(None, None, fake, fake, fake, None, 0, fake, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    assert commit(fake, None, fake, fake, fake, None, 0, None, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    assert commit(fake, None, fake, fake, fake, fake, 0, fake, fake, ctypes.byref(s), fake, ws, None) == B.VAP_EINVAL
+    assert commit(fake, None, fake, fake, fake, None, 0, fake, fake, ctypes.byref(s), fake, 0, None) == B.VAP_ENOSPC
+    assert commit(None, None, None, None, None, None, 0, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
 
 
 def test_workspace_sizes_are_consistent(lib):

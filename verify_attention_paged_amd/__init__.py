@@ -7,6 +7,8 @@ memory and streams only.
     paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale=0.0)
     spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None)
     spec_verify_tree(p, q, parents, tokens, uniforms)
+    kv_append(k_new, v_new, kv_pool, block_tables, ctx_lens, q_lens)
+    kv_commit(kv_pool, block_tables, ctx_lens, q_lens, n_accepted, path=None)
     (paged_attn_step also takes kv_scales= for an 8-bit cache and tree_mask= for token trees)
 """
 
@@ -23,11 +25,16 @@ from ._binding import (  # noqa: F401
     TIMER_ATTENTION,
     TIMER_VERIFY,
     TIMER_TREE_VERIFY,
+    TIMER_KV_APPEND,
+    TIMER_KV_COMMIT,
     attn_shape,
     attn_workspace,
     device_info,
     get_device_error,
     header_functions,
+    kv_append,
+    kv_commit,
+    kv_workspace,
     load_library,
     paged_attn_step,
     spec_verify,

@@ -19,7 +19,7 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
 
 VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
 DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
-TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY = 0, 1, 2
+TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY, TIMER_KV_APPEND, TIMER_KV_COMMIT = 0, 1, 2, 3, 4
 
 
 class VapError(RuntimeError):
@@ -55,6 +55,9 @@ SIGNATURES = {
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_tree_verify_workspace_bytes": (_sz, []),
     "spec_verify_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "vap_kv_workspace_bytes": (_sz, []),
+    "kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
+    "kv_commit": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "vap_get_device_error": (ctypes.c_int, [_vp, _vp, _pi32, ctypes.c_int]),
     "vap_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -295,6 +298,101 @@ def spec_verify_tree(p, q, parents, tokens, uniforms, out_ids=None, out_path=Non
                                   _stream(stream))
     _check(rc)
     return out_ids, out_path, n_accepted
+
+
+# ---------------------------------------------------------------------------------------
+# KV append / commit
+# ---------------------------------------------------------------------------------------
+
+def kv_workspace(device=None) -> torch.Tensor:
+    n = load_library().vap_kv_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
+
+
+def _kv_checks(kv_pool, kv_scales, block_tables, ctx_lens, q_lens, dev):
+    kv8 = kv_scales is not None
+    _need(kv_pool, "kv_pool", torch.uint8 if kv8 else torch.bfloat16, 5, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    _need(q_lens, "q_lens", torch.int32, 1, dev)
+    two, NB, BS, Hkv, D = kv_pool.shape
+    if two != 2:
+        raise ValueError(f"kv_pool must be [2, num_blocks, block_size, Hkv, D], got {tuple(kv_pool.shape)}")
+    if kv8:
+        _need(kv_scales, "kv_scales", torch.float32, 4, dev)
+        if tuple(kv_scales.shape) != (NB, Hkv, BS, 4):
+            raise ValueError("kv_scales must be [num_blocks, Hkv, block_size, 4]")
+    B = block_tables.shape[0]
+    if ctx_lens.numel() != B or q_lens.numel() != B:
+        raise ValueError("ctx_lens and q_lens need one entry per block-table row")
+
+
+def kv_append(k_new, v_new, kv_pool, block_tables, ctx_lens, q_lens, *, kv_scales=None,
+              workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Write new K/V rows into the paged pool in place; see ``kv_append`` in include/vap.h.
+
+    k_new, v_new bf16 [T, Hkv, D]; kv_pool bf16 [2, NB, bs, Hkv, D] (or uint8 codes with
+    ``kv_scales`` fp32 [NB, Hkv, bs, 4], both written); block_tables int32 [B, MB]; ctx_lens
+    (counting the new rows) and q_lens int32 [B].
+    """
+    lib = load_library()
+    dev = kv_pool.device
+    _kv_checks(kv_pool, kv_scales, block_tables, ctx_lens, q_lens, dev)
+    _need(k_new, "k_new", torch.bfloat16, 3, dev)
+    _need(v_new, "v_new", torch.bfloat16, 3, dev)
+    _, NB, BS, Hkv, D = kv_pool.shape
+    if tuple(k_new.shape[1:]) != (Hkv, D) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new and v_new must be [T, {Hkv}, {D}]")
+    B, MB = block_tables.shape
+    shape = AttnShape(B, Hkv, Hkv, D, BS, NB, MB, k_new.shape[0], 0.0)
+    if workspace is None:
+        workspace = kv_workspace(dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.kv_append(k_new.data_ptr(), v_new.data_ptr(), kv_pool.data_ptr(),
+                           kv_scales.data_ptr() if kv_scales is not None else None, block_tables.data_ptr(),
+                           ctx_lens.data_ptr(), q_lens.data_ptr(), ctypes.byref(shape), workspace.data_ptr(),
+                           workspace.numel(), _stream(stream))
+    _check(rc)
+
+
+def kv_commit(kv_pool, block_tables, ctx_lens, q_lens, n_accepted, *, path=None, kv_scales=None,
+              out_ctx_lens=None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Keep the accepted draft tokens; see ``kv_commit`` in include/vap.h.
+
+    n_accepted int32 [B]; path None (a chain) or int32 [B, stride] of accepted tree nodes
+    (spec_verify_tree's out_path).  The pool (and ``kv_scales``) change in place; returns the
+    committed lengths int32 [B] (``out_ctx_lens``, which may be ``ctx_lens`` itself).
+    """
+    lib = load_library()
+    dev = kv_pool.device
+    _kv_checks(kv_pool, kv_scales, block_tables, ctx_lens, q_lens, dev)
+    _need(n_accepted, "n_accepted", torch.int32, 1, dev)
+    B, MB = block_tables.shape
+    if n_accepted.numel() != B:
+        raise ValueError("n_accepted needs one entry per block-table row")
+    stride = 0
+    if path is not None:
+        _need(path, "path", torch.int32, 2, dev)
+        if path.shape[0] != B:
+            raise ValueError("path must be [B, stride]")
+        stride = path.shape[1]
+    if out_ctx_lens is None:
+        out_ctx_lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_ctx_lens, "out_ctx_lens", torch.int32, 1, dev)
+    _, NB, BS, Hkv, D = kv_pool.shape
+    shape = AttnShape(B, Hkv, Hkv, D, BS, NB, MB, 0, 0.0)
+    if workspace is None:
+        workspace = kv_workspace(dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.kv_commit(kv_pool.data_ptr(), kv_scales.data_ptr() if kv_scales is not None else None,
+                           block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
+                           path.data_ptr() if path is not None else None, stride, n_accepted.data_ptr(),
+                           out_ctx_lens.data_ptr(), ctypes.byref(shape), workspace.data_ptr(), workspace.numel(),
+                           _stream(stream))
+    _check(rc)
+    return out_ctx_lens
 
 
 # ---------------------------------------------------------------------------------------

@@ -78,12 +78,13 @@ const DevInfo* device_info() {
 // ---- kernel timer ------------------------------------------------------------------------
 
 constexpr int kTimerSlots = 4096;
+constexpr int kTimerKinds = 5;   // attention, spec_verify, spec_verify_tree, kv_append, kv_commit
 struct Timer {
   bool on = false;
   bool created = false;
-  hipEvent_t start[3][kTimerSlots];
-  hipEvent_t stop[3][kTimerSlots];
-  int count[3] = {0, 0, 0};
+  hipEvent_t start[kTimerKinds][kTimerSlots];
+  hipEvent_t stop[kTimerKinds][kTimerSlots];
+  int count[kTimerKinds] = {};
 };
 Timer g_timer;
 
@@ -159,6 +160,29 @@ int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2][c.kv8 ? 1 : 0];
   const int per_cu = c.rows_per_seq >= 8 ? 2 : 1;
   return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * kWavesPerWG);
+}
+
+// Shape and pointer checks shared by kv_append and kv_commit.
+int check_kv_call(const vap_attn_shape* shape, const void* kv, const float* kv_scales, const void* workspace,
+                  size_t workspace_bytes) {
+  AttnPlanChoice c;
+  const int rc = check_attn_shape(shape, &c);
+  if (rc != VAP_OK) return rc;
+  if ((long long)shape->num_blocks * shape->block_size >= (1LL << 31))
+    return fail(VAP_EINVAL, "num_blocks*block_size exceeds 2^31");
+  if (shape->num_seqs == 0) return VAP_OK;
+  if (!kv || !workspace) return fail(VAP_EINVAL, "NULL data pointer");
+  if ((reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(kv_scales)) & 15)
+    return fail(VAP_EINVAL, "the KV pool and its scales must be 16-byte aligned");
+  if (workspace_bytes < vap_kv_workspace_bytes())
+    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes, vap_kv_workspace_bytes());
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(VAP_EINVAL, "workspace must be 16-byte aligned");
+  return VAP_OK;
+}
+
+const DevInfo* gfx950_or_null() {
+  const DevInfo* d = device_info();
+  return (d != nullptr && d->gfx950) ? d : nullptr;
 }
 
 }  // namespace
@@ -415,6 +439,87 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   return ok();
 }
 
+size_t vap_kv_workspace_bytes(void) { return 256; }
+
+int kv_append(const void* k_new, const void* v_new, void* kv, float* kv_scales, const int32_t* block_tables,
+              const int32_t* ctx_lens, const int32_t* q_lens, const vap_attn_shape* shape, void* workspace,
+              size_t workspace_bytes, void* stream_) {
+  int rc = check_kv_call(shape, kv, kv_scales, workspace, workspace_bytes);
+  if (rc != VAP_OK) return rc;
+  const vap_attn_shape& s = *shape;
+  if (s.num_seqs == 0) {
+    if (s.total_q != 0) return fail(VAP_EINVAL, "num_seqs=0 but total_q=%d", s.total_q);
+    return ok();
+  }
+  if (!block_tables || !ctx_lens || !q_lens || (s.total_q > 0 && (!k_new || !v_new)))
+    return fail(VAP_EINVAL, "NULL data pointer");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(VAP_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const DevInfo* d = gfx950_or_null();
+  if (d == nullptr) return fail(VAP_ENODEV, "current device is not gfx950");
+  KVAppendParams P;
+  P.k_new = static_cast<const uint16_t*>(k_new);
+  P.v_new = static_cast<const uint16_t*>(v_new);
+  P.kv = kv;
+  P.kv_scales = kv_scales;
+  P.tables = block_tables;
+  P.ctx_lens = ctx_lens;
+  P.q_lens = q_lens;
+  P.B = s.num_seqs;
+  P.Hkv = s.num_kv_heads;
+  P.BS = s.block_size;
+  P.NB = s.num_blocks;
+  P.MB = s.max_blocks_per_seq;
+  P.T = s.total_q;
+  P.err = static_cast<int32_t*>(workspace);
+  // one wave per (row, group of 64 / (D / 8) heads); at most two workgroups per CU, each of
+  // which rebuilds the row starts of the whole batch in LDS
+  const int hpp = 64 / (s.head_dim / 8);
+  const long long items = (long long)s.total_q * ((s.num_kv_heads + hpp - 1) / hpp);
+  const long long wg = std::max(1LL, std::min((items + 3) / 4, 2LL * d->num_cus));
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  timer_begin(3, stream);
+  const hipError_t e = launch_kv_append(P, s.head_dim, kv_scales != nullptr, (int)wg, stream);
+  timer_end(3, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "kv_append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int32_t* ctx_lens, const int32_t* q_lens,
+              const int32_t* path, int32_t path_stride, const int32_t* n_accepted, int32_t* out_ctx_lens,
+              const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream_) {
+  int rc = check_kv_call(shape, kv, kv_scales, workspace, workspace_bytes);
+  if (rc != VAP_OK) return rc;
+  const vap_attn_shape& s = *shape;
+  if (s.num_seqs == 0) return ok();
+  if (!block_tables || !ctx_lens || !q_lens || !n_accepted || !out_ctx_lens) return fail(VAP_EINVAL, "NULL data pointer");
+  if (path != nullptr && path_stride < 1) return fail(VAP_EINVAL, "path_stride=%d < 1", path_stride);
+  if (gfx950_or_null() == nullptr) return fail(VAP_ENODEV, "current device is not gfx950");
+  KVCommitParams P;
+  P.kv = kv;
+  P.kv_scales = kv_scales;
+  P.tables = block_tables;
+  P.ctx_lens = ctx_lens;
+  P.q_lens = q_lens;
+  P.path = path;
+  P.path_stride = path_stride;
+  P.n_accepted = n_accepted;
+  P.out_lens = out_ctx_lens;
+  P.B = s.num_seqs;
+  P.Hkv = s.num_kv_heads;
+  P.D = s.head_dim;
+  P.BS = s.block_size;
+  P.NB = s.num_blocks;
+  P.MB = s.max_blocks_per_seq;
+  P.err = static_cast<int32_t*>(workspace);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  timer_begin(4, stream);
+  const hipError_t e = launch_kv_commit(P, kv_scales != nullptr, stream);
+  timer_end(4, stream);
+  if (e != hipSuccess) return fail(VAP_EHIP, "kv_commit launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int vap_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return fail(VAP_EINVAL, "NULL workspace");
   if (bytes == 0) return ok();
@@ -439,7 +544,7 @@ int vap_get_device_error(void* workspace, void* stream_, int32_t* err_out, int c
 int vap_timer_enable(int on) {
   std::lock_guard<std::mutex> lock(g_mu);
   if (on && !g_timer.created) {
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < kTimerKinds; ++k)
       for (int i = 0; i < kTimerSlots; ++i) {
         if (hipEventCreate(&g_timer.start[k][i]) != hipSuccess || hipEventCreate(&g_timer.stop[k][i]) != hipSuccess)
           return fail(VAP_EHIP, "hipEventCreate failed");
@@ -451,7 +556,7 @@ int vap_timer_enable(int on) {
 }
 
 int vap_timer_read(int kind, double* total_ms, int32_t* count, int reset) {
-  if (kind < 0 || kind > 2 || !total_ms || !count) return fail(VAP_EINVAL, "bad timer arguments");
+  if (kind < 0 || kind >= kTimerKinds || !total_ms || !count) return fail(VAP_EINVAL, "bad timer arguments");
   double sum = 0.0;
   const int n = g_timer.count[kind];
   for (int i = 0; i < n; ++i) {

@@ -158,4 +158,36 @@ struct TreeVerifyParams {
 
 hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream);
 
+// ---- KV append / commit ----------------------------------------------------------------------
+
+struct KVAppendParams {
+  const uint16_t* k_new;    // [T][Hkv][D] bf16, rows packed by sequence
+  const uint16_t* v_new;
+  void* kv;                 // bf16 pool [2][NB][BS][Hkv][D], or uint8 codes of the same shape
+  float* kv_scales;         // 8-bit only: [NB][Hkv][BS][4] = (k_scale, k_zero, v_scale, v_zero)
+  const int32_t* tables;    // [B][MB]
+  const int32_t* ctx_lens;  // [B], counting the new rows
+  const int32_t* q_lens;    // [B]
+  int32_t B, Hkv, BS, NB, MB, T;
+  int32_t* err;
+};
+
+struct KVCommitParams {
+  void* kv;
+  float* kv_scales;         // 8-bit only
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  const int32_t* path;      // [B][path_stride] accepted node indices, or nullptr for a chain
+  int32_t path_stride;
+  const int32_t* n_accepted;
+  int32_t* out_lens;        // may alias ctx_lens
+  int32_t B, Hkv, D, BS, NB, MB;
+  int32_t* err;
+};
+
+size_t kv_append_lds_bytes(int B);
+hipError_t launch_kv_append(const KVAppendParams& p, int D, bool u8, int num_wg, hipStream_t stream);
+hipError_t launch_kv_commit(const KVCommitParams& p, bool u8, hipStream_t stream);
+
 }  // namespace vap

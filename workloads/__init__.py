@@ -28,4 +28,5 @@ from .generate import (  # noqa: F401
     TreeVerifyInputs,
     make_tree_verify_from_probs,
     tree_verify_config,
+    new_kv_rows,
 )

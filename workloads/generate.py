@@ -20,6 +20,11 @@ Unused block-table entries are -1.
 They are drawn directly in that shape (no quantiser runs here); the scales of unowned slots and
 of rows past L_s are poisoned instead of the codes.
 
+New K/V rows of a step (``new_kv_rows``), in draw order: per (row, KV head) a spread
+sigma ~ U[0.05, 4] and an offset mu ~ N(0, 0.5) for K, then the same for V; then K and V values
+sigma * N(0, 1) + mu, rounded to bf16.  The varying ranges and signs exercise the 8-bit
+quantiser's per-row scales and zero points.
+
 Speculative-verification inputs, in draw order:
   1. logits (target rows [B, k+1, V], draft rows [B, k, V]) per the config,
   2. draft tokens x_i ~ q_i (one categorical draw per draft position),
@@ -368,6 +373,20 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
         inp.tree_mask = torch.from_numpy(np.concatenate([tree_masks(random_tree_parents(rng, int(q)))
                                                          for q in Q]))
     return inp
+
+
+def new_kv_rows(seed: int, total_q: int, num_kv_heads: int, head_dim: int):
+    """(k_new, v_new) bf16 [total_q, Hkv, D]: the K/V rows a step appends to the cache."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (total_q, num_kv_heads)
+    sig = rng.uniform(0.05, 4.0, size=(2, *shape)).astype(np.float32)
+    mu = (0.5 * rng.standard_normal((2, *shape))).astype(np.float32)
+    out = []
+    for plane in range(2):
+        z = rng.standard_normal((*shape, head_dim), dtype=np.float32)
+        x = z * sig[plane][..., None] + mu[plane][..., None]
+        out.append(torch.from_numpy(x).to(torch.bfloat16))
+    return out[0], out[1]
 
 
 # ----------------------------------------------------------------------------------------
