@@ -9,6 +9,8 @@ Default run (one JSON line on stdout):
     q_len 5, vocab 128256) -> verified tokens/s and the verifier's own GB/s;
   * roofline: the attention kernel's average duration from HIP events recorded on its own
     stream (the library's kernel timer) against the 8 TB/s HBM peak;
+  * kv_cache: kv_append of the decode batch's new rows (bf16 and 8-bit), append + attention
+    back to back, and kv_commit of the tree step's accepted paths;
   * cpu_baseline: the fp64 CPU oracle on the same decode batch, on the host's cores.
 
 Inputs are resident in HBM before timing starts.  The KV pool (and the verifier's
@@ -77,6 +79,19 @@ def verify_bytes(n_accepted, k, V) -> int:
         total += 8 * k + 4 * (k + 1) + 4 * k + 4 * (k + 2)   # gathers, uniforms, ids, outputs
         total += 8 * V if int(n) < k else 4 * V                 # residual row pair or bonus row
     return total
+
+
+def kv_append_bytes(T, B, Hkv, D, u8) -> int:
+    """New K and V rows read as bf16, written as bf16 or as codes + one (scale, zero) pair each,
+    plus the lengths, the q_lens scan and one block id per row."""
+    written = 2 * T * Hkv * D + 16 * T * Hkv if u8 else 4 * T * Hkv * D
+    return 4 * T * Hkv * D + written + 8 * B + 4 * T
+
+
+def kv_commit_bytes(n_moved, B, Hkv, D, u8) -> int:
+    """Each moved row's K and V (and scales) read and written once, plus lengths, counts, paths."""
+    row = (2 * Hkv * D + 16 * Hkv) if u8 else 4 * Hkv * D
+    return 2 * n_moved * row + 16 * B
 
 
 def code_only(text: str) -> str:
@@ -360,6 +375,57 @@ def run_default(args, dev):
         f"{qnbytes / (qms * 1e-3) / 1e9:.1f} GB/s of {qnbytes / 1e6:.1f} MB; attention kernel "
         f"{qkernel_ms * 1e3:.1f} us -> {qnbytes / (qkernel_ms * 1e-3) / 1e9:.1f} GB/s")
 
+    # ---- KV append (before attention) and commit (after verification)
+    kinp = inp
+    T, Hkv, D = kinp.total_q, kinp.num_kv_heads, kinp.head_dim
+    k_new, v_new = (x.to(dev) for x in workloads.new_kv_rows(1, T, Hkv, D))
+    kvws = vap.kv_workspace(dev)
+    app = lambda i: vap.kv_append(k_new, v_new, pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
+                                  d["q_lens"], workspace=kvws)
+    app8 = lambda i: vap.kv_append(k_new, v_new, qpools[i % len(qpools)], qd["block_tables"], qd["ctx_lens"],
+                                   qd["q_lens"], kv_scales=qd["scales"][i % len(qpools)], workspace=kvws)
+
+    def app_step(i):
+        app(i)
+        step(i)
+
+    vap.timer_enable(True)
+    res = {}
+    for key, fn in (("bf16", app), ("u8", app8)):
+        time_loop(fn, 0, args.warmup)
+        vap.timer_read(vap.TIMER_KV_APPEND, reset=True)
+        call_ms, _ = time_loop(fn, args.steps, 0)
+        ktot, kcnt = vap.timer_read(vap.TIMER_KV_APPEND, reset=True)
+        res[key] = (call_ms, ktot / max(1, kcnt))
+    time_loop(app_step, 0, args.warmup)
+    as_ms, _ = time_loop(app_step, args.steps, 0)
+    # commit the tree step's accepted paths (as the tree verifier left them) on one tree pool
+    out_lens = torch.empty_like(td["ctx_lens"])
+    com = lambda i: vap.kv_commit(tpools[0], td["block_tables"], td["ctx_lens"], td["q_lens"], t_n, path=t_path,
+                                  out_ctx_lens=out_lens, workspace=kvws)
+    time_loop(com, 0, args.warmup)
+    vap.timer_read(vap.TIMER_KV_COMMIT, reset=True)
+    com_ms, _ = time_loop(com, args.steps, 0)
+    ctot, ccnt = vap.timer_read(vap.TIMER_KV_COMMIT, reset=True)
+    vap.timer_enable(False)
+    if vap.get_device_error(kvws):
+        raise RuntimeError("device reported a data error in kv_append / kv_commit")
+    moved = sum(int(sum(1 for i in range(int(nn)) if tp[i] != i + 1)) for tp, nn in zip(t_path.cpu().numpy(), tn_host))
+    ab = kv_append_bytes(T, kinp.num_seqs, Hkv, D, False)
+    ab8 = kv_append_bytes(T, kinp.num_seqs, Hkv, D, True)
+    cb = kv_commit_bytes(moved, tinp.num_seqs, tinp.num_kv_heads, tinp.head_dim, False)
+    ckern = ctot / max(1, ccnt)
+    log(f"kv_append decode batch: bf16 {res['bf16'][1] * 1e3:.2f} us kernel ({res['bf16'][0] * 1e3:.2f} us/call), "
+        f"u8 {res['u8'][1] * 1e3:.2f} us kernel; append + attention {as_ms * 1e3:.1f} us vs attention alone "
+        f"{ms * 1e3:.1f} us; kv_commit tree step {ckern * 1e3:.2f} us kernel ({moved} rows moved)")
+    kv_line = {"workload": "kv_append of the llama3_8b_decode batch's 64 new rows (8 kv heads, head_dim 128), "
+                           "bf16 and 8-bit; kv_commit of the tree_verify_step batch's accepted paths",
+               "append_bf16_kernel_ms": round(res["bf16"][1], 5), "append_bf16_ms_per_call": round(res["bf16"][0], 5),
+               "append_bf16_bytes": ab, "append_bf16_GB_per_s": round(ab / (res["bf16"][1] * 1e-3) / 1e9, 2),
+               "append_u8_kernel_ms": round(res["u8"][1], 5), "append_u8_bytes": ab8,
+               "decode_step_with_append_ms": round(as_ms, 5),
+               "commit_tree_kernel_ms": round(ckern, 5), "commit_rows_moved": moved, "commit_bytes": cb}
+
     # ---- CPU baseline (oracle), rank 0 at N = 1 only
     cpu = None
     if not args.no_cpu_baseline:
@@ -408,6 +474,7 @@ def run_default(args, dev):
                             "GB_per_s": round(qnbytes / (qms * 1e-3) / 1e9, 2),
                             "attention_kernel_ms": round(qkernel_ms, 5),
                             "speedup_vs_bf16_step": round(ms / qms, 3)},
+        "kv_cache": kv_line,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attn_main_kernel<128,16,1>",

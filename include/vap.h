@@ -301,10 +301,11 @@ int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int
 
 /* ---- measurement helpers (not part of the step) ------------------------------------------ */
 
-/* Kernel timer.  While enabled, every paged_attn_step records a hipEvent pair around its
- * attention kernel (kind 0), every spec_verify around its kernel (kind 1), every
- * spec_verify_tree (kind 2), kv_append (kind 3) and kv_commit (kind 4) around theirs, on the
- * caller's stream, into a ring of 4096 pairs per kind.  vap_timer_read synchronises on the recorded
+/* Kernel timer.  While enabled, every paged_attn_step times its attention kernel (kind 0),
+ * every spec_verify its kernel (kind 1), and spec_verify_tree (kind 2), kv_append (kind 3) and
+ * kv_commit (kind 4) theirs, into a ring of 4096 event pairs per kind.  The events are stamped
+ * by the kernel launch itself (hipExtLaunchKernelGGL), so each pair spans the kernel's execution
+ * without the wait before its first wave.  vap_timer_read synchronises on the recorded
  * events, returns the summed milliseconds and the number of pairs, and resets the ring when
  * `reset` is nonzero. */
 int vap_timer_enable(int on);

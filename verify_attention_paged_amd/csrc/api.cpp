@@ -88,15 +88,19 @@ struct Timer {
 };
 Timer g_timer;
 
-void timer_begin(int kind, hipStream_t stream) {
-  if (!g_timer.on || g_timer.count[kind] >= kTimerSlots) return;
-  (void)hipEventRecord(g_timer.start[kind][g_timer.count[kind]], stream);
+// Events for the next timed launch of `kind` (null pair when the timer is off or its ring is
+// full); timer_commit keeps them once the launch has been enqueued.
+KTimer timer_slot(int kind) {
+  KTimer t;
+  if (g_timer.on && g_timer.count[kind] < kTimerSlots) {
+    t.start = g_timer.start[kind][g_timer.count[kind]];
+    t.stop = g_timer.stop[kind][g_timer.count[kind]];
+  }
+  return t;
 }
 
-void timer_end(int kind, hipStream_t stream) {
-  if (!g_timer.on || g_timer.count[kind] >= kTimerSlots) return;
-  (void)hipEventRecord(g_timer.stop[kind][g_timer.count[kind]], stream);
-  ++g_timer.count[kind];
+void timer_commit(int kind, const KTimer& t, hipError_t launch) {
+  if (t.start != nullptr && launch == hipSuccess) ++g_timer.count[kind];
 }
 
 // ---- attention shape checks ---------------------------------------------------------------
@@ -300,9 +304,9 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
     e = launch_attn_plan(P, stream);
     if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
   }
-  timer_begin(0, stream);
-  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / kWavesPerWG, stream);
-  timer_end(0, stream);
+  const KTimer t = timer_slot(0);
+  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / kWavesPerWG, stream, t);
+  timer_commit(0, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
   e = launch_attn_combine(P, c.D, stream);
   if (e != hipSuccess) return fail(VAP_EHIP, "combine launch: %s", hipGetErrorString(e));
@@ -391,9 +395,9 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
   const bool vec4 = (vocab % 4 == 0) &&
                     ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(k ? q : p)) & 15) == 0;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  timer_begin(1, stream);
-  hipError_t e = launch_spec_verify(P, vec4, stream);
-  timer_end(1, stream);
+  const KTimer t = timer_slot(1);
+  hipError_t e = launch_spec_verify(P, vec4, stream, t);
+  timer_commit(1, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -432,9 +436,9 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   P.err = static_cast<int32_t*>(workspace);
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  timer_begin(2, stream);
-  const hipError_t e = launch_tree_verify(P, stream);
-  timer_end(2, stream);
+  const KTimer t = timer_slot(2);
+  const hipError_t e = launch_tree_verify(P, stream, t);
+  timer_commit(2, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "tree verify launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -478,9 +482,9 @@ int kv_append(const void* k_new, const void* v_new, void* kv, float* kv_scales, 
   const long long items = (long long)s.total_q * ((s.num_kv_heads + hpp - 1) / hpp);
   const long long wg = std::max(1LL, std::min((items + 3) / 4, 2LL * d->num_cus));
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  timer_begin(3, stream);
-  const hipError_t e = launch_kv_append(P, s.head_dim, kv_scales != nullptr, (int)wg, stream);
-  timer_end(3, stream);
+  const KTimer t = timer_slot(3);
+  const hipError_t e = launch_kv_append(P, s.head_dim, kv_scales != nullptr, (int)wg, stream, t);
+  timer_commit(3, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "kv_append launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -513,9 +517,9 @@ int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int
   P.MB = s.max_blocks_per_seq;
   P.err = static_cast<int32_t*>(workspace);
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  timer_begin(4, stream);
-  const hipError_t e = launch_kv_commit(P, kv_scales != nullptr, stream);
-  timer_end(4, stream);
+  const KTimer t = timer_slot(4);
+  const hipError_t e = launch_kv_commit(P, kv_scales != nullptr, stream, t);
+  timer_commit(4, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "kv_commit launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -807,9 +807,10 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_A
 }
 
 template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
-hipError_t launch_main_t(const AttnParams& p, int num_wg, hipStream_t stream) {
+hipError_t launch_main_t(const AttnParams& p, int num_wg, hipStream_t stream, KTimer t) {
   const size_t lds = LDS_PLAN ? attn_main_lds_bytes(p.B) : 0;
-  hipLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(kAttnThreads), lds, stream, p);
+  hipExtLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(kAttnThreads),
+                        (uint32_t)lds, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 
@@ -821,15 +822,16 @@ size_t attn_main_lds_bytes(int B) { return size_t(4 * B + 1) * sizeof(int); }
   X(64, 16, 1) X(64, 16, 2) X(64, 32, 1) X(64, 32, 2) \
   X(128, 16, 1) X(128, 16, 2) X(128, 32, 1) X(128, 32, 2)
 
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream) {
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream,
+                            KTimer t) {
   const bool lds = p.B <= kLdsPlanMaxSeqs;
 #define X(d, bs, nrt)                                                                         \
   if (D == d && BS == bs && NRT == nrt) {                                                     \
     if (kv8)                                                                                  \
-      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, stream)                   \
-                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, stream);                 \
-    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, stream)                    \
-               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, stream);                  \
+      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, stream, t)                   \
+                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, stream, t);                 \
+    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, stream, t)                    \
+               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, stream, t);                  \
   }
   VAP_ATTN_VARIANTS(X)
 #undef X

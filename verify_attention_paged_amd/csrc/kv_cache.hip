@@ -37,6 +37,7 @@ namespace {
 constexpr int kAppendThreads = 256;
 constexpr int kCommitThreads = 256;
 constexpr int kCommitStageChunks = 2048;   // 32 KB of 16-byte chunks staged per pass
+constexpr int kAppendStagedSeqs = 4096;    // batches up to this size keep first new positions in LDS
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -78,12 +79,21 @@ __device__ __forceinline__ uint2 quantize8(const float* x, float* scale_out, flo
   return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
 }
 
-// s_start[s] = sum of clamp(q_lens[r], 0, T) over r < s, saturated at T + 1, for s = 0 .. B.
-// Returns the unsaturated total on every thread.
-__device__ long long build_row_starts(const int32_t* __restrict__ q_lens, int B, int T, int32_t* s_start,
+// s_start[s] = sum of clamp(q_lens[r], 0, T + 1) over r < s, saturated at T + 1, for s = 0 .. B.
+// With s_base != nullptr also s_base[s] = ctx_len - q_len (the first new position), or -1 when the
+// sequence's lengths are inconsistent.  Returns the unsaturated total on every thread.
+__device__ long long build_row_starts(const KVAppendParams& p, int32_t* s_start, int32_t* s_base,
                                       long long* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int s = tid; s < B; s += kAppendThreads) s_start[s] = min(max(q_lens[s], 0), T + 1);
+  const int B = p.B, T = p.T;
+  for (int s = tid; s < B; s += kAppendThreads) {
+    const int Q = p.q_lens[s];
+    s_start[s] = min(max(Q, 0), T + 1);
+    if (s_base != nullptr) {
+      const int L = p.ctx_lens[s];
+      s_base[s] = (Q >= 1 && Q <= L && (L - 1) / p.BS + 1 <= p.MB) ? L - Q : -1;
+    }
+  }
   __syncthreads();
   const int span = (B + kAppendThreads - 1) / kAppendThreads;
   const int s0 = tid * span;
@@ -118,22 +128,40 @@ __device__ long long build_row_starts(const int32_t* __restrict__ q_lens, int B,
 
 template <int D, bool U8>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(KVAppendParams p) {
-  extern __shared__ int32_t s_start[];   // [B + 1]
+  extern __shared__ int32_t s_lds[];     // [B + 1] row starts, then [B] first new positions
   __shared__ long long s_wsum[kAppendThreads / 64];
   constexpr int LPH = D / 8;             // lanes per head row
   constexpr int HPP = 64 / LPH;          // heads per wave pass
   const int lane = threadIdx.x & 63;
   const int B = p.B, T = p.T, Hkv = p.Hkv, BS = p.BS;
-  const long long total = build_row_starts(p.q_lens, B, T, s_start, s_wsum);
-  int derr = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0 && total != T) derr |= VAP_DERR_TOTAL_Q;
+  const bool staged = B <= kAppendStagedSeqs;
+  int32_t* s_start = s_lds;
+  int32_t* s_base = staged ? s_lds + B + 1 : nullptr;
 
   const int passes = (Hkv + HPP - 1) / HPP;
   const long long items = (long long)T * passes;
   const int g = lane / LPH, sub = lane % LPH;
   const size_t plane = (size_t)p.NB * BS * Hkv * D;
   const long long stride = (long long)gridDim.x * (kAppendThreads / 64);
-  for (long long it = (long long)blockIdx.x * (kAppendThreads / 64) + (threadIdx.x >> 6); it < items; it += stride) {
+  long long it = (long long)blockIdx.x * (kAppendThreads / 64) + (threadIdx.x >> 6);
+  // an item's new rows do not depend on the lengths: the first item's loads start before the scan
+  auto load_rows = [&](long long item, uint4& k, uint4& v) {
+    const int r = (int)(item / passes);
+    const int h = (int)(item % passes) * HPP + g;
+    if (item < items && h < Hkv) {
+      const size_t src = ((size_t)r * Hkv + h) * D + sub * 8;
+      k = *reinterpret_cast<const uint4*>(p.k_new + src);
+      v = *reinterpret_cast<const uint4*>(p.v_new + src);
+    }
+  };
+  uint4 kin = make_uint4(0, 0, 0, 0), vin = make_uint4(0, 0, 0, 0);
+  load_rows(it, kin, vin);
+  const long long total = build_row_starts(p, s_start, s_base, s_wsum);
+  int derr = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && total != T) derr |= VAP_DERR_TOTAL_Q;
+
+  for (bool first = true; it < items; it += stride, first = false) {
+    if (!first) load_rows(it, kin, vin);
     const int r = wave_uniform((int)(it / passes));
     const int h = (int)(it % passes) * HPP + g;
     if (r >= s_start[B]) continue;       // the lengths cover fewer rows than total_q
@@ -143,22 +171,25 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(KVAppendParam
       if (s_start[mid] <= r) lo = mid; else hi = mid;
     }
     const int s = wave_uniform(lo);
-    const int i = r - s_start[s];
-    const int L = p.ctx_lens[s], Q = p.q_lens[s];
-    if (Q < 1 || Q > L || (L - 1) / BS + 1 > p.MB) {
+    int base;
+    if (staged) {
+      base = s_base[s];
+    } else {
+      const int L = p.ctx_lens[s], Q = p.q_lens[s];
+      base = (Q >= 1 && Q <= L && (L - 1) / BS + 1 <= p.MB) ? L - Q : -1;
+    }
+    base = wave_uniform(base);
+    if (base < 0) {
       derr |= VAP_DERR_LENS;
       continue;
     }
-    const int pos = L - Q + i;
+    const int pos = base + r - s_start[s];
     const int blk = p.tables[(size_t)s * p.MB + pos / BS];
     if (blk < 0 || blk >= p.NB) {
       derr |= VAP_DERR_BLOCK_ID;
       continue;
     }
     if (h >= Hkv) continue;
-    const size_t src = ((size_t)r * Hkv + h) * D + sub * 8;
-    const uint4 kin = *reinterpret_cast<const uint4*>(p.k_new + src);
-    const uint4 vin = *reinterpret_cast<const uint4*>(p.v_new + src);
     const int row = pos % BS;
     const size_t dst = (((size_t)blk * BS + row) * Hkv + h) * D + sub * 8;
     if constexpr (!U8) {
@@ -190,7 +221,9 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(KVCommitParam
   const int s = blockIdx.x, tid = threadIdx.x;
   const int BS = p.BS;
   if (tid < 64) {
-    // wave 0 reads the sequence's lengths and path and decides everything
+    // wave 0 reads the sequence's lengths and path (in one round of loads) and decides everything
+    const int32_t* path = p.path != nullptr ? p.path + (size_t)s * p.path_stride : nullptr;
+    const int a = (path != nullptr && tid < min(p.path_stride, 64)) ? path[tid] : 0;
     const int L = p.ctx_lens[s], Q = p.q_lens[s], n = p.n_accepted[s];
     int derr = 0;
     bool ok = Q >= 1 && Q <= L && (L - 1) / BS + 1 <= p.MB && n >= 0 && n <= Q - 1;
@@ -201,11 +234,9 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(KVCommitParam
     }
     bool mv = false;
     int src = 0, dst = 0;
-    if (ok && p.path != nullptr && tid < n) {
-      const int32_t* path = p.path + (size_t)s * p.path_stride;
-      const int a = path[tid];
-      const int prev = tid ? path[tid - 1] : 0;
-      if (a <= prev || a > Q - 1) {
+    const int prev = __shfl_up(a, 1);
+    if (ok && path != nullptr && tid < n) {
+      if (a <= (tid ? prev : 0) || a > Q - 1) {
         derr |= VAP_DERR_TREE;
       } else if (a != tid + 1) {
         const int ps = L - Q + a, pd = L - Q + tid + 1;
@@ -262,24 +293,25 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(KVCommitParam
 
 }  // namespace
 
-size_t kv_append_lds_bytes(int B) { return (size_t)(B + 1) * sizeof(int32_t); }
+size_t kv_append_lds_bytes(int B) { return (size_t)(B + 1 + (B <= kAppendStagedSeqs ? B : 0)) * sizeof(int32_t); }
 
-hipError_t launch_kv_append(const KVAppendParams& p, int D, bool u8, int num_wg, hipStream_t stream) {
-  const size_t lds = kv_append_lds_bytes(p.B);
+hipError_t launch_kv_append(const KVAppendParams& p, int D, bool u8, int num_wg, hipStream_t stream, KTimer t) {
+  const uint32_t lds = (uint32_t)kv_append_lds_bytes(p.B);
   const dim3 grid((unsigned)num_wg), block(kAppendThreads);
   if (D == 128) {
-    if (u8) hipLaunchKernelGGL((kv_append_kernel<128, true>), grid, block, lds, stream, p);
-    else hipLaunchKernelGGL((kv_append_kernel<128, false>), grid, block, lds, stream, p);
+    if (u8) hipExtLaunchKernelGGL((kv_append_kernel<128, true>), grid, block, lds, stream, t.start, t.stop, 0, p);
+    else hipExtLaunchKernelGGL((kv_append_kernel<128, false>), grid, block, lds, stream, t.start, t.stop, 0, p);
   } else {
-    if (u8) hipLaunchKernelGGL((kv_append_kernel<64, true>), grid, block, lds, stream, p);
-    else hipLaunchKernelGGL((kv_append_kernel<64, false>), grid, block, lds, stream, p);
+    if (u8) hipExtLaunchKernelGGL((kv_append_kernel<64, true>), grid, block, lds, stream, t.start, t.stop, 0, p);
+    else hipExtLaunchKernelGGL((kv_append_kernel<64, false>), grid, block, lds, stream, t.start, t.stop, 0, p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_kv_commit(const KVCommitParams& p, bool u8, hipStream_t stream) {
-  if (u8) hipLaunchKernelGGL((kv_commit_kernel<true>), dim3((unsigned)p.B), dim3(kCommitThreads), 0, stream, p);
-  else hipLaunchKernelGGL((kv_commit_kernel<false>), dim3((unsigned)p.B), dim3(kCommitThreads), 0, stream, p);
+hipError_t launch_kv_commit(const KVCommitParams& p, bool u8, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)p.B), block(kCommitThreads);
+  if (u8) hipExtLaunchKernelGGL((kv_commit_kernel<true>), grid, block, 0, stream, t.start, t.stop, 0, p);
+  else hipExtLaunchKernelGGL((kv_commit_kernel<false>), grid, block, 0, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 

@@ -361,12 +361,12 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
 
 }  // namespace
 
-hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream) {
+hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
   const dim3 grid((unsigned)((long long)p.C * p.B));
   if (vec4) {
-    hipLaunchKernelGGL(spec_verify_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL(spec_verify_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   } else {
-    hipLaunchKernelGGL(spec_verify_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL(spec_verify_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   }
   return hipGetLastError();
 }

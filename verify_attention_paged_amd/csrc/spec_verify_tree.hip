@@ -319,8 +319,8 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
 
 }  // namespace
 
-hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(tree_verify_kernel, dim3((unsigned)p.B), dim3(kThreads), 0, stream, p);
+hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream, KTimer t) {
+  hipExtLaunchKernelGGL(tree_verify_kernel, dim3((unsigned)p.B), dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP sources of the library (not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,14 @@
 #include "vap.h"
 
 namespace vap {
+
+// Timing events of one launch (both null when the kernel timer is off).  The launchers pass them
+// to hipExtLaunchKernelGGL, which stamps the kernel's own start and end, so the interval excludes
+// the wait between the previous kernel's end and this kernel's first wave.
+struct KTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
 
 constexpr int kMaxSeqs = 8192;      // plan kernel keeps per-sequence work offsets in LDS
 constexpr int kPlanThreads = 1024;
@@ -128,11 +137,12 @@ struct VerifyParams {
 
 // launchers (defined in the .hip files); return hipError_t of the launch
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream);
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream,
+                            KTimer t = {});
 hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);
-hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream);
+hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
@@ -156,7 +166,7 @@ struct TreeVerifyParams {
   int32_t* err;
 };
 
-hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream);
+hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream, KTimer t = {});
 
 // ---- KV append / commit ----------------------------------------------------------------------
 
@@ -187,7 +197,7 @@ struct KVCommitParams {
 };
 
 size_t kv_append_lds_bytes(int B);
-hipError_t launch_kv_append(const KVAppendParams& p, int D, bool u8, int num_wg, hipStream_t stream);
-hipError_t launch_kv_commit(const KVCommitParams& p, bool u8, hipStream_t stream);
+hipError_t launch_kv_append(const KVAppendParams& p, int D, bool u8, int num_wg, hipStream_t stream, KTimer t = {});
+hipError_t launch_kv_commit(const KVCommitParams& p, bool u8, hipStream_t stream, KTimer t = {});
 
 }  // namespace vap
