@@ -20,6 +20,8 @@ Modules:
   attention    -- paged KV address translation and causal softmax attention (fp64)
   spec_verify  -- sequential modified rejection sampling with residual resampling (fp64)
   tree_verify  -- the same rule walked over a draft token tree (fp64)
+  logits_verify -- verification from logits: temperature, softmax (fp64), then spec_verify;
+                  temperature 0 is the greedy (one-hot) limit
   kv_cache     -- writing new K/V rows into the paged pool (bf16 copy, 8-bit per-token
                   quantisation in fp32) and committing accepted draft tokens
 
@@ -27,4 +29,4 @@ Every function is pinned by ``tests/test_oracle_*.py`` against closed forms, inv
 pages fix, library routines and hand-worked fixtures under ``tests/golden/``.
 """
 
-from . import attention, kv_cache, spec_verify, tree_verify  # noqa: F401
+from . import attention, kv_cache, logits_verify, spec_verify, tree_verify  # noqa: F401

@@ -13,6 +13,8 @@ from oracle import spec_verify as S
 import tests.test_oracle_attention as TA
 import tests.test_oracle_kv8 as TK
 import tests.test_oracle_kv_cache as TC
+import tests.test_oracle_logits_verify as TL
+from oracle import logits_verify as LV
 from oracle import kv_cache as KC
 import tests.test_oracle_spec_verify as TS
 import tests.test_oracle_tree as TT
@@ -290,6 +292,59 @@ KV_CACHE_MUTANTS = {
 }
 
 
+LOGITS_PINS = [
+    lambda: TL.test_golden_worked_cases(GOLDEN),
+    lambda: TL.test_tempered_softmax_is_scipy(0.37),
+    lambda: TL.test_positive_temperature_is_the_probability_verifier(0),
+    TL.test_shift_and_scale_invariance,
+    TL.test_zero_temperature_is_exact_matching,
+    TL.test_small_temperature_approaches_greedy,
+    TL.test_lossless_first_token_at_temperature,
+]
+
+
+def _softmax_variant(use_T="divide", shift=True, axis=-1):
+    def tempered_softmax(z, T):
+        z = np.asarray(z, dtype=np.float64)
+        y = {"divide": z / float(T), "multiply": z * float(T), "ignore": z}[use_T]
+        if shift:
+            y = y - y.max(axis=axis, keepdims=True)
+        with np.errstate(over="ignore", invalid="ignore"):
+            e = np.exp(y)
+            return e / e.sum(axis=axis, keepdims=True)
+    return tempered_softmax
+
+
+def _greedy_variant(last=False):
+    def greedy_rows(z):
+        z = np.asarray(z)
+        out = np.zeros(z.shape, dtype=np.float64)
+        idx = z.shape[-1] - 1 - np.argmax(z[..., ::-1], axis=-1) if last else np.argmax(z, axis=-1)
+        np.put_along_axis(out, idx[..., None], 1.0, axis=-1)
+        return out
+    return greedy_rows
+
+
+def _distributions_variant(draft_tempered=True, zero_as_one=False):
+    def distributions(zp, zq, T):
+        if T == 0.0:
+            if zero_as_one:
+                return LV.tempered_softmax(zp, 1.0), LV.tempered_softmax(zq, 1.0)
+            return LV.greedy_rows(zp), LV.greedy_rows(zq)
+        return LV.tempered_softmax(zp, T), LV.tempered_softmax(zq, T if draft_tempered else 1.0)
+    return distributions
+
+
+LOGITS_MUTANTS = {
+    "temperature ignored": ("tempered_softmax", _softmax_variant(use_T="ignore")),
+    "temperature multiplies the logits": ("tempered_softmax", _softmax_variant(use_T="multiply")),
+    "no max shift before exp": ("tempered_softmax", _softmax_variant(shift=False)),
+    "softmax over the draft positions": ("tempered_softmax", _softmax_variant(axis=0)),
+    "greedy ties to the largest id": ("greedy_rows", _greedy_variant(last=True)),
+    "draft rows not tempered": ("distributions", _distributions_variant(draft_tempered=False)),
+    "temperature 0 sampled as temperature 1": ("distributions", _distributions_variant(zero_as_one=True)),
+}
+
 def _any_pin_fails(pins):
     for pin in pins:
         try:
@@ -406,6 +461,13 @@ def test_kv_cache_mutant_is_caught(name, monkeypatch):
     assert _any_pin_fails(KV_CACHE_PINS), f"no KV-cache pin caught: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(LOGITS_MUTANTS))
+def test_logits_verify_mutant_is_caught(name, monkeypatch):
+    attr, fn = LOGITS_MUTANTS[name]
+    monkeypatch.setattr(LV, attr, fn)
+    assert _any_pin_fails(LOGITS_PINS), f"no logits-verification pin caught: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(SPEC_MUTANTS))
 def test_spec_verify_mutant_is_caught(name, monkeypatch):
     attr, fn = SPEC_MUTANTS[name]
@@ -429,3 +491,7 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     monkeypatch.setattr(KC, "_new_slots", _new_slots_variant())
     monkeypatch.setattr(KC, "kv_commit_tree", _commit_variant())
     assert not _any_pin_fails(KV_CACHE_PINS)
+    monkeypatch.setattr(LV, "tempered_softmax", _softmax_variant())
+    monkeypatch.setattr(LV, "greedy_rows", _greedy_variant())
+    monkeypatch.setattr(LV, "distributions", _distributions_variant())
+    assert not _any_pin_fails(LOGITS_PINS)

@@ -29,4 +29,7 @@ from .generate import (  # noqa: F401
     make_tree_verify_from_probs,
     tree_verify_config,
     new_kv_rows,
+    LogitsVerifyInputs,
+    make_logits_verify_inputs,
+    logits_verify_config,
 )

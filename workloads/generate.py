@@ -455,6 +455,95 @@ def verify_config(name: str, seed: int | None = None, batch: int | None = None) 
 
 
 # ----------------------------------------------------------------------------------------
+# verification from logits
+# ----------------------------------------------------------------------------------------
+
+@dataclass
+class LogitsVerifyInputs:
+    """One batch for verification from logits (CPU tensors).
+
+    zp         fp32  [B, k+1, V]   target logits for the k drafts plus the bonus row
+    zq         fp32  [B, k, V]     draft logits
+    temps      fp32  [B]           sampling temperature per sequence (0 = greedy)
+    draft_ids  int32 [B, k]        x_i ~ softmax(zq_i / T) (the first argmax when T = 0)
+    uniforms   fp32  [B, k+1]
+    """
+
+    name: str
+    seed: int
+    zp: torch.Tensor
+    zq: torch.Tensor
+    temps: torch.Tensor
+    draft_ids: torch.Tensor
+    uniforms: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.zp.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.zq.shape[1])
+
+    @property
+    def vocab(self) -> int:
+        return int(self.zp.shape[2])
+
+
+def make_logits_verify_inputs(seed: int, zp: np.ndarray, zq: np.ndarray, temps,
+                              rng: np.random.Generator | None = None, name: str = "custom") -> LogitsVerifyInputs:
+    """fp32 logits as given; drafts drawn from the tempered draft rows (input recipe only: the
+    draft model's own sampling); open-interval uniforms."""
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    zp32 = np.ascontiguousarray(zp, dtype=np.float32)
+    zq32 = np.ascontiguousarray(zq, dtype=np.float32)
+    B, k1, V = zp32.shape
+    k = k1 - 1
+    temps = np.asarray(temps, dtype=np.float32).reshape(B)
+    drafts = np.zeros((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            if temps[b] == 0:
+                drafts[b, i] = int(np.argmax(zq32[b, i]))
+            else:
+                w = _softmax_rows_f64(zq32[b, i].astype(np.float64) / float(temps[b]))
+                drafts[b, i] = rng.choice(V, p=w / w.sum())
+    u = open_uniforms(rng, (B, k + 1))
+    return LogitsVerifyInputs(name=name, seed=seed, zp=torch.from_numpy(zp32), zq=torch.from_numpy(zq32),
+                              temps=torch.from_numpy(temps), draft_ids=torch.from_numpy(drafts),
+                              uniforms=torch.from_numpy(u))
+
+
+def logits_verify_config(name: str, seed: int | None = None, batch: int | None = None,
+                         temps=None) -> LogitsVerifyInputs:
+    """Named verification-from-logits workloads.
+
+    tiny              B 4, k 4, V 1000; logits as verify_config("tiny"); temperatures cycle
+                      through 1.0, 0.7, 0 (greedy), 1.3
+    spec_verify_step  B 16, k 4, V 128256; logits as verify_config("spec_verify_step");
+                      temperature 1 for every sequence
+    ``batch`` overrides B, ``temps`` the temperatures.
+    """
+    if seed is None:
+        seed = DEFAULT_SEEDS[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if name == "tiny":
+        B, k, V = batch or 4, 4, 1000
+        pl = 2.0 * rng.standard_normal((B, k + 1, V))
+        ql = 2.0 * rng.standard_normal((B, k, V))
+        default = np.resize(np.array([1.0, 0.7, 0.0, 1.3]), B)
+    elif name == "spec_verify_step":
+        B, k, V = batch or 16, 4, 128256
+        pl = 3.0 * rng.standard_normal((B, k + 1, V))
+        ql = pl[:, :k] + 0.7 * rng.standard_normal((B, k, V))
+        default = np.ones(B)
+    else:
+        raise KeyError(name)
+    return make_logits_verify_inputs(seed, pl, ql, default if temps is None else temps, rng=rng, name=name)
+
+
+# ----------------------------------------------------------------------------------------
 # tree verification inputs
 # ----------------------------------------------------------------------------------------
 
