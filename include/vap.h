@@ -71,6 +71,7 @@ extern "C" {
 #define VAP_DERR_TREE 0x20      /* tree mask without the row's own bit or with bits past it, or
                                    a tree of more than 64 rows (the row is then repaired: own
                                    bit set, later bits cleared; or kept causal)              */
+#define VAP_DERR_TEMP 0x40      /* temperature negative or not finite (the sequence is greedy)  */
 
 /*
  * Shape of one attention step.
@@ -193,6 +194,38 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
                 int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes spec_verify_logits needs (0 on bad sizes). */
+size_t vap_verify_logits_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);
+
+/*
+ * spec_verify_logits -- spec_verify from logits: temperature, softmax and the verification in
+ * one pass over the logits, without writing probability rows (tempatgunting.com article,
+ * section "Speculative Decoding: Turning Verification Parallelism into Latency Wins": the
+ * verify pass returns logits [k+1][vocab] and tokens are sampled from logits).
+ *
+ *   target_logits  fp32 [B][k+1][V]   logits at the k draft positions and the bonus position
+ *   draft_logits   fp32 [B][k][V]     the draft model's logits (may be NULL when k == 0)
+ *   temperatures   fp32 [B]           sampling temperature T per sequence
+ *   draft_ids, uniforms, out_ids, n_accepted, B, k, V  as for spec_verify (V <= 2^20)
+ *
+ * With T > 0: p_i = softmax(target_logits_i / T) and q_i = softmax(draft_logits_i / T), and
+ * spec_verify's rule runs on them.  Every probability the rule needs is evaluated in fp64 as
+ * 2^((z - max z) log2(e) / T) / S, S being the row's fp64 sum of those terms.  With T = 0
+ * (greedy, exact token matching: tempatgunting.com article, section "Frequently Asked
+ * Questions"): draft x_i is accepted while it is the first argmax of target row i; the
+ * emitted token is the first argmax of target row n; draft logits are not read.  A negative
+ * or non-finite T sets VAP_DERR_TEMP and the sequence is treated as greedy.  Logits must be
+ * finite or -inf, with at least one finite entry per row.
+ *
+ * Two kernels on `stream`: row statistics (max, argmax, sum of exponentials) of all rows,
+ * then the verification.  The workspace (vap_verify_logits_workspace_bytes) serves
+ * spec_verify_logits calls only; pass the same workspace_bytes on every call.
+ */
+int spec_verify_logits(const float* target_logits, const float* draft_logits, const int32_t* draft_ids,
+                       const float* uniforms, const float* temperatures, int32_t* out_ids, int32_t* n_accepted,
+                       int32_t num_seqs, int32_t k, int32_t vocab, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Zero-fill `bytes` of a workspace on `stream` (a fill kernel, no memset node). */
 int vap_workspace_init(void* workspace, size_t bytes, void* stream);
 
@@ -302,8 +335,9 @@ int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int
 /* ---- measurement helpers (not part of the step) ------------------------------------------ */
 
 /* Kernel timer.  While enabled, every paged_attn_step times its attention kernel (kind 0),
- * every spec_verify its kernel (kind 1), and spec_verify_tree (kind 2), kv_append (kind 3) and
- * kv_commit (kind 4) theirs, into a ring of 4096 event pairs per kind.  The events are stamped
+ * every spec_verify its kernel (kind 1), and spec_verify_tree (kind 2), kv_append (kind 3),
+ * kv_commit (kind 4) theirs; spec_verify_logits its statistics kernel (kind 5) and its
+ * verification kernel (kind 6); into a ring of 4096 event pairs per kind.  The events are stamped
  * by the kernel launch itself (hipExtLaunchKernelGGL), so each pair spans the kernel's execution
  * without the wait before its first wave.  vap_timer_read synchronises on the recorded
  * events, returns the summed milliseconds and the number of pairs, and resets the ring when

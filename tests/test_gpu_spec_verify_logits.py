@@ -1,0 +1,163 @@
+"""GPU parity of spec_verify_logits against the fp64 oracle (through the C ABI).
+
+Bar: emitted ids and accepted counts bit-exact, with uniforms placed at least 1e-6 from every
+threshold the oracle evaluates (oracle.logits_verify.uniforms_with_margin).  The kernel takes
+its exponentials in fp64 (relative error near 1e-15), far inside that margin.  A Monte Carlo
+test with raw uniforms checks the emitted distribution directly.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+from scipy.special import softmax as sp_softmax
+
+import verify_attention_paged_amd as vap
+import workloads
+from oracle import logits_verify as OL
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _t(x, dt):
+    return torch.as_tensor(np.ascontiguousarray(x, dtype=dt), device=DEV)
+
+
+def _gpu(zp, zq, ids, u, temps, workspace=None):
+    k = zp.shape[1] - 1
+    out, n = vap.spec_verify_logits(_t(zp, np.float32), _t(zq, np.float32) if k else None,
+                                    _t(ids, np.int32) if k else None, _t(u, np.float32), _t(temps, np.float32),
+                                    workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), n.cpu().numpy()
+
+
+def _compare(zp, zq, ids, u, temps, what, workspace=None):
+    ref = OL.verify_logits(zp, zq, ids, u, temps)
+    got = _gpu(zp, zq, ids, u, temps, workspace)
+    assert np.array_equal(got[1], ref[1]), f"{what}: n_accepted {got[1]} vs {ref[1]}"
+    assert np.array_equal(got[0], ref[0]), f"{what}: ids\n{got[0]}\n{ref[0]}"
+    return ref
+
+
+def _margin(inp, seed):
+    zp, zq, ids, T = inp.zp.numpy(), inp.zq.numpy(), inp.draft_ids.numpy(), inp.temps.numpy()
+    u = OL.uniforms_with_margin(zp, zq, ids, inp.uniforms.numpy(), T, np.random.default_rng(seed))
+    return zp, zq, ids, u, T
+
+
+def test_tiny_mixed_temperatures_bit_exact():
+    _compare(*_margin(workloads.logits_verify_config("tiny"), 1), "tiny")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tiny_many_seeds_and_temperatures(seed):
+    rng = np.random.default_rng(seed)
+    temps = rng.choice([0.0, 0.3, 0.7, 1.0, 1.6, 3.0], size=24)
+    inp = workloads.logits_verify_config("tiny", seed=4000 + seed, batch=24, temps=temps)
+    _compare(*_margin(inp, seed), f"tiny seed {seed}")
+
+
+def test_full_vocab_temperature_one_bit_exact():
+    ref = _compare(*_margin(workloads.logits_verify_config("spec_verify_step"), 2), "spec_verify_step")
+    print("accepted per sequence", ref[1].tolist(), flush=True)
+
+
+def test_full_vocab_mixed_temperatures():
+    temps = np.array([0.0, 0.5, 1.0, 1.7] * 4)
+    inp = workloads.logits_verify_config("spec_verify_step", seed=77, temps=temps)
+    _compare(*_margin(inp, 3), "spec_verify_step, mixed temperatures")
+
+
+def test_golden_cases_on_gpu():
+    with open(os.path.join(GOLDEN, "logits_verify_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        out, n = _gpu(np.array(c["zp"], np.float32)[None], np.array(c["zq"], np.float32)[None],
+                      np.array(c["drafts"])[None], np.array(c["uniforms"], np.float32)[None],
+                      np.array([c["T"]], np.float32))
+        assert out[0].tolist() == c["out_ids"], c["name"]
+        assert n[0] == c["n_accepted"], c["name"]
+
+
+@pytest.mark.parametrize("V,k", [(3001, 4), (1, 2), (2, 1), (4097, 0), (5000, 8), (8192, 16)])
+def test_shapes_scalar_path_and_k(V, k):
+    rng = np.random.default_rng(V + k)
+    B = 5
+    zp = (2.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zq = (zp[:, :k] + 0.5 * rng.standard_normal((B, k, V))).astype(np.float32)
+    temps = np.array([1.0, 0.6, 0.0, 2.0, 1.0])
+    inp = workloads.make_logits_verify_inputs(V * 7 + k, zp, zq, temps)
+    _compare(*_margin(inp, 5), f"V {V} k {k}")
+
+
+def test_large_and_masked_logits():
+    rng = np.random.default_rng(12)
+    B, k, V = 6, 4, 2048
+    zp = (3.0 * rng.standard_normal((B, k + 1, V)) + 1e4).astype(np.float32)
+    zq = (zp[:, :k] - 2e4 + rng.standard_normal((B, k, V))).astype(np.float32)
+    zp[:, :, ::7] = -np.inf                         # masked tokens
+    zq[:, :, 3::11] = -np.inf
+    temps = np.array([1.0, 0.5, 0.0, 1.3, 1.0, 0.9])
+    inp = workloads.make_logits_verify_inputs(99, zp, zq, temps)
+    _compare(*_margin(inp, 6), "large / masked logits")
+
+
+def test_invalid_temperature_is_greedy_and_flagged():
+    inp = workloads.logits_verify_config("tiny", seed=8, batch=4, temps=[1.0, 0.0, 1.0, 1.0])
+    zp, zq, ids, u, T = _margin(inp, 7)
+    bad = T.copy()
+    bad[2], bad[3] = -1.0, np.nan
+    ws = vap.verify_logits_workspace(4, inp.k, inp.vocab, DEV)
+    out, n = _gpu(zp, zq, ids, u, bad, workspace=ws)
+    assert vap.get_device_error(ws, clear=True) & vap.DERR_TEMP
+    greedy = T.copy()
+    greedy[2] = greedy[3] = 0.0
+    ref = OL.verify_logits(zp, zq, ids, u, greedy)
+    assert np.array_equal(out, ref[0]) and np.array_equal(n, ref[1])
+
+
+def test_matches_the_probability_path():
+    """T = 1 from logits and spec_verify on the oracle's fp64 softmax stored as fp32."""
+    inp = workloads.logits_verify_config("tiny", seed=31, batch=32, temps=np.ones(32))
+    zp, zq, ids, u, T = _margin(inp, 8)
+    p = sp_softmax(zp.astype(np.float64), axis=-1).astype(np.float32)
+    q = sp_softmax(zq.astype(np.float64), axis=-1).astype(np.float32)
+    out_l, n_l = _gpu(zp, zq, ids, u, T)
+    out_p, n_p = vap.spec_verify(_t(p, np.float32), _t(q, np.float32), _t(ids, np.int32), _t(u, np.float32))
+    assert np.array_equal(n_l, n_p.cpu().numpy()) and np.array_equal(out_l, out_p.cpu().numpy())
+
+
+def test_workspace_reuse_across_shapes():
+    shapes = [(16, 4, 128256), (1, 0, 7), (64, 2, 1000), (3, 12, 4099), (16, 4, 128256)]
+    size = max(vap.load_library().vap_verify_logits_workspace_bytes(B, k, V) for B, k, V in shapes)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    for i, (B, k, V) in enumerate(shapes):
+        rng = np.random.default_rng(100 + i)
+        zp = (2.5 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+        zq = (zp[:, :k] + 0.6 * rng.standard_normal((B, k, V))).astype(np.float32)
+        temps = rng.choice([0.0, 0.8, 1.0], size=B)
+        inp = workloads.make_logits_verify_inputs(200 + i, zp, zq, temps)
+        _compare(*_margin(inp, 9 + i), f"call {i} {(B, k, V)}", workspace=ws)
+
+
+def test_monte_carlo_first_token_at_temperature():
+    """4096 copies of one sequence with drafts drawn from softmax(z_q / T) and raw uniforms:
+    the first emitted token follows softmax(z_p / T) (chi-square at the 0.999 quantile)."""
+    rng = np.random.default_rng(123)
+    V, k, B, T = 8, 3, 1 << 12, 0.8
+    zp1 = (1.5 * rng.standard_normal((k + 1, V))).astype(np.float32)
+    zq1 = (1.5 * rng.standard_normal((k, V))).astype(np.float32)
+    qd = sp_softmax(zq1.astype(np.float64) / T, axis=-1)
+    ids = np.stack([np.array([rng.choice(V, p=qd[i]) for i in range(k)]) for _ in range(B)])
+    u = workloads.open_uniforms(rng, (B, k + 1))
+    out, n = _gpu(np.broadcast_to(zp1, (B, k + 1, V)), np.broadcast_to(zq1, (B, k, V)), ids, u, np.full(B, T))
+    counts = np.bincount(out[:, 0], minlength=V)
+    exp = B * sp_softmax(zp1[0].astype(np.float64) / T)
+    chi2 = float(((counts - exp) ** 2 / exp).sum())
+    assert chi2 < stats.chi2.ppf(0.999, V - 1), f"chi2 {chi2}"

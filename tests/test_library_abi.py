@@ -107,6 +107,26 @@ def test_kv_append_and_commit_rejected_on_host(lib):
     assert commit(None, None, None, None, None, None, 0, None, None, ctypes.byref(empty), None, 0, None) == B.VAP_OK
 
 
+def test_verify_logits_rejected_on_host(lib):
+    f = lib.spec_verify_logits
+    assert lib.vap_verify_logits_workspace_bytes(16, 4, 128256) > 0
+    assert lib.vap_verify_logits_workspace_bytes(16, 65, 100) == 0
+    assert lib.vap_verify_logits_workspace_bytes(16, 4, (1 << 20) + 1) == 0
+    assert f(None, None, None, None, None, None, None, 4, 65, 10, None, 0, None) == B.VAP_EINVAL
+    assert f(None, None, None, None, None, None, None, 4, 4, 0, None, 0, None) == B.VAP_EINVAL
+    assert f(None, None, None, None, None, None, None, 4, 4, 10, None, 0, None) == B.VAP_EINVAL
+    fake = ctypes.c_void_p(256)
+    # temperatures missing
+    assert f(fake, fake, fake, fake, None, fake, fake, 4, 4, 10, fake, 1 << 20, None) == B.VAP_EINVAL
+    # workspace too small
+    assert f(fake, fake, fake, fake, fake, fake, fake, 4, 4, 10, fake, 64, None) == B.VAP_ENOSPC
+    assert f(None, None, None, None, None, None, None, 0, 4, 10, None, 0, None) == B.VAP_OK
+    # the layout keeps data and tickets in separate halves
+    n1 = lib.vap_verify_logits_workspace_bytes(1, 4, 1 << 20)
+    n2 = lib.vap_verify_logits_workspace_bytes(1000, 0, 4)
+    assert n1 % 512 == 0 and n2 % 512 == 0
+
+
 def test_workspace_sizes_are_consistent(lib):
     s = _shape(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, num_blocks=6000,
                max_blocks_per_seq=512, total_q=64)

@@ -7,6 +7,7 @@ memory and streams only.
     paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale=0.0)
     spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None)
     spec_verify_tree(p, q, parents, tokens, uniforms)
+    spec_verify_logits(target_logits, draft_logits, draft_ids, uniforms, temperatures)
     kv_append(k_new, v_new, kv_pool, block_tables, ctx_lens, q_lens)
     kv_commit(kv_pool, block_tables, ctx_lens, q_lens, n_accepted, path=None)
     (paged_attn_step also takes kv_scales= for an 8-bit cache and tree_mask= for token trees)
@@ -22,11 +23,14 @@ from ._binding import (  # noqa: F401
     DERR_DRAFT_ID,
     DERR_EMPTY_ROW,
     DERR_TREE,
+    DERR_TEMP,
     TIMER_ATTENTION,
     TIMER_VERIFY,
     TIMER_TREE_VERIFY,
     TIMER_KV_APPEND,
     TIMER_KV_COMMIT,
+    TIMER_LOGIT_STATS,
+    TIMER_VERIFY_LOGITS,
     attn_shape,
     attn_workspace,
     device_info,
@@ -39,6 +43,8 @@ from ._binding import (  # noqa: F401
     paged_attn_step,
     spec_verify,
     spec_verify_tree,
+    spec_verify_logits,
+    verify_logits_workspace,
     tree_verify_workspace,
     stream_copy,
     stream_read,

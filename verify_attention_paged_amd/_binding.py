@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libv
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vap.h")
 
 VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
-DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
+DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE, DERR_TEMP = (
+    0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40)
 TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY, TIMER_KV_APPEND, TIMER_KV_COMMIT = 0, 1, 2, 3, 4
+TIMER_LOGIT_STATS, TIMER_VERIFY_LOGITS = 5, 6
 
 
 class VapError(RuntimeError):
@@ -53,6 +55,8 @@ SIGNATURES = {
     "paged_attn_step_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "vap_verify_logits_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "spec_verify_logits": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_tree_verify_workspace_bytes": (_sz, []),
     "spec_verify_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_kv_workspace_bytes": (_sz, []),
@@ -251,6 +255,54 @@ def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
         rc = lib.spec_verify(p.data_ptr(), qp, ip, uniforms.data_ptr(), out_ids.data_ptr(),
                              n_accepted.data_ptr(), B, k, V, workspace.data_ptr(),
                              workspace.numel(), _stream(stream))
+    _check(rc)
+    return out_ids, n_accepted
+
+
+def verify_logits_workspace(num_seqs: int, k: int, vocab: int, device=None) -> torch.Tensor:
+    lib = load_library()
+    n = lib.vap_verify_logits_workspace_bytes(num_seqs, k, vocab)
+    if n == 0:
+        _check(VAP_EINVAL)
+    return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
+
+
+def spec_verify_logits(target_logits, draft_logits, draft_ids, uniforms, temperatures, out_ids=None,
+                       n_accepted=None, *, workspace: torch.Tensor | None = None, stream=None):
+    """Verification from logits; see ``spec_verify_logits`` in include/vap.h.
+
+    target_logits fp32 [B, k+1, V]; draft_logits fp32 [B, k, V]; draft_ids int32 [B, k];
+    uniforms fp32 [B, k+1]; temperatures fp32 [B] (0 = greedy).
+    Returns (out_ids int32 [B, k+1], n_accepted int32 [B]).
+    """
+    lib = load_library()
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, 3)
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _need(uniforms, "uniforms", torch.float32, 2, dev)
+    _need(temperatures, "temperatures", torch.float32, 1, dev)
+    if tuple(uniforms.shape) != (B, k + 1) or temperatures.numel() != B:
+        raise ValueError("uniforms must be [B, k+1] and temperatures [B]")
+    if k > 0:
+        _need(draft_logits, "draft_logits", torch.float32, 3, dev)
+        _need(draft_ids, "draft_ids", torch.int32, 2, dev)
+        if tuple(draft_logits.shape) != (B, k, V) or tuple(draft_ids.shape) != (B, k):
+            raise ValueError("draft_logits must be [B, k, V] and draft_ids [B, k]")
+    if out_ids is None:
+        out_ids = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_ids, "out_ids", torch.int32, 2, dev)
+    _need(n_accepted, "n_accepted", torch.int32, 1, dev)
+    if workspace is None:
+        workspace = verify_logits_workspace(B, k, V, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_logits(target_logits.data_ptr(), draft_logits.data_ptr() if k > 0 else None,
+                                    draft_ids.data_ptr() if k > 0 else None, uniforms.data_ptr(),
+                                    temperatures.data_ptr(), out_ids.data_ptr(), n_accepted.data_ptr(), B, k, V,
+                                    workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(rc)
     return out_ids, n_accepted
 

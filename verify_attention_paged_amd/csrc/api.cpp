@@ -78,7 +78,8 @@ const DevInfo* device_info() {
 // ---- kernel timer ------------------------------------------------------------------------
 
 constexpr int kTimerSlots = 4096;
-constexpr int kTimerKinds = 5;   // attention, spec_verify, spec_verify_tree, kv_append, kv_commit
+constexpr int kTimerKinds = 7;   // attention, spec_verify, spec_verify_tree, kv_append, kv_commit,
+                                  // logit statistics, verification from logits
 struct Timer {
   bool on = false;
   bool created = false;
@@ -399,6 +400,89 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
   hipError_t e = launch_spec_verify(P, vec4, stream, t);
   timer_commit(1, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t vap_verify_logits_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs || k < 0 || k > 64 || vocab < 1 || vocab > kMaxChunks * 4096) return 0;
+  return logits_layout(num_seqs, k, vocab).total;
+}
+
+int spec_verify_logits(const float* target_logits, const float* draft_logits, const int32_t* draft_ids,
+                       const float* uniforms, const float* temperatures, int32_t* out_ids, int32_t* n_accepted,
+                       int32_t num_seqs, int32_t k, int32_t vocab, void* workspace, size_t workspace_bytes,
+                       void* stream_) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs)
+    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
+  if (k < 0 || k > 64) return fail(VAP_EINVAL, "k=%d outside [0, 64]", k);
+  if (vocab < 1 || vocab > kMaxChunks * 4096) return fail(VAP_EINVAL, "vocab=%d outside [1, %d]", vocab, kMaxChunks * 4096);
+  if (num_seqs == 0) return ok();
+  if (!target_logits || !uniforms || !temperatures || !out_ids || !n_accepted || !workspace ||
+      (k > 0 && (!draft_logits || !draft_ids)))
+    return fail(VAP_EINVAL, "NULL data pointer");
+  const LogitsLayout lay = logits_layout(num_seqs, k, vocab);
+  if (workspace_bytes < lay.total)
+    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes, lay.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
+  const long long R = (long long)num_seqs * (2 * k + 1);
+  const long long C1 = ((long long)vocab + kStatChunk - 1) / kStatChunk;
+  if (R * C1 >= (1LL << 31)) return fail(VAP_EINVAL, "too many logit rows");
+  const DevInfo* d = device_info();
+  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
+  const bool vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(target_logits) |
+                                           reinterpret_cast<uintptr_t>(k ? draft_logits : target_logits)) & 15) == 0;
+  LogitStatsParams S;
+  S.zp = target_logits;
+  S.zq = draft_logits;
+  S.temps = temperatures;
+  S.part = reinterpret_cast<LogitRowStat*>(ws + lay.part);
+  S.stats = reinterpret_cast<LogitRowStat*>(ws + lay.stats);
+  S.row_tickets = tickets_end - num_seqs - R;
+  S.B = num_seqs;
+  S.k = k;
+  S.V = vocab;
+  S.C = (int)C1;
+  S.CS = kStatChunk;
+  S.err = reinterpret_cast<int32_t*>(ws);
+
+  // verification chunks: as spec_verify
+  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
+  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
+  C = std::max(1LL, std::min(C, cmax));
+  C = std::max(C, ((long long)vocab + 4095) / 4096);
+  long long CS = ((long long)vocab + C - 1) / C;
+  CS = (CS + 3) / 4 * 4;
+  C = ((long long)vocab + CS - 1) / CS;
+  VerifyParams P;
+  P.p = target_logits;
+  P.q = draft_logits;
+  P.draft_ids = draft_ids;
+  P.uniforms = uniforms;
+  P.out_ids = out_ids;
+  P.n_accepted = n_accepted;
+  P.B = num_seqs;
+  P.k = k;
+  P.V = vocab;
+  P.C = (int)C;
+  P.CS = (int)CS;
+  P.err = reinterpret_cast<int32_t*>(ws);
+  P.tickets_end = tickets_end;
+  P.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk_sums);
+  P.temps = temperatures;
+  P.stats = S.stats;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const KTimer t1 = timer_slot(5);
+  hipError_t e = launch_logit_stats(S, vec4, stream, t1);
+  timer_commit(5, t1, e);
+  if (e != hipSuccess) return fail(VAP_EHIP, "logit statistics launch: %s", hipGetErrorString(e));
+  const KTimer t2 = timer_slot(6);
+  e = launch_spec_verify_logits(P, vec4, stream, t2);
+  timer_commit(6, t2, e);
+  if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify_logits launch: %s", hipGetErrorString(e));
   return ok();
 }
 

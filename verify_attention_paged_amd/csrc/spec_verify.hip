@@ -19,6 +19,21 @@
 // holds t and rescans only that chunk to pick the token.  The counter returns to 0, so the
 // workspace is ready for the next call.  All bytes of the vocabulary are read once, in
 // parallel over about 2 x (number of CUs) workgroups.
+//
+// Verification from logits (tempatgunting.com article, section "Speculative Decoding: Turning
+// Verification Parallelism into Latency Wins": the verify pass yields logits and tokens are
+// sampled from logits): p_i = softmax(z_p,i / T), q_i = softmax(z_q,i / T) for a temperature
+// T > 0, then the same rule; at T = 0 (same page, section "Frequently Asked Questions": exact
+// token matching) a draft passes when it is its target row's first argmax and the emitted token
+// is the argmax of row n.  A statistics kernel first reduces every logit row to (max, first
+// argmax, S = sum 2^((z - max) log2(e) / T)) with one workgroup per (row, 4096-token chunk)
+// and an arrival ticket per row; the verification kernel above then evaluates
+// p(x) = 2^((z_x - max) log2(e) / T) / S wherever it needs a probability, so no probability
+// row is ever written.  The exponentials are taken in fp64 (exp2_f64), which keeps every
+// decision within rounding of the fp64 oracle.
+#include <cfloat>
+#include <type_traits>
+
 #include "vap_internal.h"
 
 namespace vap {
@@ -30,6 +45,45 @@ __device__ __forceinline__ double residual_or_p(float p, float q, bool residual)
   const double d = residual ? (double)p - (double)q : (double)p;
   return residual ? fmax(0.0, d) : d;
 }
+
+// 2^a in fp64 for a <= 0: a = n + f with n = rint(a) and |f| <= 1/2, 2^f = e^y with y = f ln 2
+// (|y| <= 0.347) from the Taylor series of e^y through y^12 (truncation below 2e-16 relative,
+// Horner form), then scaled by 2^n.  Arguments below -1080 (and NaN) give 0.
+__device__ __forceinline__ double exp2_f64(double a) {
+  if (!(a > -1080.0)) return 0.0;
+  const double n = rint(a);
+  const double y = (a - n) * 0.69314718055994530942;
+  double p = 1.0 / 479001600.0;
+  p = fma(p, y, 1.0 / 39916800.0);
+  p = fma(p, y, 1.0 / 3628800.0);
+  p = fma(p, y, 1.0 / 362880.0);
+  p = fma(p, y, 1.0 / 40320.0);
+  p = fma(p, y, 1.0 / 5040.0);
+  p = fma(p, y, 1.0 / 720.0);
+  p = fma(p, y, 1.0 / 120.0);
+  p = fma(p, y, 1.0 / 24.0);
+  p = fma(p, y, 1.0 / 6.0);
+  p = fma(p, y, 0.5);
+  p = fma(p, y, 1.0);
+  p = fma(p, y, 1.0);
+  return ldexp(p, (int)n);
+}
+
+// Weight of a token in the row that is sampled, from the two values loaded for it (the target
+// and draft entries; the draft entry is 0 and unused when !residual).
+struct ProbWeight {
+  bool residual;
+  __device__ __forceinline__ double operator()(float p, float q) const { return residual_or_p(p, q, residual); }
+};
+
+struct LogitWeight {
+  bool residual;
+  double mp, mq, c, inv_sp, inv_sq;   // row maxima, log2(e) / T, reciprocals of the row sums
+  __device__ __forceinline__ double operator()(float zp, float zq) const {
+    const double p = exp2_f64(((double)zp - mp) * c) * inv_sp;
+    return residual ? fmax(0.0, p - exp2_f64(((double)zq - mq) * c) * inv_sq) : p;
+  }
+};
 
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
@@ -103,9 +157,9 @@ __device__ __forceinline__ int block_max(int x, int* s_int) {
 // the chunk read a clamped in-bounds address and are discarded.
 constexpr int kMaxChunkLen = 4096;
 
-template <bool VEC4>
-__device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, bool residual,
-                                                int x0, int x1) {
+template <bool VEC4, class W>
+__device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, const W& w, int x0, int x1) {
+  const bool residual = w.residual;
   double acc = 0.0;
   if (VEC4) {
     constexpr int kIt = kMaxChunkLen / (4 * kThreads);
@@ -119,8 +173,7 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       if (x0 + 4 * ((int)threadIdx.x + i * kThreads) < x1)
-        acc += residual_or_p(pv[i].x, qv[i].x, residual) + residual_or_p(pv[i].y, qv[i].y, residual) +
-               residual_or_p(pv[i].z, qv[i].z, residual) + residual_or_p(pv[i].w, qv[i].w, residual);
+        acc += w(pv[i].x, qv[i].x) + w(pv[i].y, qv[i].y) + w(pv[i].z, qv[i].z) + w(pv[i].w, qv[i].w);
     }
   } else {
     constexpr int kIt = kMaxChunkLen / kThreads;
@@ -133,7 +186,7 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i)
-      if (x0 + (int)threadIdx.x + i * kThreads < x1) acc += residual_or_p(pv[i], qv[i], residual);
+      if (x0 + (int)threadIdx.x + i * kThreads < x1) acc += w(pv[i], qv[i]);
   }
   return acc;
 }
@@ -144,11 +197,12 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
 // are at most kThreads * kSlice long), so the scan never goes back to memory.
 constexpr int kSlice = 16;
 
-template <bool VEC4>
-__device__ __forceinline__ void chunk_select(const float* prow, const float* qrow, bool residual,
+template <bool VEC4, class W>
+__device__ __forceinline__ void chunk_select(const float* prow, const float* qrow, const W& w,
                                              int x0, int x1, double base, double t,
                                              double* s_red, int* s_int, int& first_above,
                                              int& last_positive) {
+  const bool residual = w.residual;
   const int len = x1 - x0;
   const int per = ((len + kThreads - 1) / kThreads + 3) & ~3;   // multiple of 4, <= kSlice
   const int a = x0 + min(len, (int)threadIdx.x * per);
@@ -177,7 +231,7 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
   int lastpos = -1;
 #pragma unroll
   for (int j = 0; j < kSlice; ++j) {
-    const double wx = (a + j < b) ? residual_or_p(pv[j], residual ? qv[j] : 0.f, residual) : 0.0;
+    const double wx = (a + j < b) ? w(pv[j], qv[j]) : 0.0;
     mine += wx;
     if (wx > 0.0) lastpos = a + j;
   }
@@ -187,7 +241,7 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
   int found = INT_MAX;
 #pragma unroll
   for (int j = 0; j < kSlice; ++j) {
-    const double wx = (a + j < b) ? residual_or_p(pv[j], residual ? qv[j] : 0.f, residual) : 0.0;
+    const double wx = (a + j < b) ? w(pv[j], qv[j]) : 0.0;
     run += wx;
     if (found == INT_MAX && a + j < b && run > t) found = a + j;
   }
@@ -195,8 +249,13 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
   last_positive = block_max(lastpos, s_int);
 }
 
-template <bool VEC4>
+// Temperature of sequence b in verification from logits: T > 0 samples; T = 0, and any value
+// that is negative or not finite (reported), is greedy.
+__device__ __forceinline__ bool greedy_temperature(float T) { return !(T > 0.f && T <= FLT_MAX); }
+
+template <bool VEC4, bool LOGITS>
 __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParams P) {
+  using W = std::conditional_t<LOGITS, LogitWeight, ProbWeight>;
   __shared__ int s_n;
   __shared__ int s_last;
   __shared__ int s_ids[64];          // draft ids (accepted ones are copied to the output)
@@ -212,6 +271,15 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int k = P.k, V = P.V;
+  const long long srow = (long long)b * (2 * k + 1);   // first statistics row of sequence b
+  bool greedy = false;
+  double cT = 0.0;
+  if constexpr (LOGITS) {
+    const float T = P.temps[b];
+    greedy = greedy_temperature(T);
+    if (!(T >= 0.f && T <= FLT_MAX) && cidx == 0 && tid == 0) atomicOr(P.err, VAP_DERR_TEMP);
+    cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
+  }
 
   // 1. accept tests (first wave; k <= 64); the second wave fetches u_k meanwhile
   if (tid == 64) s_uk = P.uniforms[(long long)b * (k + 1) + k];
@@ -220,15 +288,27 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     if (lane < k) {
       const int x = P.draft_ids[(long long)b * k + lane];
       const bool inside = x >= 0 && x < V;
-      float pv = 0.f, qv = 0.f;
-      if (inside) {
-        pv = P.p[((long long)b * (k + 1) + lane) * V + x];
-        qv = P.q[((long long)b * k + lane) * V + x];
-      } else if (cidx == 0) {
-        atomicOr(P.err, VAP_DERR_DRAFT_ID);
-      }
+      if (!inside && cidx == 0) atomicOr(P.err, VAP_DERR_DRAFT_ID);
       const double r = (double)P.uniforms[(long long)b * (k + 1) + lane];
-      reject = !(pv > 0.f && r * (double)qv <= (double)pv);
+      if constexpr (!LOGITS) {
+        float pv = 0.f, qv = 0.f;
+        if (inside) {
+          pv = P.p[((long long)b * (k + 1) + lane) * V + x];
+          qv = P.q[((long long)b * k + lane) * V + x];
+        }
+        reject = !(pv > 0.f && r * (double)qv <= (double)pv);
+      } else {
+        if (!inside) {
+          reject = true;
+        } else if (greedy) {
+          reject = x != P.stats[srow + lane].argmax;
+        } else {
+          const LogitRowStat sp = P.stats[srow + lane], sq = P.stats[srow + k + 1 + lane];
+          const double pv = exp2_f64(((double)P.p[((long long)b * (k + 1) + lane) * V + x] - sp.m) * cT) / sp.S;
+          const double qv = exp2_f64(((double)P.q[((long long)b * k + lane) * V + x] - sq.m) * cT) / sq.S;
+          reject = !(pv > 0.0 && r * qv <= pv);
+        }
+      }
       s_ids[lane] = x;
     }
 
@@ -237,14 +317,32 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   }
   __syncthreads();
   const int n = s_n;
+  if constexpr (LOGITS) {
+    if (greedy) {   // exact matching: the emitted token is the argmax of target row n
+      if (cidx == 0) {
+        if (tid <= k)
+          P.out_ids[(long long)b * (k + 1) + tid] = tid < n ? s_ids[tid] : (tid == n ? P.stats[srow + n].argmax : -1);
+        if (tid == 0) P.n_accepted[b] = n;
+      }
+      return;
+    }
+  }
   const bool residual = n < k;
   const float* prow = P.p + ((long long)b * (k + 1) + n) * V;
   const float* qrow = residual ? P.q + ((long long)b * k + n) * V : prow;
+  W w;
+  if constexpr (LOGITS) {
+    const LogitRowStat sp = P.stats[srow + n];
+    const LogitRowStat sq = residual ? P.stats[srow + k + 1 + n] : sp;
+    w = LogitWeight{residual, (double)sp.m, (double)sq.m, cT, 1.0 / sp.S, 1.0 / sq.S};
+  } else {
+    w = ProbWeight{residual};
+  }
 
   // 2-3. this chunk's sum of w
   const int x0 = cidx * P.CS;
   const int x1 = min(V, x0 + P.CS);
-  double part = block_sum(chunk_partial<VEC4>(prow, qrow, residual, x0, x1), s_red);
+  double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
   if (tid == 0) {
     // publish the chunk sum with an agent-coherent (write-through) store, wait until it has
     // completed, then arrive; the L2-wide writeback/invalidate of an agent-scope fence is not
@@ -264,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   // 4. last workgroup of sequence b: locate t among the chunk sums (one wave, each lane holds
   // up to four consecutive chunks; C <= 256), then inside one chunk
   if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bool use_res = residual;
+  W wsel = w;
   const float* srow_q = qrow;
   double Z = 0.0;
   if (tid < 64) {
@@ -318,12 +416,12 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   double base = s_loc[0], t = s_loc[1];
   if (cstar < 0) {
     // empty residual: draw from p_n itself (its chunk sums are computed here)
-    use_res = false;
+    wsel.residual = false;
     srow_q = prow;
     double cs = 0.0;
     for (int j = 0; j < C; ++j) {
       const int a = j * P.CS, e = min(V, a + P.CS);
-      const double sj = block_sum(chunk_partial<VEC4>(prow, prow, false, a, e), s_red);
+      const double sj = block_sum(chunk_partial<VEC4>(prow, prow, wsel, a, e), s_red);
       if (tid == j) cs = sj;
     }
     double before = block_exclusive_scan(cs, s_red, Z);
@@ -344,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if (cstar >= 0) {
     const int a = cstar * P.CS, e = min(V, a + P.CS);
     int first_above, last_positive;
-    chunk_select<VEC4>(prow, srow_q, use_res, a, e, base, t, s_red, s_int, first_above, last_positive);
+    chunk_select<VEC4>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above, last_positive);
     token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
   }
 
@@ -359,14 +457,157 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if (tid == 0) P.n_accepted[b] = n;
 }
 
+// Row statistics of the logits (see LogitRowStat): one workgroup per (row, chunk of kStatChunk
+// tokens), every load issued up front; the chunk's (max, first argmax, sum of exponentials
+// relative to its own max) is published, and the last workgroup of the row merges the chunks
+// in order: M = max m_c, S = sum_c S_c 2^((m_c - M) log2(e) / T).  Draft rows of greedy
+// sequences are skipped.
+__device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi) {
+  if (om > m || (om == m && oi < i)) {
+    m = om;
+    i = oi;
+  }
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsParams P) {
+  __shared__ float s_m[kThreads / 64];
+  __shared__ int s_i[kThreads / 64];
+  __shared__ double s_red[kThreads / 64];
+  __shared__ int s_last;
+  constexpr int kEl = kStatChunk / kThreads;   // elements per thread
+  const int C = P.C;
+  const int row = blockIdx.x / C;
+  const int cidx = blockIdx.x - row * C;
+  const int k = P.k;
+  const int b = row / (2 * k + 1), r = row - b * (2 * k + 1);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float T = P.temps[b];
+  const bool greedy = greedy_temperature(T);
+  if (greedy && r > k) return;
+  const float* z = r <= k ? P.zp + ((long long)b * (k + 1) + r) * P.V : P.zq + ((long long)b * k + (r - k - 1)) * P.V;
+  const int x0 = cidx * P.CS, x1 = min(P.V, x0 + P.CS);
+
+  // element j of this thread: VEC4 -> x0 + 4 (tid + (j / 4) kThreads) + j % 4, else
+  // x0 + tid + j kThreads; both increase with j.  Loads past the chunk read a clamped address.
+  float v[kEl];
+  auto index = [&](int j) {
+    return VEC4 ? x0 + 4 * (tid + (j >> 2) * kThreads) + (j & 3) : x0 + tid + j * kThreads;
+  };
+#pragma unroll
+  for (int j = 0; j < kEl; j += 4) {
+    if (VEC4) {
+      const float4 u = *reinterpret_cast<const float4*>(z + min(index(j), x1 - 4));
+      v[j] = u.x; v[j + 1] = u.y; v[j + 2] = u.z; v[j + 3] = u.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[j + u] = z[min(index(j + u), x1 - 1)];
+    }
+  }
+  float m = -INFINITY;
+  int mi = INT_MAX;
+#pragma unroll
+  for (int j = 0; j < kEl; ++j)
+    if (index(j) < x1 && v[j] > m) {
+      m = v[j];
+      mi = index(j);
+    }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) argmax_merge(m, mi, __shfl_xor(m, d), __shfl_xor(mi, d));
+  if (lane == 0) {
+    s_m[wv] = m;
+    s_i[wv] = mi;
+  }
+  __syncthreads();
+  m = s_m[0];
+  mi = s_i[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) argmax_merge(m, mi, s_m[w], s_i[w]);
+  double S = 0.0;
+  const double cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
+  if (!greedy) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kEl; ++j)
+      if (index(j) < x1) acc += exp2_f64(((double)v[j] - (double)m) * cT);
+    S = block_sum(acc, s_red);
+  }
+  if (tid == 0) {
+    unsigned long long* dst = reinterpret_cast<unsigned long long*>(P.part + (long long)row * C + cidx);
+    const unsigned long long mw = (unsigned long long)__float_as_uint(m) | ((unsigned long long)(unsigned)mi << 32);
+    __hip_atomic_store(dst, (unsigned long long)__double_as_longlong(S), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, mw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int ticket = __hip_atomic_fetch_add(P.row_tickets + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (ticket == C - 1);
+  }
+  __syncthreads();
+  if (!s_last || tid >= 64) return;
+
+  // merge the row's chunks (one wave; lane holds chunks 4 lane .. 4 lane + 3; C <= 256)
+  if (tid == 0) __hip_atomic_store(P.row_tickets + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float cm[4];
+  int ci_[4];
+  double cs[4];
+  float M = -INFINITY;
+  int I = INT_MAX;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ci = 4 * lane + j;
+    cm[j] = -INFINITY;
+    ci_[j] = INT_MAX;
+    cs[j] = 0.0;
+    if (ci < C) {
+      const unsigned long long* src = reinterpret_cast<const unsigned long long*>(P.part + (long long)row * C + ci);
+      cs[j] = __longlong_as_double((long long)__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const unsigned long long mw = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      cm[j] = __uint_as_float((unsigned)(mw & 0xffffffffu));
+      ci_[j] = (int)(mw >> 32);
+    }
+    argmax_merge(M, I, cm[j], ci_[j]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) argmax_merge(M, I, __shfl_xor(M, d), __shfl_xor(I, d));
+  double Ssum = 0.0;
+  if (!greedy) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * lane + j < C) Ssum += cs[j] * exp2_f64(((double)cm[j] - (double)M) * cT);
+    Ssum = wave_sum(Ssum);
+  }
+  if (lane == 0) P.stats[row] = LogitRowStat{Ssum, M, I};
+}
+
 }  // namespace
 
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
   const dim3 grid((unsigned)((long long)p.C * p.B));
   if (vec4) {
-    hipExtLaunchKernelGGL(spec_verify_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    hipExtLaunchKernelGGL((spec_verify_kernel<true, false>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   } else {
-    hipExtLaunchKernelGGL(spec_verify_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    hipExtLaunchKernelGGL((spec_verify_kernel<false, false>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)((long long)p.C * p.B));
+  if (vec4) {
+    hipExtLaunchKernelGGL((spec_verify_kernel<true, true>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  } else {
+    hipExtLaunchKernelGGL((spec_verify_kernel<false, true>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)((long long)p.B * (2 * p.k + 1) * p.C));
+  if (vec4) {
+    hipExtLaunchKernelGGL(logit_stats_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  } else {
+    hipExtLaunchKernelGGL(logit_stats_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   }
   return hipGetLastError();
 }

@@ -120,6 +120,14 @@ inline size_t verify_bytes(long long B) {
   return align256(256 + (size_t)B * (kMaxChunks * 8 + 4));
 }
 
+// Statistics of one logit row z at temperature T > 0: m = max z, argmax = its first index,
+// S = sum_x 2^((z_x - m) * log2(e) / T) (fp64).  At T = 0 only m and argmax are set.
+struct LogitRowStat {
+  double S;
+  float m;
+  int32_t argmax;
+};
+
 struct VerifyParams {
   const float* p;
   const float* q;
@@ -133,6 +141,54 @@ struct VerifyParams {
   int32_t* err;
   int32_t* tickets_end;   // ticket of sequence b is tickets_end[-(b + 1)]
   double* chunk_sums;
+  // verification from logits: p and q hold target and draft logits, temps the per-sequence
+  // temperature, stats the rows' (max, argmax, sum of exponentials) from the statistics kernel
+  const float* temps = nullptr;
+  const LogitRowStat* stats = nullptr;
+};
+
+// ---------------------------------------------------------------------------------------
+// Verification-from-logits workspace layout (R = B(2k+1) rows, C1 = ceil(V / 4096)).
+//   [0, 256)        header: err word
+//   stats           LogitRowStat [R]
+//   part            LogitRowStat [R][C1]
+//   chunk_sums      double [B][kMaxChunks]
+//   tickets         int32, growing down from the end: sequence b at end - 4(b+1), row r at
+//                   end - 4(B + r + 1); all return to 0 at the end of every call.
+// The data lies in the first half of the workspace and the tickets in the second half (the
+// size required is twice the larger of the two), so no call's tickets ever overlap data an
+// earlier call of another shape left behind.
+// ---------------------------------------------------------------------------------------
+constexpr int kStatChunk = 4096;
+
+struct LogitsLayout {
+  size_t stats, part, chunk_sums, data_end, tickets, total;
+};
+
+inline LogitsLayout logits_layout(long long B, int k, int V) {
+  LogitsLayout L;
+  const long long R = B * (2 * k + 1);
+  const long long C1 = (V + kStatChunk - 1) / kStatChunk;
+  size_t o = 256;
+  L.stats = o;       o = align256(o + (size_t)R * sizeof(LogitRowStat));
+  L.part = o;        o = align256(o + (size_t)(R * C1) * sizeof(LogitRowStat));
+  L.chunk_sums = o;  o = align256(o + (size_t)B * kMaxChunks * 8);
+  L.data_end = o;
+  L.tickets = (size_t)(R + B) * 4;
+  L.total = 2 * align256(L.data_end > L.tickets ? L.data_end : L.tickets);
+  return L;
+}
+
+struct LogitStatsParams {
+  const float* zp;          // [B][k+1][V] target logits
+  const float* zq;          // [B][k][V] draft logits
+  const float* temps;       // [B]
+  LogitRowStat* part;       // [B * (2k+1)][C] per-chunk partials
+  LogitRowStat* stats;      // [B * (2k+1)] merged rows: k+1 target rows, then k draft rows
+  int32_t* row_tickets;     // [B * (2k+1)], zero between calls
+  int32_t B, k, V;
+  int32_t C, CS;            // chunks per row and their length (multiple of 4, <= 4096)
+  int32_t* err;
 };
 
 // launchers (defined in the .hip files); return hipError_t of the launch
@@ -143,6 +199,8 @@ hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
+hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
+hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
