@@ -426,7 +426,8 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
   const long long R = (long long)num_seqs * (2 * k + 1);
   const long long C1 = ((long long)vocab + kStatChunk - 1) / kStatChunk;
-  if (R * C1 >= (1LL << 31)) return fail(VAP_EINVAL, "too many logit rows");
+  if (C1 > kStatMaxChunks) return fail(VAP_EINVAL, "vocab=%d needs more than %d statistics chunks", vocab, kStatMaxChunks);
+  if (R * C1 + (long long)kStatWavesPerCU * 1024 >= (1LL << 31)) return fail(VAP_EINVAL, "too many logit rows");
   const DevInfo* d = device_info();
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
 
@@ -439,14 +440,14 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   S.zq = draft_logits;
   S.temps = temperatures;
   S.part = reinterpret_cast<LogitRowStat*>(ws + lay.part);
-  S.stats = reinterpret_cast<LogitRowStat*>(ws + lay.stats);
-  S.row_tickets = tickets_end - num_seqs - R;
   S.B = num_seqs;
   S.k = k;
   S.V = vocab;
   S.C = (int)C1;
-  S.CS = kStatChunk;
   S.err = reinterpret_cast<int32_t*>(ws);
+  // persistent statistics waves: kStatWavesPerCU per CU, no more than there are items
+  const long long stat_waves = std::min(R * C1, (long long)d->num_cus * kStatWavesPerCU);
+  const int stat_wg = (int)((stat_waves + kWavesPerWG - 1) / kWavesPerWG);
 
   // verification chunks: as spec_verify
   long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
@@ -472,11 +473,12 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   P.tickets_end = tickets_end;
   P.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk_sums);
   P.temps = temperatures;
-  P.stats = S.stats;
+  P.part = S.part;
+  P.C1 = (int)C1;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const KTimer t1 = timer_slot(5);
-  hipError_t e = launch_logit_stats(S, vec4, stream, t1);
+  hipError_t e = launch_logit_stats(S, vec4, stat_wg, stream, t1);
   timer_commit(5, t1, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "logit statistics launch: %s", hipGetErrorString(e));
   const KTimer t2 = timer_slot(6);

@@ -25,12 +25,14 @@
 // sampled from logits): p_i = softmax(z_p,i / T), q_i = softmax(z_q,i / T) for a temperature
 // T > 0, then the same rule; at T = 0 (same page, section "Frequently Asked Questions": exact
 // token matching) a draft passes when it is its target row's first argmax and the emitted token
-// is the argmax of row n.  A statistics kernel first reduces every logit row to (max, first
-// argmax, S = sum 2^((z - max) log2(e) / T)) with one workgroup per (row, 4096-token chunk)
-// and an arrival ticket per row; the verification kernel above then evaluates
-// p(x) = 2^((z_x - max) log2(e) / T) / S wherever it needs a probability, so no probability
-// row is ever written.  The exponentials are taken in fp64 (exp2_f64), which keeps every
-// decision within rounding of the fp64 oracle.
+// is the argmax of row n.  A statistics kernel of persistent waves reduces every 2048-token
+// chunk of every logit row to (max, first argmax, S = sum 2^((z - max) log2(e) / T)), loading
+// its next chunk while it computes the current one; each verification workgroup then merges
+// the chunks of its own sequence's rows in LDS (M = max m_c, S = sum S_c 2^((m_c - M) log2(e) / T),
+// in chunk order, so every workgroup of a sequence gets the same values) and evaluates
+// p(x) = 2^((z_x - M) log2(e) / T) / S wherever the rule needs a probability.  No probability
+// row is written.  The exponentials are taken in fp64 (exp2_f64), which keeps every decision
+// within rounding of the fp64 oracle.
 #include <cfloat>
 #include <type_traits>
 
@@ -46,27 +48,24 @@ __device__ __forceinline__ double residual_or_p(float p, float q, bool residual)
   return residual ? fmax(0.0, d) : d;
 }
 
-// 2^a in fp64 for a <= 0: a = n + f with n = rint(a) and |f| <= 1/2, 2^f = e^y with y = f ln 2
-// (|y| <= 0.347) from the Taylor series of e^y through y^12 (truncation below 2e-16 relative,
-// Horner form), then scaled by 2^n.  Arguments below -1080 (and NaN) give 0.
-__device__ __forceinline__ double exp2_f64(double a) {
-  if (!(a > -1080.0)) return 0.0;
-  const double n = rint(a);
-  const double y = (a - n) * 0.69314718055994530942;
-  double p = 1.0 / 479001600.0;
-  p = fma(p, y, 1.0 / 39916800.0);
-  p = fma(p, y, 1.0 / 3628800.0);
-  p = fma(p, y, 1.0 / 362880.0);
-  p = fma(p, y, 1.0 / 40320.0);
-  p = fma(p, y, 1.0 / 5040.0);
-  p = fma(p, y, 1.0 / 720.0);
-  p = fma(p, y, 1.0 / 120.0);
-  p = fma(p, y, 1.0 / 24.0);
-  p = fma(p, y, 1.0 / 6.0);
-  p = fma(p, y, 0.5);
-  p = fma(p, y, 1.0);
-  p = fma(p, y, 1.0);
-  return ldexp(p, (int)n);
+// 2^a in fp64 for a <= 0 (arguments below -1080, and NaN, give 0): a = (n + j/64) + r with
+// n + j/64 = rint(64 a) / 64, j in [0, 64) and |r| <= 1/128; 2^(j/64) comes from a 64-entry table
+// (tab, filled by fill_exp2_table) and 2^r = e^(r ln 2) from its Taylor series through r^3
+// (coefficients (ln 2)^i / i!, truncation below 4e-11 relative); the product is scaled by 2^n.
+__device__ __forceinline__ void fill_exp2_table(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
+__device__ __forceinline__ double exp2_f64(double a, const double* tab) {
+  a = fmax(a, -1080.0);
+  const double n64 = rint(a * 64.0);
+  const double r = fma(n64, -1.0 / 64.0, a);
+  const int ni = (int)n64;
+  double p = 0.055504108664821576;
+  p = fma(p, r, 0.2402265069591007);
+  p = fma(p, r, 0.6931471805599453);
+  p = fma(p, r, 1.0);
+  return ldexp(p * tab[ni & 63], ni >> 6);
 }
 
 // Weight of a token in the row that is sampled, from the two values loaded for it (the target
@@ -79,9 +78,10 @@ struct ProbWeight {
 struct LogitWeight {
   bool residual;
   double mp, mq, c, inv_sp, inv_sq;   // row maxima, log2(e) / T, reciprocals of the row sums
+  const double* tab;                  // 2^(j/64) table in LDS
   __device__ __forceinline__ double operator()(float zp, float zq) const {
-    const double p = exp2_f64(((double)zp - mp) * c) * inv_sp;
-    return residual ? fmax(0.0, p - exp2_f64(((double)zq - mq) * c) * inv_sq) : p;
+    const double p = exp2_f64(((double)zp - mp) * c, tab) * inv_sp;
+    return residual ? fmax(0.0, p - exp2_f64(((double)zq - mq) * c, tab) * inv_sq) : p;
   }
 };
 
@@ -227,13 +227,14 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
       }
     }
   }
+  double wv[kSlice];   // each weight is evaluated once and kept for the second pass
   double mine = 0.0;
   int lastpos = -1;
 #pragma unroll
   for (int j = 0; j < kSlice; ++j) {
-    const double wx = (a + j < b) ? w(pv[j], qv[j]) : 0.0;
-    mine += wx;
-    if (wx > 0.0) lastpos = a + j;
+    wv[j] = (a + j < b) ? w(pv[j], qv[j]) : 0.0;
+    mine += wv[j];
+    if (wv[j] > 0.0) lastpos = a + j;
   }
   double total;
   const double before = block_exclusive_scan(mine, s_red, total);
@@ -241,12 +242,51 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
   int found = INT_MAX;
 #pragma unroll
   for (int j = 0; j < kSlice; ++j) {
-    const double wx = (a + j < b) ? w(pv[j], qv[j]) : 0.0;
+    const double wx = wv[j];
     run += wx;
     if (found == INT_MAX && a + j < b && run > t) found = a + j;
   }
   first_above = block_min(found, s_int);
   last_positive = block_max(lastpos, s_int);
+}
+
+__device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi) {
+  if (om > m || (om == m && oi < i)) {
+    m = om;
+    i = oi;
+  }
+}
+
+// Merge the chunk partials of `rows` consecutive logit rows (part: [rows][C1]) into s_st: per
+// row M = max m_c with its first argmax, and (unless greedy) S = sum_c S_c 2^((m_c - M) cT), in a
+// fixed order.  Partials are staged through LDS in groups of rows; wave w merges rows w, w+4, ...
+constexpr int kMergeStage = 2048;   // 16-byte partials staged per pass (32 KB)
+
+__device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool greedy, double cT,
+                                LogitRowStat* s_st, uint4* s_stage, const double* tab) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = max(1, kMergeStage / C1);
+  for (int r0 = 0; r0 < rows; r0 += per) {
+    const int nr = min(per, rows - r0);
+    const uint4* src = reinterpret_cast<const uint4*>(part + (long long)r0 * C1);
+    for (int e = tid; e < nr * C1; e += kThreads) s_stage[e] = src[e];
+    __syncthreads();
+    for (int rr = wv; rr < nr; rr += kThreads / 64) {
+      const LogitRowStat* st = reinterpret_cast<const LogitRowStat*>(s_stage) + rr * C1;
+      float M = -INFINITY;
+      int I = INT_MAX;
+      for (int c = lane; c < C1; c += 64) argmax_merge(M, I, st[c].m, st[c].argmax);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) argmax_merge(M, I, __shfl_xor(M, d), __shfl_xor(I, d));
+      double S = 0.0;
+      if (!greedy) {
+        for (int c = lane; c < C1; c += 64) S += st[c].S * exp2_f64(((double)st[c].m - (double)M) * cT, tab);
+        S = wave_sum(S);
+      }
+      if (lane == 0) s_st[r0 + rr] = LogitRowStat{S, M, I};
+    }
+    __syncthreads();
+  }
 }
 
 // Temperature of sequence b in verification from logits: T > 0 samples; T = 0, and any value
@@ -264,6 +304,9 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   __shared__ int s_cstar;
   __shared__ double s_red[kThreads / 64];
   __shared__ int s_int[kThreads / 64];
+  __shared__ LogitRowStat s_st[LOGITS ? 2 * 64 + 1 : 1];        // merged row statistics
+  __shared__ uint4 s_stage[LOGITS ? kMergeStage : 1];           // staged chunk partials
+  __shared__ double s_tab[LOGITS ? 64 : 1];                     // 2^(j/64)
 
   const int C = P.C;
   const int b = blockIdx.x / C;
@@ -279,6 +322,8 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     greedy = greedy_temperature(T);
     if (!(T >= 0.f && T <= FLT_MAX) && cidx == 0 && tid == 0) atomicOr(P.err, VAP_DERR_TEMP);
     cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
+    fill_exp2_table(s_tab);   // visible after the merge's first barrier
+    merge_row_stats(P.part + srow * P.C1, P.C1, greedy ? k + 1 : 2 * k + 1, greedy, cT, s_st, s_stage, s_tab);
   }
 
   // 1. accept tests (first wave; k <= 64); the second wave fetches u_k meanwhile
@@ -301,11 +346,11 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
         if (!inside) {
           reject = true;
         } else if (greedy) {
-          reject = x != P.stats[srow + lane].argmax;
+          reject = x != s_st[lane].argmax;
         } else {
-          const LogitRowStat sp = P.stats[srow + lane], sq = P.stats[srow + k + 1 + lane];
-          const double pv = exp2_f64(((double)P.p[((long long)b * (k + 1) + lane) * V + x] - sp.m) * cT) / sp.S;
-          const double qv = exp2_f64(((double)P.q[((long long)b * k + lane) * V + x] - sq.m) * cT) / sq.S;
+          const LogitRowStat sp = s_st[lane], sq = s_st[k + 1 + lane];
+          const double pv = exp2_f64(((double)P.p[((long long)b * (k + 1) + lane) * V + x] - sp.m) * cT, s_tab) / sp.S;
+          const double qv = exp2_f64(((double)P.q[((long long)b * k + lane) * V + x] - sq.m) * cT, s_tab) / sq.S;
           reject = !(pv > 0.0 && r * qv <= pv);
         }
       }
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     if (greedy) {   // exact matching: the emitted token is the argmax of target row n
       if (cidx == 0) {
         if (tid <= k)
-          P.out_ids[(long long)b * (k + 1) + tid] = tid < n ? s_ids[tid] : (tid == n ? P.stats[srow + n].argmax : -1);
+          P.out_ids[(long long)b * (k + 1) + tid] = tid < n ? s_ids[tid] : (tid == n ? s_st[n].argmax : -1);
         if (tid == 0) P.n_accepted[b] = n;
       }
       return;
@@ -332,9 +377,9 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const float* qrow = residual ? P.q + ((long long)b * k + n) * V : prow;
   W w;
   if constexpr (LOGITS) {
-    const LogitRowStat sp = P.stats[srow + n];
-    const LogitRowStat sq = residual ? P.stats[srow + k + 1 + n] : sp;
-    w = LogitWeight{residual, (double)sp.m, (double)sq.m, cT, 1.0 / sp.S, 1.0 / sq.S};
+    const LogitRowStat sp = s_st[n];
+    const LogitRowStat sq = residual ? s_st[k + 1 + n] : sp;
+    w = LogitWeight{residual, (double)sp.m, (double)sq.m, cT, 1.0 / sp.S, 1.0 / sq.S, s_tab};
   } else {
     w = ProbWeight{residual};
   }
@@ -457,127 +502,107 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if (tid == 0) P.n_accepted[b] = n;
 }
 
-// Row statistics of the logits (see LogitRowStat): one workgroup per (row, chunk of kStatChunk
-// tokens), every load issued up front; the chunk's (max, first argmax, sum of exponentials
-// relative to its own max) is published, and the last workgroup of the row merges the chunks
-// in order: M = max m_c, S = sum_c S_c 2^((m_c - M) log2(e) / T).  Draft rows of greedy
-// sequences are skipped.
-__device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi) {
-  if (om > m || (om == m && oi < i)) {
-    m = om;
-    i = oi;
-  }
-}
-
+// Row statistics of the logits (see LogitRowStat), per chunk of kStatChunk tokens: persistent
+// waves take (row, chunk) items with a grid stride and keep the next item's loads in flight
+// while they reduce the current one (lane j holds 32 tokens; max and first argmax by cross-lane
+// shuffles, then the fp64 sum of exponentials).  Each item writes its partial with a plain
+// store; the verification kernel merges them.  Draft rows of greedy sequences are skipped.
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsParams P) {
-  __shared__ float s_m[kThreads / 64];
-  __shared__ int s_i[kThreads / 64];
-  __shared__ double s_red[kThreads / 64];
-  __shared__ int s_last;
-  constexpr int kEl = kStatChunk / kThreads;   // elements per thread
-  const int C = P.C;
-  const int row = blockIdx.x / C;
-  const int cidx = blockIdx.x - row * C;
-  const int k = P.k;
-  const int b = row / (2 * k + 1), r = row - b * (2 * k + 1);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float T = P.temps[b];
-  const bool greedy = greedy_temperature(T);
-  if (greedy && r > k) return;
-  const float* z = r <= k ? P.zp + ((long long)b * (k + 1) + r) * P.V : P.zq + ((long long)b * k + (r - k - 1)) * P.V;
-  const int x0 = cidx * P.CS, x1 = min(P.V, x0 + P.CS);
-
-  // element j of this thread: VEC4 -> x0 + 4 (tid + (j / 4) kThreads) + j % 4, else
-  // x0 + tid + j kThreads; both increase with j.  Loads past the chunk read a clamped address.
-  float v[kEl];
-  auto index = [&](int j) {
-    return VEC4 ? x0 + 4 * (tid + (j >> 2) * kThreads) + (j & 3) : x0 + tid + j * kThreads;
-  };
-#pragma unroll
-  for (int j = 0; j < kEl; j += 4) {
-    if (VEC4) {
-      const float4 u = *reinterpret_cast<const float4*>(z + min(index(j), x1 - 4));
-      v[j] = u.x; v[j + 1] = u.y; v[j + 2] = u.z; v[j + 3] = u.w;
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[j + u] = z[min(index(j + u), x1 - 1)];
-    }
-  }
-  float m = -INFINITY;
-  int mi = INT_MAX;
-#pragma unroll
-  for (int j = 0; j < kEl; ++j)
-    if (index(j) < x1 && v[j] > m) {
-      m = v[j];
-      mi = index(j);
-    }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) argmax_merge(m, mi, __shfl_xor(m, d), __shfl_xor(mi, d));
-  if (lane == 0) {
-    s_m[wv] = m;
-    s_i[wv] = mi;
-  }
+  constexpr int kEl = kStatChunk / 64;
+  __shared__ double s_tab[64];
+  fill_exp2_table(s_tab);
   __syncthreads();
-  m = s_m[0];
-  mi = s_i[0];
+  const int lane = threadIdx.x & 63;
+  const int k = P.k, C = P.C, V = P.V;
+  const int rows_per_seq = 2 * k + 1;
+  const int items = P.B * rows_per_seq * C;             // < 2^31 (checked on the host)
+  const int stride = gridDim.x * (kThreads / 64);
+
+  struct Item {
+    const float* z;
+    int x0, x1;
+    bool need, greedy;
+    double cT;
+  };
+  auto item_of = [&](int it) {
+    Item d;
+    const int row = it / C;
+    const int c = it - row * C;
+    const int b = row / rows_per_seq, r = row - b * rows_per_seq;
+    const float T = P.temps[b];
+    d.greedy = greedy_temperature(T);
+    d.need = !(d.greedy && r > k);
+    d.cT = d.greedy ? 0.0 : 1.4426950408889634 / (double)T;
+    d.z = r <= k ? P.zp + ((long long)b * (k + 1) + r) * V : P.zq + ((long long)b * k + (r - k - 1)) * V;
+    d.x0 = c * kStatChunk;
+    d.x1 = min(V, d.x0 + kStatChunk);
+    return d;
+  };
+  // lane's element j: VEC4 -> x0 + 4 (lane + 64 (j / 4)) + j % 4, else x0 + lane + 64 j (both
+  // increase with j); loads past the chunk read a clamped address and are masked
+  auto index = [&](const Item& d, int j) {
+    return VEC4 ? d.x0 + 4 * (lane + 64 * (j >> 2)) + (j & 3) : d.x0 + lane + 64 * j;
+  };
+  auto load = [&](const Item& d, float (&v)[kEl]) {
+    if (!d.need) return;
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) argmax_merge(m, mi, s_m[w], s_i[w]);
-  double S = 0.0;
-  const double cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
-  if (!greedy) {
-    double acc = 0.0;
+    for (int j = 0; j < kEl; j += 4) {
+      if (VEC4) {
+        const float4 u = *reinterpret_cast<const float4*>(d.z + min(index(d, j), d.x1 - 4));
+        v[j] = u.x; v[j + 1] = u.y; v[j + 2] = u.z; v[j + 3] = u.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[j + u] = d.z[min(index(d, j + u), d.x1 - 1)];
+      }
+    }
+  };
+  auto reduce = [&](const Item& d, int it, const float (&v)[kEl]) {
+    if (!d.need) return;
+    float m = -INFINITY;
+    int mi = INT_MAX;
 #pragma unroll
     for (int j = 0; j < kEl; ++j)
-      if (index(j) < x1) acc += exp2_f64(((double)v[j] - (double)m) * cT);
-    S = block_sum(acc, s_red);
-  }
-  if (tid == 0) {
-    unsigned long long* dst = reinterpret_cast<unsigned long long*>(P.part + (long long)row * C + cidx);
-    const unsigned long long mw = (unsigned long long)__float_as_uint(m) | ((unsigned long long)(unsigned)mi << 32);
-    __hip_atomic_store(dst, (unsigned long long)__double_as_longlong(S), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, mw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int ticket = __hip_atomic_fetch_add(P.row_tickets + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (ticket == C - 1);
-  }
-  __syncthreads();
-  if (!s_last || tid >= 64) return;
-
-  // merge the row's chunks (one wave; lane holds chunks 4 lane .. 4 lane + 3; C <= 256)
-  if (tid == 0) __hip_atomic_store(P.row_tickets + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float cm[4];
-  int ci_[4];
-  double cs[4];
-  float M = -INFINITY;
-  int I = INT_MAX;
+      if (index(d, j) < d.x1 && v[j] > m) {
+        m = v[j];
+        mi = index(d, j);
+      }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ci = 4 * lane + j;
-    cm[j] = -INFINITY;
-    ci_[j] = INT_MAX;
-    cs[j] = 0.0;
-    if (ci < C) {
-      const unsigned long long* src = reinterpret_cast<const unsigned long long*>(P.part + (long long)row * C + ci);
-      cs[j] = __longlong_as_double((long long)__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      const unsigned long long mw = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      cm[j] = __uint_as_float((unsigned)(mw & 0xffffffffu));
-      ci_[j] = (int)(mw >> 32);
+    for (int dd = 32; dd >= 1; dd >>= 1) argmax_merge(m, mi, __shfl_xor(m, dd), __shfl_xor(mi, dd));
+    double S = 0.0;
+    if (!d.greedy) {
+#pragma unroll
+      for (int j = 0; j < kEl; ++j)
+        if (index(d, j) < d.x1) S += exp2_f64(((double)v[j] - (double)m) * d.cT, s_tab);
+      S = wave_sum(S);
     }
-    argmax_merge(M, I, cm[j], ci_[j]);
+    if (lane == 0) P.part[it] = LogitRowStat{S, m, mi};
+  };
+
+  int it = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6));
+  if (it >= items) return;
+  float va[kEl], vb[kEl];
+  Item da = item_of(it), db;
+  load(da, va);
+  while (true) {
+    // ping: b's loads in flight while a is reduced, then pong
+    const int nb = it + stride;
+    if (nb < items) {
+      db = item_of(nb);
+      load(db, vb);
+    }
+    reduce(da, it, va);
+    if (nb >= items) break;
+    it = nb;
+    const int na = it + stride;
+    if (na < items) {
+      da = item_of(na);
+      load(da, va);
+    }
+    reduce(db, it, vb);
+    if (na >= items) break;
+    it = na;
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) argmax_merge(M, I, __shfl_xor(M, d), __shfl_xor(I, d));
-  double Ssum = 0.0;
-  if (!greedy) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * lane + j < C) Ssum += cs[j] * exp2_f64(((double)cm[j] - (double)M) * cT);
-    Ssum = wave_sum(Ssum);
-  }
-  if (lane == 0) P.stats[row] = LogitRowStat{Ssum, M, I};
 }
 
 }  // namespace
@@ -602,8 +627,8 @@ hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, hipStream_t stream, KTimer t) {
-  const dim3 grid((unsigned)((long long)p.B * (2 * p.k + 1) * p.C));
+hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)num_wg);
   if (vec4) {
     hipExtLaunchKernelGGL(logit_stats_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   } else {

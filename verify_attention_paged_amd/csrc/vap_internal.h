@@ -120,8 +120,8 @@ inline size_t verify_bytes(long long B) {
   return align256(256 + (size_t)B * (kMaxChunks * 8 + 4));
 }
 
-// Statistics of one logit row z at temperature T > 0: m = max z, argmax = its first index,
-// S = sum_x 2^((z_x - m) * log2(e) / T) (fp64).  At T = 0 only m and argmax are set.
+// Statistics of (a chunk of) one logit row z at temperature T > 0: m = max z, argmax = its first
+// index, S = sum_x 2^((z_x - m) * log2(e) / T) (fp64).  At T = 0 only m and argmax are set.
 struct LogitRowStat {
   double S;
   float m;
@@ -142,27 +142,34 @@ struct VerifyParams {
   int32_t* tickets_end;   // ticket of sequence b is tickets_end[-(b + 1)]
   double* chunk_sums;
   // verification from logits: p and q hold target and draft logits, temps the per-sequence
-  // temperature, stats the rows' (max, argmax, sum of exponentials) from the statistics kernel
+  // temperature, part the statistics kernel's per-chunk partials ([B(2k+1)][C1])
   const float* temps = nullptr;
-  const LogitRowStat* stats = nullptr;
+  const LogitRowStat* part = nullptr;
+  int32_t C1 = 0;
 };
 
 // ---------------------------------------------------------------------------------------
-// Verification-from-logits workspace layout (R = B(2k+1) rows, C1 = ceil(V / 4096)).
+// Verification-from-logits workspace layout (R = B(2k+1) rows, C1 = ceil(V / kStatChunk)).
 //   [0, 256)        header: err word
-//   stats           LogitRowStat [R]
-//   part            LogitRowStat [R][C1]
+//   part            LogitRowStat [R][C1]: per-chunk (max, first argmax, sum of exponentials
+//                   relative to the chunk's max), written by the statistics kernel and merged
+//                   by every verification workgroup for its own sequence
 //   chunk_sums      double [B][kMaxChunks]
-//   tickets         int32, growing down from the end: sequence b at end - 4(b+1), row r at
-//                   end - 4(B + r + 1); all return to 0 at the end of every call.
+//   tickets         int32 [B], growing down from the end (sequence b at end - 4(b+1)); they
+//                   return to 0 at the end of every call.
 // The data lies in the first half of the workspace and the tickets in the second half (the
 // size required is twice the larger of the two), so no call's tickets ever overlap data an
 // earlier call of another shape left behind.
 // ---------------------------------------------------------------------------------------
-constexpr int kStatChunk = 4096;
+constexpr int kStatChunk = 2048;        // tokens per statistics item (32 per lane of a wave)
+constexpr int kStatMaxChunks = 512;     // V <= 2^20
+#ifndef VAP_STAT_WAVES_PER_CU
+#define VAP_STAT_WAVES_PER_CU 8
+#endif
+constexpr int kStatWavesPerCU = VAP_STAT_WAVES_PER_CU;   // persistent statistics waves
 
 struct LogitsLayout {
-  size_t stats, part, chunk_sums, data_end, tickets, total;
+  size_t part, chunk_sums, data_end, tickets, total;
 };
 
 inline LogitsLayout logits_layout(long long B, int k, int V) {
@@ -170,11 +177,10 @@ inline LogitsLayout logits_layout(long long B, int k, int V) {
   const long long R = B * (2 * k + 1);
   const long long C1 = (V + kStatChunk - 1) / kStatChunk;
   size_t o = 256;
-  L.stats = o;       o = align256(o + (size_t)R * sizeof(LogitRowStat));
   L.part = o;        o = align256(o + (size_t)(R * C1) * sizeof(LogitRowStat));
   L.chunk_sums = o;  o = align256(o + (size_t)B * kMaxChunks * 8);
   L.data_end = o;
-  L.tickets = (size_t)(R + B) * 4;
+  L.tickets = (size_t)B * 4;
   L.total = 2 * align256(L.data_end > L.tickets ? L.data_end : L.tickets);
   return L;
 }
@@ -183,11 +189,9 @@ struct LogitStatsParams {
   const float* zp;          // [B][k+1][V] target logits
   const float* zq;          // [B][k][V] draft logits
   const float* temps;       // [B]
-  LogitRowStat* part;       // [B * (2k+1)][C] per-chunk partials
-  LogitRowStat* stats;      // [B * (2k+1)] merged rows: k+1 target rows, then k draft rows
-  int32_t* row_tickets;     // [B * (2k+1)], zero between calls
+  LogitRowStat* part;       // [B * (2k+1)][C] per-chunk partials (rows: k+1 target, then k draft)
   int32_t B, k, V;
-  int32_t C, CS;            // chunks per row and their length (multiple of 4, <= 4096)
+  int32_t C;                // chunks per row (ceil(V / kStatChunk) <= kStatMaxChunks)
   int32_t* err;
 };
 
@@ -200,7 +204,7 @@ const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8
 size_t attn_main_lds_bytes(int B);
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
-hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, hipStream_t stream, KTimer t = {});
+hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t = {});
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
