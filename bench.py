@@ -9,6 +9,8 @@ Default run (one JSON line on stdout):
     q_len 5, vocab 128256) -> verified tokens/s and the verifier's own GB/s;
   * roofline: the attention kernel's average duration from HIP events recorded on its own
     stream (the library's kernel timer) against the 8 TB/s HBM peak;
+  * logits_verify_step: spec_verify_logits on the verify batch's logits (temperature 1), beside
+    torch's softmax followed by spec_verify;
   * kv_cache: kv_append of the decode batch's new rows (bf16 and 8-bit), append + attention
     back to back, and kv_commit of the tree step's accepted paths;
   * cpu_baseline: the fp64 CPU oracle on the same decode batch, on the host's cores.
@@ -40,7 +42,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode/verify attention HBM GB/s (% of peak); verified tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_decode_traffic.txt")
 KERNEL_SOURCES = ["verify_attention_paged_amd/csrc/attn_paged.hip",
-                  "verify_attention_paged_amd/csrc/vap_internal.h"]
+                  "verify_attention_paged_amd/csrc/attn_internal.h",
+                  "verify_attention_paged_amd/csrc/vap_common.h"]
 
 
 def log(*a):
@@ -92,6 +95,19 @@ def kv_commit_bytes(n_moved, B, Hkv, D, u8) -> int:
     """Each moved row's K and V (and scales) read and written once, plus lengths, counts, paths."""
     row = (2 * Hkv * D + 16 * Hkv) if u8 else 4 * Hkv * D
     return 2 * n_moved * row + 16 * B
+
+
+def logits_verify_bytes(n_accepted, temps, k, V) -> int:
+    """Statistics pass: every target row, and the draft rows of sampled (T > 0) sequences, read
+    once; verification: the gathers and the row pair (or bonus row) drawn from, read again."""
+    total = 0
+    for n, T in zip(n_accepted, temps):
+        rows = (k + 1) + (k if T > 0 else 0)
+        total += 4 * V * rows + 16 * rows
+        total += 8 * k + 4 * (k + 1) + 4 * k + 4 * (k + 2) + 4
+        if T > 0:
+            total += 8 * V if n < k else 4 * V
+    return total
 
 
 def code_only(text: str) -> str:
@@ -375,6 +391,53 @@ def run_default(args, dev):
         f"{qnbytes / (qms * 1e-3) / 1e9:.1f} GB/s of {qnbytes / 1e6:.1f} MB; attention kernel "
         f"{qkernel_ms * 1e3:.1f} us -> {qnbytes / (qkernel_ms * 1e-3) / 1e9:.1f} GB/s")
 
+    # ---- verification from logits (spec_verify_step logits, T = 1), and the unfused path
+    lver = workloads.logits_verify_config("spec_verify_step")
+    zps = rotating_copies(lver.zp.to(dev), 768 << 20)
+    zqs = [lver.zq.to(dev) for _ in range(len(zps))]
+    lids, luni, ltemps = lver.draft_ids.to(dev), lver.uniforms.to(dev), lver.temps.to(dev)
+    l_out = torch.empty((lver.num_seqs, lver.k + 1), dtype=torch.int32, device=dev)
+    l_n = torch.empty((lver.num_seqs,), dtype=torch.int32, device=dev)
+    lws = vap.verify_logits_workspace(lver.num_seqs, lver.k, lver.vocab, dev)
+    lstep = lambda i: vap.spec_verify_logits(zps[i % len(zps)], zqs[i % len(zqs)], lids, luni, ltemps, l_out, l_n,
+                                             workspace=lws)
+    vap.timer_enable(True)
+    time_loop(lstep, 0, args.warmup)
+    vap.timer_read(vap.TIMER_LOGIT_STATS, reset=True)
+    vap.timer_read(vap.TIMER_VERIFY_LOGITS, reset=True)
+    lms, _ = time_loop(lstep, args.steps, 0)
+    st_ms, sc = vap.timer_read(vap.TIMER_LOGIT_STATS, reset=True)
+    lv_ms, lc = vap.timer_read(vap.TIMER_VERIFY_LOGITS, reset=True)
+    vap.timer_enable(False)
+    if vap.get_device_error(lws):
+        raise RuntimeError("device reported a data error in spec_verify_logits")
+    ln_host = l_n.cpu().numpy()
+    lbytes = logits_verify_bytes(ln_host, lver.temps.numpy(), lver.k, lver.vocab)
+    stats_bytes = 4 * lver.vocab * (2 * lver.k + 1) * lver.num_seqs
+    st_kernel, lv_kernel = st_ms / max(1, sc), lv_ms / max(1, lc)
+    # the unfused alternative: probability rows written by torch's softmax, then spec_verify
+    p_buf = torch.empty_like(zps[0])
+    q_buf = torch.empty_like(zqs[0])
+    uws = vap.verify_workspace(lver.num_seqs, lver.k, lver.vocab, dev)
+
+    def ustep(i):
+        torch.softmax(zps[i % len(zps)], dim=-1, out=p_buf)
+        torch.softmax(zqs[i % len(zqs)], dim=-1, out=q_buf)
+        vap.spec_verify(p_buf, q_buf, lids, luni, l_out, l_n, workspace=uws)
+
+    time_loop(ustep, 0, args.warmup)
+    ums, _ = time_loop(ustep, args.steps, 0)
+    log(f"verify from logits: {lms * 1e3:.1f} us per call (statistics kernel {st_kernel * 1e3:.1f} us -> "
+        f"{stats_bytes / (st_kernel * 1e-3) / 1e9:.0f} GB/s, verify kernel {lv_kernel * 1e3:.1f} us); "
+        f"torch softmax + spec_verify {ums * 1e3:.1f} us")
+    logits_line = {"workload": "spec_verify_step logits: 16 seqs, k 4, vocab 128256, target and draft logits fp32, "
+                               "temperature 1",
+                   "ms_per_call": round(lms, 5), "bytes": lbytes,
+                   "stats_kernel_ms": round(st_kernel, 5), "stats_bytes": stats_bytes,
+                   "stats_GB_per_s": round(stats_bytes / (st_kernel * 1e-3) / 1e9, 2),
+                   "verify_kernel_ms": round(lv_kernel, 5),
+                   "unfused_torch_softmax_plus_spec_verify_ms": round(ums, 5)}
+
     # ---- KV append (before attention) and commit (after verification)
     kinp = inp
     T, Hkv, D = kinp.total_q, kinp.num_kv_heads, kinp.head_dim
@@ -475,6 +538,7 @@ def run_default(args, dev):
                             "attention_kernel_ms": round(qkernel_ms, 5),
                             "speedup_vs_bf16_step": round(ms / qms, 3)},
         "kv_cache": kv_line,
+        "logits_verify_step": logits_line,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attn_main_kernel<128,16,1>",

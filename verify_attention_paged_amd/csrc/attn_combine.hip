@@ -17,7 +17,7 @@
 //  * nq = ceil(rows/4) quads; with nq < 8 the partial list is split too: S = 8 / nq waves per
 //    quad take partials p, p+S, p+2S, ... and merge in LDS in wave order;
 //  * up to kBatch partials are loaded before any is folded (one round trip per batch).
-#include "vap_internal.h"
+#include "attn_internal.h"
 
 namespace vap {
 namespace {

@@ -37,7 +37,7 @@
 //  * Only edge tiles (segment end, causal region of verify/prefill rows) are masked, and the
 //    masking is select-based: tokens past the segment -- including a block's unused tail,
 //    which may hold anything, even NaN -- get probability 0 and a zeroed V operand.
-#include "vap_internal.h"
+#include "attn_internal.h"
 
 #include <type_traits>
 

@@ -13,7 +13,7 @@
 //     head and UH stands for the fixed cost of starting a unit,
 //   * records the sequence holding the first work block of each worker wave, the waves
 //     splitting the total work TB evenly: wave w owns [w*TB/W', (w+1)*TB/W'), W' = min(W, TB).
-#include "vap_internal.h"
+#include "attn_internal.h"
 
 namespace vap {
 namespace {
