@@ -74,6 +74,39 @@ def test_ragged_fuzz_full_parity(case):
     H.assert_close_rows(out, H.oracle_rows(inp), f"fuzz {case}")
 
 
+WIDE = [
+    # batches averaging >= 48 rows per KV head and sequence run 64-row units (four row tiles);
+    # (ctx_lens, q_lens, Hq, Hkv, D, bs, kv_format)
+    ([40, 100, 20, 300], [16, 16, 16, 16], 32, 8, 128, 16, "bf16"),     # 64 rows per KV head
+    ([1500, 3000, 64], [64, 17, 64], 16, 2, 64, 32, "bf16"),            # long contexts: 64-row partials
+    ([4096, 900], [48, 48], 8, 8, 128, 16, "bf16"),                     # 48 rows (12 quads) per unit
+    ([700, 33], [33, 33], 16, 4, 128, 32, "bf16"),                      # 132 rows: units 64, 64, 4
+    ([2500, 70, 200], [64, 64, 17], 32, 8, 128, 16, "u8"),              # 8-bit cache
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_wide_units_full_parity(case):
+    ctx, ql, Hq, Hkv, D, bs, fmt = WIDE[case]
+    print("wide", WIDE[case], flush=True)
+    inp = _case(300 + case, ctx, ql, Hq, Hkv, D, bs, kv_format=fmt)
+    d = H.to_device(inp)
+    out = vap.paged_attn_step(**d)
+    torch.cuda.synchronize()
+    H.assert_close_rows(out, H.oracle_rows(inp), f"wide {case}")
+
+
+def test_wide_units_with_the_minimum_workspace():
+    """64-row units split over few worker waves: long partial lists of 64 rows each."""
+    inp = _case(310, [4096, 2000, 80], [64, 64, 64], 32, 8, 128, 16)
+    shape = vap.attn_shape(inp.q, inp.kv_pool, inp.block_tables)
+    import ctypes
+    lo = vap.load_library().vap_attn_workspace_min_bytes(ctypes.byref(shape))
+    ws = torch.zeros(lo, dtype=torch.uint8, device=H.device())
+    out, _ = _run(inp, workspace=ws)
+    H.assert_close_rows(out, H.oracle_rows(inp), "wide, minimum workspace")
+
+
 def test_block_placement_does_not_change_a_bit():
     """Same logical KV, two different pool permutations and pool sizes -> identical outputs."""
     ctx, ql = np.array([17, 300, 64, 1000]), np.array([1, 5, 1, 5])

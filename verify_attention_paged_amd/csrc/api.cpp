@@ -38,7 +38,7 @@ struct DevInfo {
   bool gfx950 = false;
   int num_cus = 0;
   char arch[64] = {0};
-  int attn_occ[2][2][2][2] = {};   // workgroups per CU of the attention kernel [D128][BS32][NRT2][KV8]
+  int attn_occ[2][2][3][2] = {};   // workgroups per CU of the attention kernel [D128][BS32][NRT 1/2/4][KV8]
 };
 
 constexpr int kMaxDevices = 64;
@@ -58,11 +58,11 @@ const DevInfo* device_info() {
     d.gfx950 = std::strncmp(d.arch, "gfx950", 6) == 0;
     for (int a = 0; a < 2; ++a)
       for (int b = 0; b < 2; ++b)
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 3; ++c)
           for (int k8 = 0; k8 < 2; ++k8) {
             int nb = 0;
             // occupancy with the largest in-workgroup plan (LDS never binds before registers)
-            const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, c ? 2 : 1, true, k8 != 0);
+            const void* f = attn_main_kernel_ptr(a ? 128 : 64, b ? 32 : 16, 1 << c, true, k8 != 0);
             if (f == nullptr ||
                 hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kAttnThreads,
                                                               attn_main_lds_bytes(kLdsPlanMaxSeqs)) != hipSuccess ||
@@ -142,8 +142,11 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
   c->BS = s->block_size;
   c->G = s->num_q_heads / s->num_kv_heads;
   // decode-only batches (one row per sequence) with at most 16 rows per KV head use one
-  // 16-row MFMA tile per unit; everything else uses two (32 rows per unit)
-  c->NRT = (s->total_q == s->num_seqs && c->G <= 16) ? 1 : 2;
+  // 16-row MFMA tile per unit; batches averaging 48 or more rows per KV head and sequence
+  // (token trees, prefill chunks) use four (64 rows per unit, so K/V are read once for up to
+  // 64 rows); everything else uses two (32 rows per unit)
+  const long long rows_per_kvh = s->num_seqs > 0 ? (long long)c->G * s->total_q / s->num_seqs : 0;
+  c->NRT = (s->total_q == s->num_seqs && c->G <= 16) ? 1 : (rows_per_kvh >= 48 ? 4 : 2);
   c->RG = 16 * c->NRT;
   const long long cap = (long long)s->max_blocks_per_seq * s->block_size;
   if (cap * s->num_q_heads >= (1LL << 31))
@@ -162,7 +165,7 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
 // (and partials to merge).  Batches averaging 8 or more query rows per sequence (prefill
 // chunks) make the MFMA work per byte large enough that a second wave per SIMD pays.
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
-  const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 2][c.kv8 ? 1 : 0];
+  const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 1 ? 0 : (c.NRT == 2 ? 1 : 2)][c.kv8 ? 1 : 0];
   const int per_cu = c.rows_per_seq >= 8 ? 2 : 1;
   return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * kWavesPerWG);
 }

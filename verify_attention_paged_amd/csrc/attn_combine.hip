@@ -10,20 +10,19 @@
 //
 // Layout of the work (the step is latency-bound: every partial was written by the previous
 // kernel, so each dependent round trip to L2/MALL costs more than the bytes):
-//  * one workgroup (8 waves) per descriptor; wave w's descriptor is valid when w holds the
+//  * one workgroup (NW = 8 waves, 16 for 64-row units) per descriptor; wave w's descriptor is valid when w holds the
 //    first block of a split unit, and then names the last wave wb holding part of it;
 //  * 16 lanes per row, each lane D/16 consecutive dims (float4 loads), so a wave covers a
 //    quad of 4 rows;
-//  * nq = ceil(rows/4) quads; with nq < 8 the partial list is split too: S = 8 / nq waves per
-//    quad take partials p, p+S, p+2S, ... and merge in LDS in wave order;
+//  * nq = ceil(rows/4) quads (up to 16 for 64-row units); with nq >= NW each wave merges whole
+//    quads (wave, wave + NW, ...); with nq < NW the partial list is split too: S = NW / nq
+//    waves per quad take partials p, p+S, p+2S, ... and merge in LDS in wave order;
 //  * up to kBatch partials are loaded before any is folded (one round trip per batch).
 #include "attn_internal.h"
 
 namespace vap {
 namespace {
 
-constexpr int kCombineWaves = 8;
-constexpr int kCombineThreads = 64 * kCombineWaves;
 constexpr int kBatch = 8;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -47,8 +46,10 @@ __device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const f
   s.M = Mn;
 }
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const AttnParams P) {
+// NW waves per workgroup: 8 for units of up to 32 rows, 16 for 64-row units (16 quads).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P) {
+  constexpr int kCombineWaves = NW;
   constexpr int DPL = D / 16;   // dims per lane
   constexpr int NV4 = DPL / 4;  // float4 loads per lane and partial
   __shared__ float s_ml[kCombineWaves][64][2];
@@ -72,19 +73,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Att
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int li = lane & 15;
-  const int quad = wave % nq;
-  const int sub = wave / nq;
-  const int r_raw = 4 * quad + (lane >> 4);
-  const int r = min(r_raw, nrows - 1);   // rows past the unit load a valid row, write nothing
 
-  RowState<DPL> st;
-  st.M = kNegInf;
-  st.L = 0.f;
+  // fold partials sub, sub+S, ... of the unit for row r into st (kBatch loads per round trip)
+  auto fold_rows = [&](RowState<DPL>& st, int r, int sub) {
+    st.M = kNegInf;
+    st.L = 0.f;
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) st.a[k] = 0.f;
-
-  if (sub < S) {
-    const int cnt = (n - sub + S - 1) / S;          // partials of this wave: sub, sub+S, ...
+    for (int k = 0; k < DPL; ++k) st.a[k] = 0.f;
+    const int cnt = (n - sub + S - 1) / S;
     for (int i0 = 0; i0 < cnt; i0 += kBatch) {
       float2 ml[kBatch];
       float v[kBatch][DPL];
@@ -108,51 +104,76 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Att
       for (int j = 0; j < kBatch; ++j)
         if (i0 + j < cnt) fold<DPL>(st, ml[j].x, ml[j].y, v[j]);
     }
-  }
-
-  if (S > 1) {                          // S is uniform over the workgroup
-    s_ml[wave][lane][0] = st.M;
-    s_ml[wave][lane][1] = st.L;
+  };
+  auto write_row = [&](const RowState<DPL>& st, int r_raw) {
+    if (r_raw >= nrows) return;
+    const int row = rg * RG + r_raw;
+    const int i = row / G;
+    float* op = P.out + ((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + DPL * li;
+    const float inv = 1.f / st.L;
 #pragma unroll
     for (int t = 0; t < NV4; ++t)
-      s_acc[wave][t][lane] = make_float4(st.a[4 * t], st.a[4 * t + 1], st.a[4 * t + 2], st.a[4 * t + 3]);
-    __syncthreads();
-    if (sub != 0) return;
-    for (int t2 = 1; t2 < S; ++t2) {
-      const int ow = quad + t2 * nq;
-      float v[DPL];
-#pragma unroll
-      for (int t = 0; t < NV4; ++t) {
-        const float4 x = s_acc[ow][t][lane];
-        v[4 * t] = x.x;
-        v[4 * t + 1] = x.y;
-        v[4 * t + 2] = x.z;
-        v[4 * t + 3] = x.w;
-      }
-      fold<DPL>(st, s_ml[ow][lane][0], s_ml[ow][lane][1], v);
+      reinterpret_cast<float4*>(op)[t] =
+          make_float4(st.a[4 * t] * inv, st.a[4 * t + 1] * inv, st.a[4 * t + 2] * inv, st.a[4 * t + 3] * inv);
+  };
+
+  RowState<DPL> st;
+  if (S == 1) {
+    // at least as many quads as waves: each wave takes quads wave, wave + NW, ... alone
+    for (int quad = wave; quad < nq; quad += kCombineWaves) {
+      const int r_raw = 4 * quad + (lane >> 4);
+      fold_rows(st, min(r_raw, nrows - 1), 0);   // rows past the unit load a valid row, write nothing
+      write_row(st, r_raw);
     }
-  } else if (sub != 0) {
     return;
   }
 
-  if (r_raw >= nrows) return;
-  const int row = rg * RG + r_raw;
-  const int i = row / G;
-  float* op = P.out + ((long long)(qoff + i) * P.Hq + kvh * G + (row - i * G)) * D + DPL * li;
-  const float inv = 1.f / st.L;
+  // fewer quads than waves: S waves per quad split its partials and merge in LDS in wave order
+  const int quad = wave % nq;
+  const int sub = wave / nq;
+  const int r_raw = 4 * quad + (lane >> 4);
+  if (sub < S) {
+    fold_rows(st, min(r_raw, nrows - 1), sub);
+  } else {
+    st.M = kNegInf;
+    st.L = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) st.a[k] = 0.f;
+  }
+  s_ml[wave][lane][0] = st.M;
+  s_ml[wave][lane][1] = st.L;
 #pragma unroll
   for (int t = 0; t < NV4; ++t)
-    reinterpret_cast<float4*>(op)[t] =
-        make_float4(st.a[4 * t] * inv, st.a[4 * t + 1] * inv, st.a[4 * t + 2] * inv, st.a[4 * t + 3] * inv);
+    s_acc[wave][t][lane] = make_float4(st.a[4 * t], st.a[4 * t + 1], st.a[4 * t + 2], st.a[4 * t + 3]);
+  __syncthreads();
+  if (sub != 0) return;
+  for (int t2 = 1; t2 < S; ++t2) {
+    const int ow = quad + t2 * nq;
+    float v[DPL];
+#pragma unroll
+    for (int t = 0; t < NV4; ++t) {
+      const float4 x = s_acc[ow][t][lane];
+      v[4 * t] = x.x;
+      v[4 * t + 1] = x.y;
+      v[4 * t + 2] = x.z;
+      v[4 * t + 3] = x.w;
+    }
+    fold<DPL>(st, s_ml[ow][lane][0], s_ml[ow][lane][1], v);
+  }
+  write_row(st, r_raw);
 }
 
 }  // namespace
 
 hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream) {
+  const bool wide = p.RG > 32;
+  const dim3 grid((unsigned)p.W), block(wide ? 1024 : 512);
   if (D == 64) {
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
+    if (wide) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p);
   } else if (D == 128) {
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.W), dim3(kCombineThreads), 0, stream, p);
+    if (wide) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

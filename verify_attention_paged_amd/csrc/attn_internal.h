@@ -19,7 +19,7 @@ constexpr int kWavesPerWG = kAttnThreads / 64;
 //              {kv head, row group, first packed row of the sequence, q_len,
 //               last wave holding part of the unit, slot of this wave's partial, valid, 0};
 //              valid = 0 when the wave holds the first block of no split unit.  Read by
-//              the combine kernel.  A unit has at most 32 rows (RG = 16 or 32).
+//              the combine kernel.  A unit has at most 64 rows (RG = 16, 32 or 64).
 //   g_L, g_Q   int32 [B]          per-sequence lengths (g_L = 0 for a skipped sequence)   \  only
 //   q_off      int32 [B]          first packed row of each sequence                        |  for
 //   seq_off    int32 [B+1]        exclusive prefix of per-sequence work                   |  B >

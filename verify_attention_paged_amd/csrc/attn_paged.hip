@@ -21,10 +21,12 @@
 //    the combine kernel merges the partials of each split unit in wave order (flash-decoding's
 //    combine) and writes its rows.
 //  * One wave processes all rows of a unit at once: the G query heads of a GQA group times
-//    the q_len rows (up to 16 * NRT rows).  Every K and V byte is loaded once from HBM,
-//    straight into MFMA operand registers (16 bytes per lane per load), and serves all those
-//    rows.  A wave keeps one 16-token tile in flight; the 8 to 12 other resident waves of its
-//    CU hide the latency.
+//    the q_len rows, up to 16 * NRT rows (NRT = 1, 2 or 4 row tiles: decode, verify / mixed,
+//    and batches averaging 48 or more rows per KV head such as token trees and prefill
+//    chunks).  Every K and V byte a unit needs is loaded once from HBM, straight into MFMA
+//    operand registers (16 bytes per lane per load), and serves all those rows.  A wave keeps
+//    two 16-token tiles in flight (a two-stage register pipeline); one wave per SIMD (two for
+//    prefill-heavy batches) already saturates the memory system for this access pattern.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the K tile is
 //    the A operand (lane = token, 16 contiguous bytes per lane), the query rows the B operand.
 //    Each lane then holds one query row and four tokens, so a row's softmax statistics live
@@ -730,7 +732,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
 }
 
 template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
-__global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : VAP_ATTN_WAVES_2RT) void attn_main_kernel(const AttnParams P) {
+__global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT == 2 ? VAP_ATTN_WAVES_2RT : 1)) void attn_main_kernel(const AttnParams P) {
   extern __shared__ int s_mem[];
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -819,8 +821,8 @@ hipError_t launch_main_t(const AttnParams& p, int num_wg, hipStream_t stream, KT
 size_t attn_main_lds_bytes(int B) { return size_t(4 * B + 1) * sizeof(int); }
 
 #define VAP_ATTN_VARIANTS(X) \
-  X(64, 16, 1) X(64, 16, 2) X(64, 32, 1) X(64, 32, 2) \
-  X(128, 16, 1) X(128, 16, 2) X(128, 32, 1) X(128, 32, 2)
+  X(64, 16, 1) X(64, 16, 2) X(64, 16, 4) X(64, 32, 1) X(64, 32, 2) X(64, 32, 4) \
+  X(128, 16, 1) X(128, 16, 2) X(128, 16, 4) X(128, 32, 1) X(128, 32, 2) X(128, 32, 4)
 
 hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream,
                             KTimer t) {
