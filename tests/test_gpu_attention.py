@@ -107,6 +107,34 @@ def test_wide_units_with_the_minimum_workspace():
     H.assert_close_rows(out, H.oracle_rows(inp), "wide, minimum workspace")
 
 
+LARGE = [
+    # batches above 2048 sequences take their plan from the plan kernel instead of LDS;
+    # (batch, max ctx_len, max q_len, Hq, Hkv, D, bs, kv_format)
+    (2049, 300, 5, 4, 1, 128, 16, "bf16"),
+    (3000, 200, 1, 8, 2, 64, 16, "bf16"),
+    (3000, 200, 3, 8, 2, 64, 32, "u8"),
+    (8192, 40, 1, 2, 1, 64, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LARGE)))
+def test_plan_kernel_path_large_batches(case):
+    B, Lmax, Qmax, Hq, Hkv, D, bs, fmt = LARGE[case]
+    print("large batch", LARGE[case], flush=True)
+    rng = np.random.default_rng(900 + case)
+    Q = rng.integers(1, Qmax + 1, size=B)
+    L = np.maximum(Q, rng.integers(1, Lmax + 1, size=B))
+    inp = _case(900 + case, L, Q, Hq, Hkv, D, bs, kv_format=fmt)
+    d = H.to_device(inp)
+    shape = vap.attn_shape(d["q"], d["kv_pool"], d["block_tables"])
+    ws = vap.attn_workspace(shape, H.device())
+    out = vap.paged_attn_step(**d, workspace=ws)
+    torch.cuda.synchronize()
+    assert vap.get_device_error(ws) == 0
+    assert torch.isfinite(out).all()
+    H.assert_close_rows(out, H.oracle_rows(inp, rows=H.sample_rows(inp, 400, seed=case)), f"large {case}")
+
+
 def test_block_placement_does_not_change_a_bit():
     """Same logical KV, two different pool permutations and pool sizes -> identical outputs."""
     ctx, ql = np.array([17, 300, 64, 1000]), np.array([1, 5, 1, 5])

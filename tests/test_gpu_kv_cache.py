@@ -87,6 +87,20 @@ def test_append_full_size_bit_exact(fmt, name):
     _assert_same(got, ref, f"{name} {fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "u8"])
+def test_append_above_the_staged_batch_limit(fmt):
+    """More than 4096 sequences: the append kernel reads the lengths from global memory."""
+    rng = np.random.default_rng(44)
+    B = 5000
+    Q = rng.integers(1, 4, size=B)
+    L = np.maximum(Q, rng.integers(1, 80, size=B))
+    inp = _inp(45, L, Q, Hq=4, Hkv=2, D=64, bs=16, fmt=fmt)
+    k, v = workloads.new_kv_rows(46, inp.total_q, 2, 64)
+    got, ref, err = _append_both(inp, k, v)
+    assert err == 0
+    _assert_same(got, ref, f"B {B} {fmt}")
+
+
 def test_append_quantiser_edge_rows():
     """All-zero, constant, one-signed, single-outlier and tiny-range rows."""
     L, Q = [40, 9], [8, 9]

@@ -175,6 +175,13 @@ def test_workspace_reuse_and_batch_sweep():
         _compare(p, q, ids, u, f"B={B}", workspace=ws)
 
 
+def test_large_batch_small_vocab():
+    """B = 4096 sequences of a 1000-token vocabulary: one chunk per row, one workgroup each."""
+    vin = workloads.verify_config("tiny", seed=77, batch=4096)
+    p, q, ids, u = _margin_inputs(vin, 5)
+    _compare(p, q, ids, u, "B=4096")
+
+
 def test_monte_carlo_emitted_distribution():
     """Raw uniforms, 2^18 sequences sharing fixed p_j, q_j (V = 8, k = 4): the tokens the GPU
     emits at each position follow p_j (chi-square at the 0.999 quantile)."""
