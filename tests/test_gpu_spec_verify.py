@@ -182,6 +182,17 @@ def test_large_batch_small_vocab():
     _compare(p, q, ids, u, "B=4096")
 
 
+def test_largest_vocabulary():
+    """V = 2^20, the largest vocabulary: 256 chunks of 4096 tokens per row."""
+    rng = np.random.default_rng(2020)
+    B, k, V = 2, 4, 1 << 20
+    pl = 3.0 * rng.standard_normal((B, k + 1, V))
+    ql = pl[:, :k] + 0.7 * rng.standard_normal((B, k, V))
+    vin = workloads.make_verify_inputs(2020, p_logits=pl, q_logits=ql, rng=rng)
+    p, q, ids, u = _margin_inputs(vin, 11)
+    _compare(p, q, ids, u, "V=2^20")
+
+
 def test_monte_carlo_emitted_distribution():
     """Raw uniforms, 2^18 sequences sharing fixed p_j, q_j (V = 8, k = 4): the tokens the GPU
     emits at each position follow p_j (chi-square at the 0.999 quantile)."""

@@ -146,6 +146,16 @@ def test_workspace_reuse_across_shapes():
         _compare(*_margin(inp, 9 + i), f"call {i} {(B, k, V)}", workspace=ws)
 
 
+def test_largest_vocabulary():
+    """V = 2^20: 512 statistics chunks per row, merged in three LDS passes per sequence."""
+    rng = np.random.default_rng(2021)
+    B, k, V = 2, 4, 1 << 20
+    zp = (3.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zq = (zp[:, :k] + 0.7 * rng.standard_normal((B, k, V))).astype(np.float32)
+    inp = workloads.make_logits_verify_inputs(2021, zp, zq, [1.0, 0.8])
+    _compare(*_margin(inp, 12), "V=2^20")
+
+
 def test_monte_carlo_first_token_at_temperature():
     """4096 copies of one sequence with drafts drawn from softmax(z_q / T) and raw uniforms:
     the first emitted token follows softmax(z_p / T) (chi-square at the 0.999 quantile)."""

@@ -110,6 +110,18 @@ def test_scalar_path_and_widest_tree():
     _compare(*_margin(tin, 4), "V 3001, 64 nodes")
 
 
+def test_large_vocabulary():
+    """V = 2^20 with 16-node trees."""
+    rng = np.random.default_rng(2022)
+    B, N, V = 2, 16, 1 << 20
+    pl = 3.0 * rng.standard_normal((B, N, V))
+    ql = pl + 0.7 * rng.standard_normal((B, N, V))
+    soft = lambda z: (np.exp(z - z.max(-1, keepdims=True)) / np.exp(z - z.max(-1, keepdims=True)).sum(-1, keepdims=True))
+    parents = np.stack([workloads.random_tree_parents(rng, N) for _ in range(B)])
+    tin = workloads.make_tree_verify_from_probs(2022, soft(pl).astype(np.float32), soft(ql).astype(np.float32), parents)
+    _compare(*_margin(tin, 13), "V=2^20, 16 nodes")
+
+
 def test_invalid_parent_sets_error_and_is_ignored():
     tin = workloads.tree_verify_config("tiny_tree", batch=2)
     p, q, parents, tokens, u = _margin(tin, 6)
