@@ -55,13 +55,15 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
   __shared__ float s_ml[kCombineWaves][64][2];
   __shared__ float4 s_acc[kCombineWaves][NV4][64];
 
+  // every worker wave w < W writes its descriptor on every call (zeroed when it has no split
+  // unit to open, including the waves past the step's work), so no other check is needed
   const int w = blockIdx.x;
-  const int TB = P.hdr->total_work;
-  if (w >= min(P.W, TB)) return;
   const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * w;
   const int4 d1 = dp[1];
-  if (d1.z == 0) return;                 // whole workgroup leaves: no barrier is pending
   const int4 d0 = dp[0];
+  // whole workgroup leaves: no barrier is pending.  (kvh = d0.x is never negative; testing it
+  // keeps the loads of both descriptor halves ahead of the branch, one round trip instead of two)
+  if (d1.z == 0 || d0.x < 0) return;
   const int kvh = d0.x, rg = d0.y, qoff = d0.z, Q = d0.w;
   const int wb = d1.x, slot_a = d1.y;
   const int G = P.G, RG = P.RG;
