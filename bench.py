@@ -348,7 +348,7 @@ def run_default(args, dev):
     t_ids = torch.empty((tver.num_seqs, tver.num_nodes), dtype=torch.int32, device=dev)
     t_path = torch.empty_like(t_ids)
     t_n = torch.empty((tver.num_seqs,), dtype=torch.int32, device=dev)
-    tvws = vap.tree_verify_workspace(dev)
+    tvws = vap.tree_verify_workspace(tver.num_seqs, dev)
 
     def tstep(i):
         vap.paged_attn_step(td["q"], tpools[i % len(tpools)], td["block_tables"], td["ctx_lens"], td["q_lens"],
@@ -360,18 +360,23 @@ def run_default(args, dev):
     time_loop(tstep, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
+    vap.timer_read(vap.TIMER_TREE_DRAW, reset=True)
     tms, _ = time_loop(tstep, args.steps, 0)
     tattn_ms, tc0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     tsv_ms, tc1 = vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
+    tdr_ms, tc2 = vap.timer_read(vap.TIMER_TREE_DRAW, reset=True)
     vap.timer_enable(False)
     tn_host = t_n.cpu().numpy()
     t_emitted = int((tn_host + 1).sum())
     tsv_bytes = tree_verify_bytes(tver.parents.numpy(), t_path.cpu().numpy(), tn_host, tver.vocab)
-    tsv_kernel_ms = tsv_ms / max(1, tc1)
+    tsv_walk_ms = tsv_ms / max(1, tc1)
+    tsv_draw_ms = tdr_ms / max(1, tc2)
+    tsv_kernel_ms = tsv_walk_ms + tsv_draw_ms
     tree_tok_s = t_emitted / (tms * 1e-3)
     log(f"tree verify step {tms * 1e3:.1f} us ({t_emitted} tokens emitted, {tn_host.mean():.2f} accepted per "
-        f"sequence); tree attention kernel {tattn_ms / max(1, tc0) * 1e3:.1f} us; spec_verify_tree kernel "
-        f"{tsv_kernel_ms * 1e3:.1f} us -> {tsv_bytes / (tsv_kernel_ms * 1e-3) / 1e9:.1f} GB/s")
+        f"sequence); tree attention kernel {tattn_ms / max(1, tc0) * 1e3:.1f} us; spec_verify_tree walk "
+        f"{tsv_walk_ms * 1e3:.1f} us + draw {tsv_draw_ms * 1e3:.1f} us -> "
+        f"{tsv_bytes / (tsv_kernel_ms * 1e-3) / 1e9:.1f} GB/s")
 
     # ---- decode step over an 8-bit KV cache (same lengths and shapes)
     qinp, qd, qpools, qout, qws, qnbytes = setup_attention("llama3_8b_decode", dev, kv_format="u8")
@@ -530,6 +535,8 @@ def run_default(args, dev):
                              "verified_tokens_per_s": round(tree_tok_s, 1),
                              "attention_kernel_ms": round(tattn_ms / max(1, tc0), 5),
                              "spec_verify_tree_kernel_ms": round(tsv_kernel_ms, 5),
+                             "spec_verify_tree_walk_ms": round(tsv_walk_ms, 5),
+                             "spec_verify_tree_draw_ms": round(tsv_draw_ms, 5),
                              "spec_verify_tree_bytes": tsv_bytes},
         "kv8_decode_step": {"workload": "llama3_8b_decode with uint8 K/V codes and per-token (scale, zero) "
                                         "pairs, dequantised in the kernel",

@@ -239,8 +239,8 @@ const char* vap_strerror(int code);
 /* Detail of the calling thread's last host-side error ("" if none). */
 const char* vap_last_error_message(void);
 
-/* Workspace bytes spec_verify_tree needs (its sticky error word). */
-size_t vap_tree_verify_workspace_bytes(void);
+/* Workspace bytes spec_verify_tree needs for num_seqs sequences (0 on bad sizes). */
+size_t vap_tree_verify_workspace_bytes(int32_t num_seqs);
 
 /*
  * spec_verify_tree -- verify a draft token tree per sequence (modified rejection sampling,
@@ -257,7 +257,7 @@ size_t vap_tree_verify_workspace_bytes(void);
  *   out_ids    int32 [B][N]    accepted tokens along the path, then the drawn token, then -1
  *   out_path   int32 [B][N]    accepted node indices along the path, then -1
  *   n_accepted int32 [B]       number of accepted draft nodes
- *   1 <= N <= 64, 1 <= V <= 2^24.
+ *   1 <= N <= 64, 1 <= V <= 2^20.
  *
  * Per sequence: at the current node, its children are tested in index order; child c with
  * token x passes when p_cur(x) > 0 and uniforms[c] * q(x) <= p_cur(x) (q = the current node's
@@ -266,7 +266,9 @@ size_t vap_tree_verify_workspace_bytes(void);
  * it with p_cur = its target row.  With no child left, one token is drawn from p_cur (inverse
  * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
  * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
- * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  One workgroup per sequence.
+ * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk (one
+ * workgroup per sequence), then the final draw spread over the GPU.  The workspace (zero-filled
+ * before first use) serves spec_verify_tree calls only.
  */
 int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
                      const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,
@@ -335,9 +337,10 @@ int kv_commit(void* kv, float* kv_scales, const int32_t* block_tables, const int
 /* ---- measurement helpers (not part of the step) ------------------------------------------ */
 
 /* Kernel timer.  While enabled, every paged_attn_step times its attention kernel (kind 0),
- * every spec_verify its kernel (kind 1), and spec_verify_tree (kind 2), kv_append (kind 3),
- * kv_commit (kind 4) theirs; spec_verify_logits its statistics kernel (kind 5) and its
- * verification kernel (kind 6); into a ring of 4096 event pairs per kind.  The events are stamped
+ * every spec_verify its kernel (kind 1), spec_verify_tree its walk (kind 2) and its final
+ * draw (kind 7), kv_append (kind 3) and kv_commit (kind 4) theirs, and spec_verify_logits its
+ * statistics kernel (kind 5) and its verification kernel (kind 6); into a ring of 4096 event
+ * pairs per kind.  The events are stamped
  * by the kernel launch itself (hipExtLaunchKernelGGL), so each pair spans the kernel's execution
  * without the wait before its first wave.  vap_timer_read synchronises on the recorded
  * events, returns the summed milliseconds and the number of pairs, and resets the ring when

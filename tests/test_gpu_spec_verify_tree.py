@@ -127,7 +127,7 @@ def test_invalid_parent_sets_error_and_is_ignored():
     p, q, parents, tokens, u = _margin(tin, 6)
     bad = parents.copy()
     bad[1, 5] = 7                              # a parent after its child
-    ws = vap.tree_verify_workspace(DEV)
+    ws = vap.tree_verify_workspace(2, DEV)
     out, path, n = vap.spec_verify_tree(_t(p, np.float32), _t(q, np.float32), _t(bad, np.int32),
                                         _t(tokens, np.int32), _t(u, np.float32), workspace=ws)
     assert vap.get_device_error(ws, clear=True) & vap.DERR_TREE

@@ -73,11 +73,14 @@ def test_u8_attention_null_pointers_and_empty_batch(lib):
 
 
 def test_tree_verify_rejected_on_host(lib):
-    ws = lib.vap_tree_verify_workspace_bytes()
-    assert ws >= 4
+    ws = lib.vap_tree_verify_workspace_bytes(4)
+    assert ws >= 256 + 4 * (32 + 256 * 8 + 4) and ws % 256 == 0
+    assert lib.vap_tree_verify_workspace_bytes(-1) == 0
+    assert lib.vap_tree_verify_workspace_bytes(8) > ws
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 65, 10, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 0, 10, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 0, None, 0, None) == B.VAP_EINVAL
+    assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, (1 << 20) + 1, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 4, 8, 10, None, 0, None) == B.VAP_EINVAL
     assert lib.spec_verify_tree(None, None, None, None, None, None, None, None, 0, 8, 10, None, 0, None) == B.VAP_OK
 

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     TIMER_KV_COMMIT,
     TIMER_LOGIT_STATS,
     TIMER_VERIFY_LOGITS,
+    TIMER_TREE_DRAW,
     attn_shape,
     attn_workspace,
     device_info,

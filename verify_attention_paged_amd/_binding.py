@@ -21,7 +21,7 @@ VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
 DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE, DERR_TEMP = (
     0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40)
 TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY, TIMER_KV_APPEND, TIMER_KV_COMMIT = 0, 1, 2, 3, 4
-TIMER_LOGIT_STATS, TIMER_VERIFY_LOGITS = 5, 6
+TIMER_LOGIT_STATS, TIMER_VERIFY_LOGITS, TIMER_TREE_DRAW = 5, 6, 7
 
 
 class VapError(RuntimeError):
@@ -57,7 +57,7 @@ SIGNATURES = {
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_verify_logits_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify_logits": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
-    "vap_tree_verify_workspace_bytes": (_sz, []),
+    "vap_tree_verify_workspace_bytes": (_sz, [_i32]),
     "spec_verify_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_kv_workspace_bytes": (_sz, []),
     "kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
@@ -307,8 +307,10 @@ def spec_verify_logits(target_logits, draft_logits, draft_ids, uniforms, tempera
     return out_ids, n_accepted
 
 
-def tree_verify_workspace(device=None) -> torch.Tensor:
-    n = load_library().vap_tree_verify_workspace_bytes()
+def tree_verify_workspace(num_seqs: int, device=None) -> torch.Tensor:
+    n = load_library().vap_tree_verify_workspace_bytes(num_seqs)
+    if n == 0:
+        _check(VAP_EINVAL)
     return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
 
 
@@ -341,7 +343,7 @@ def spec_verify_tree(p, q, parents, tokens, uniforms, out_ids=None, out_path=Non
         _need(t, name, torch.int32, 2, dev)
     _need(n_accepted, "n_accepted", torch.int32, 1, dev)
     if workspace is None:
-        workspace = tree_verify_workspace(dev)
+        workspace = tree_verify_workspace(B, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
     with torch.cuda.device(dev):
         rc = lib.spec_verify_tree(p.data_ptr(), q.data_ptr(), parents.data_ptr(), tokens.data_ptr(),

@@ -78,8 +78,8 @@ const DevInfo* device_info() {
 // ---- kernel timer ------------------------------------------------------------------------
 
 constexpr int kTimerSlots = 4096;
-constexpr int kTimerKinds = 7;   // attention, spec_verify, spec_verify_tree, kv_append, kv_commit,
-                                  // logit statistics, verification from logits
+constexpr int kTimerKinds = 8;   // attention, spec_verify, spec_verify_tree walk, kv_append, kv_commit,
+                                  // logit statistics, verification from logits, tree draw
 struct Timer {
   bool on = false;
   bool created = false;
@@ -491,7 +491,10 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   return ok();
 }
 
-size_t vap_tree_verify_workspace_bytes(void) { return 256; }
+size_t vap_tree_verify_workspace_bytes(int32_t num_seqs) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs) return 0;
+  return tree_verify_bytes(num_seqs);
+}
 
 int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
                      const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,
@@ -501,15 +504,17 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
     return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
   if (num_nodes < 1 || num_nodes > kMaxTreeNodes)
     return fail(VAP_EINVAL, "num_nodes=%d outside [1, %d]", num_nodes, kMaxTreeNodes);
-  if (vocab < 1 || vocab > (1 << 24)) return fail(VAP_EINVAL, "vocab=%d outside [1, 2^24]", vocab);
+  if (vocab < 1 || vocab > kMaxChunks * 4096) return fail(VAP_EINVAL, "vocab=%d outside [1, %d]", vocab, kMaxChunks * 4096);
   if (num_seqs == 0) return ok();
   if (!p || !q || !parents || !tokens || !uniforms || !out_ids || !out_path || !n_accepted || !workspace)
     return fail(VAP_EINVAL, "NULL data pointer");
-  if (workspace_bytes < vap_tree_verify_workspace_bytes())
-    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes, vap_tree_verify_workspace_bytes());
+  if (workspace_bytes < vap_tree_verify_workspace_bytes(num_seqs))
+    return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes,
+                vap_tree_verify_workspace_bytes(num_seqs));
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
   const DevInfo* d = device_info();
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+  char* ws = static_cast<char*>(workspace);
   TreeVerifyParams P;
   P.p = p;
   P.q = q;
@@ -523,12 +528,41 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.N = num_nodes;
   P.V = vocab;
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
-  P.err = static_cast<int32_t*>(workspace);
+  P.err = reinterpret_cast<int32_t*>(ws);
+  P.draws = reinterpret_cast<TreeDraw*>(ws + 256);
+
+  // draw chunks: as spec_verify (about two workgroups per CU over the batch)
+  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
+  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
+  C = std::max(1LL, std::min(C, cmax));
+  C = std::max(C, ((long long)vocab + 4095) / 4096);
+  long long CS = ((long long)vocab + C - 1) / C;
+  CS = (CS + 3) / 4 * 4;
+  C = ((long long)vocab + CS - 1) / CS;
+  TreeDrawParams D;
+  D.p = p;
+  D.q = q;
+  D.uniforms = uniforms;
+  D.out_ids = out_ids;
+  D.draws = P.draws;
+  D.B = num_seqs;
+  D.N = num_nodes;
+  D.V = vocab;
+  D.C = (int)C;
+  D.CS = (int)CS;
+  D.chunk_sums = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
+  D.tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
+  D.err = P.err;
+
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const KTimer t = timer_slot(2);
-  const hipError_t e = launch_tree_verify(P, stream, t);
+  hipError_t e = launch_tree_verify(P, stream, t);
   timer_commit(2, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "tree verify launch: %s", hipGetErrorString(e));
+  const KTimer t2 = timer_slot(7);
+  e = launch_tree_draw(D, P.vec4, stream, t2);
+  timer_commit(7, t2, e);
+  if (e != hipSuccess) return fail(VAP_EHIP, "tree draw launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -85,6 +85,16 @@ struct LogitWeight {
   }
 };
 
+// Final draw of a draft-tree walk: max(0, p - c q) with the closed-form residual's c (the tree
+// walk's weight; c = 0 is p itself).
+struct TreeDrawWeight {
+  bool residual;
+  double c;
+  __device__ __forceinline__ double operator()(float p, float q) const {
+    return residual ? fmax(0.0, fma(-c, (double)q, (double)p)) : (double)p;
+  }
+};
+
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
@@ -289,6 +299,103 @@ __device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool
   }
 }
 
+// Step 4 of a draw by the last workgroup of a sequence: with every chunk's sum of w published
+// (chunk_sums[0 .. C)), find the chunk holding t = u Z (one wave; each lane holds up to four
+// consecutive chunks, C <= 256), then the token inside it.  If Z = 0 the weights `fallback`
+// are drawn from instead (their chunk sums computed here); if those are all zero too,
+// VAP_DERR_EMPTY_ROW and token 0.  If rounding leaves t at or past the total, the last token
+// with positive weight.
+template <bool VEC4, class W>
+__device__ int finish_draw(const double* chunk_sums, int C, int CS, int V, float uk, const float* prow,
+                           const float* qrow, const W& w, const W& fallback, int32_t* err, double* s_loc,
+                           int& s_cstar, double* s_red, int* s_int) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  W wsel = w;
+  const float* srow_q = qrow;
+  double Z = 0.0;
+  if (tid < 64) {
+    double cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ci = 4 * lane + j;
+      cs[j] = ci < C ? __longlong_as_double((long long)__hip_atomic_load(
+                           reinterpret_cast<const unsigned long long*>(chunk_sums) + ci, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT))
+                     : 0.0;
+    }
+    const double mine = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+    double incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    Z = __shfl(incl, 63);
+    if (Z > 0.0) {
+      const double t = (double)uk * Z;
+      // first chunk whose inclusive running sum exceeds t; else (rounding left t at or above
+      // the total) the last chunk with a positive sum
+      double run = incl - mine;
+      int first = INT_MAX, lastnz = -1;
+      double base_first = 0.0, base_last = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ci = 4 * lane + j;
+        if (ci < C && first == INT_MAX && run + cs[j] > t) { first = ci; base_first = run; }
+        if (ci < C && cs[j] > 0.0) { lastnz = ci; base_last = run; }
+        run += cs[j];
+      }
+      const unsigned long long mf = __ballot(first != INT_MAX);
+      const unsigned long long ml = __ballot(lastnz >= 0);
+      if (mf) {
+        const int src = __ffsll((long long)mf) - 1;
+        if (lane == src) { s_cstar = first; s_loc[0] = base_first; s_loc[1] = t; }
+      } else {
+        const int src = 63 - __clzll((long long)ml);
+        if (lane == src) { s_cstar = lastnz; s_loc[0] = base_last; s_loc[1] = t; }
+      }
+    } else if (lane == 0) {
+      s_cstar = -1;
+    }
+  }
+  __syncthreads();
+  int token = 0;
+  int cstar = s_cstar;
+  double base = s_loc[0], t = s_loc[1];
+  if (cstar < 0) {
+    // empty weights: draw from the fallback weights (their chunk sums are computed here)
+    wsel = fallback;
+    srow_q = fallback.residual ? qrow : prow;
+    double cs = 0.0;
+    for (int j = 0; j < C; ++j) {
+      const int a = j * CS, e = min(V, a + CS);
+      const double sj = block_sum(chunk_partial<VEC4>(prow, srow_q, wsel, a, e), s_red);
+      if (tid == j) cs = sj;
+    }
+    double before = block_exclusive_scan(cs, s_red, Z);
+    if (Z > 0.0) {
+      t = (double)uk * Z;
+      const int cand = (tid < C && before + cs > t) ? tid : INT_MAX;
+      cstar = block_min(cand, s_int);
+      const int lastnz = block_max((tid < C && cs > 0.0) ? tid : -1, s_int);
+      if (cstar == INT_MAX) cstar = lastnz;
+      if (tid == cstar) s_loc[0] = before;
+      __syncthreads();
+      base = s_loc[0];
+      __syncthreads();
+    } else if (tid == 0) {
+      atomicOr(err, VAP_DERR_EMPTY_ROW);
+    }
+  }
+  if (cstar >= 0) {
+    const int a = cstar * CS, e = min(V, a + CS);
+    int first_above, last_positive;
+    chunk_select<VEC4>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above, last_positive);
+    token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
+  }
+  return token;
+}
+
 // Temperature of sequence b in verification from logits: T > 0 samples; T = 0, and any value
 // that is negative or not finite (reported), is greedy.
 __device__ __forceinline__ bool greedy_temperature(float T) { return !(T > 0.f && T <= FLT_MAX); }
@@ -404,92 +511,12 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   __syncthreads();
   if (!s_last) return;
 
-  // 4. last workgroup of sequence b: locate t among the chunk sums (one wave, each lane holds
-  // up to four consecutive chunks; C <= 256), then inside one chunk
+  // 4. last workgroup of sequence b: the chunk holding t, then the token inside it
   if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  W wsel = w;
-  const float* srow_q = qrow;
-  double Z = 0.0;
-  if (tid < 64) {
-    double cs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ci = 4 * lane + j;
-      cs[j] = ci < C ? __longlong_as_double((long long)__hip_atomic_load(
-                           reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + ci,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                     : 0.0;
-    }
-    const double mine = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-    double incl = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    Z = __shfl(incl, 63);
-    if (Z > 0.0) {
-      const double t = (double)s_uk * Z;
-      // first chunk whose inclusive running sum exceeds t; else (rounding left t at or above
-      // the total) the last chunk with a positive sum
-      double run = incl - mine;
-      int first = INT_MAX, lastnz = -1;
-      double base_first = 0.0, base_last = 0.0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ci = 4 * lane + j;
-        if (ci < C && first == INT_MAX && run + cs[j] > t) { first = ci; base_first = run; }
-        if (ci < C && cs[j] > 0.0) { lastnz = ci; base_last = run; }
-        run += cs[j];
-      }
-      const unsigned long long mf = __ballot(first != INT_MAX);
-      const unsigned long long ml = __ballot(lastnz >= 0);
-      if (mf) {
-        const int src = __ffsll((long long)mf) - 1;
-        if (lane == src) { s_cstar = first; s_loc[0] = base_first; s_loc[1] = t; }
-      } else {
-        const int src = 63 - __clzll((long long)ml);
-        if (lane == src) { s_cstar = lastnz; s_loc[0] = base_last; s_loc[1] = t; }
-      }
-    } else if (lane == 0) {
-      s_cstar = -1;
-    }
-  }
-  __syncthreads();
-  int token = 0;
-  int cstar = s_cstar;
-  double base = s_loc[0], t = s_loc[1];
-  if (cstar < 0) {
-    // empty residual: draw from p_n itself (its chunk sums are computed here)
-    wsel.residual = false;
-    srow_q = prow;
-    double cs = 0.0;
-    for (int j = 0; j < C; ++j) {
-      const int a = j * P.CS, e = min(V, a + P.CS);
-      const double sj = block_sum(chunk_partial<VEC4>(prow, prow, wsel, a, e), s_red);
-      if (tid == j) cs = sj;
-    }
-    double before = block_exclusive_scan(cs, s_red, Z);
-    if (Z > 0.0) {
-      t = (double)s_uk * Z;
-      const int cand = (tid < C && before + cs > t) ? tid : INT_MAX;
-      cstar = block_min(cand, s_int);
-      const int lastnz = block_max((tid < C && cs > 0.0) ? tid : -1, s_int);
-      if (cstar == INT_MAX) cstar = lastnz;
-      if (tid == cstar) s_loc[0] = before;
-      __syncthreads();
-      base = s_loc[0];
-      __syncthreads();
-    } else if (tid == 0) {
-      atomicOr(P.err, VAP_DERR_EMPTY_ROW);
-    }
-  }
-  if (cstar >= 0) {
-    const int a = cstar * P.CS, e = min(V, a + P.CS);
-    int first_above, last_positive;
-    chunk_select<VEC4>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above, last_positive);
-    token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
-  }
+  W p_only = w;   // an empty residual falls back to the row p_n itself
+  p_only.residual = false;
+  const int token = finish_draw<VEC4>(P.chunk_sums + (long long)b * C, C, P.CS, V, s_uk, prow, qrow, w, p_only,
+                                      P.err, s_loc, s_cstar, s_red, s_int);
 
   // 5. outputs
   if (tid <= k) {
@@ -605,6 +632,50 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
   }
 }
 
+// Final draw of spec_verify_tree (the walk itself is tree_verify_kernel in spec_verify_tree.hip):
+// one workgroup per (sequence, vocabulary chunk) sums its chunk of the weights max(0, p - c q)
+// of the node where the sequence's walk ended and publishes the sum; the last workgroup of the
+// sequence finds the token t = u_0 Z falls on, in ascending token id, as in spec_verify.
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParams P) {
+  __shared__ int s_last;
+  __shared__ double s_loc[2];
+  __shared__ int s_cstar;
+  __shared__ double s_red[kThreads / 64];
+  __shared__ int s_int[kThreads / 64];
+  const int C = P.C;
+  const int b = blockIdx.x / C;
+  const int cidx = blockIdx.x - b * C;
+  const int tid = threadIdx.x;
+  const TreeDraw d = P.draws[b];
+  const long long row = (long long)b * P.N + d.node;
+  const float* prow = P.p + row * P.V;
+  const float* qrow = P.q + row * P.V;
+  const TreeDrawWeight w{d.c > 0.0, d.c};
+  const int x0 = cidx * P.CS;
+  const int x1 = min(P.V, x0 + P.CS);
+  const double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
+  if (tid == 0) {
+    // publish the chunk sum write-through, wait for it, then arrive (as in spec_verify_kernel)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + cidx,
+                       (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (ticket == C - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float uk = P.uniforms[(long long)b * P.N];
+  const TreeDrawWeight prev{d.c_prev > 0.0, d.c_prev};
+  const int token = finish_draw<VEC4>(P.chunk_sums + (long long)b * C, C, P.CS, P.V, uk, prow, qrow, w, prev,
+                                      P.err, s_loc, s_cstar, s_red, s_int);
+  if (tid == 0) P.out_ids[(long long)b * P.N + d.n] = token;
+}
+
 }  // namespace
 
 hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
@@ -633,6 +704,16 @@ hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, 
     hipExtLaunchKernelGGL(logit_stats_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   } else {
     hipExtLaunchKernelGGL(logit_stats_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_draw(const TreeDrawParams& p, bool vec4, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)((long long)p.C * p.B));
+  if (vec4) {
+    hipExtLaunchKernelGGL(tree_draw_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+  } else {
+    hipExtLaunchKernelGGL(tree_draw_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   }
   return hipGetLastError();
 }

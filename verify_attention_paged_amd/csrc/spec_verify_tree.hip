@@ -19,10 +19,12 @@
 //     p_cur(x) = max(0, p(x) - c_j q(x)) / D_j,   c_0 = 0, D_0 = 1,
 //     c_{j+1} = c_j + D_j,   D_{j+1} = sum_x max(0, p(x) - c_{j+1} q(x))
 // (induction on max(0, max(0, p - c q) / D - q) = max(0, p - (c + D) q) / D), and a zero sum keeps
-// (c, D).  So the accept test evaluates p_cur at one token on one thread, each rejection costs
-// one streaming fp64 pass over the two rows, and the final draw scans the unnormalised weights
-// max(0, p - c q) (the inverse CDF is scale-invariant).  Values differ from the oracle's
-// step-by-step residuals only by rounding.
+// (c, D).  So the accept test evaluates p_cur at one token on one thread and each rejection costs
+// one streaming fp64 pass over the two rows.  The walk ends by recording (node, c, n); the final
+// draw over the unnormalised weights max(0, p - c q) (the inverse CDF is scale-invariant) is a
+// second kernel, tree_draw_kernel in spec_verify.hip, spread over about two workgroups per CU
+// like spec_verify's draw.  Values differ from the oracle's step-by-step residuals only by
+// rounding.
 #include "vap_internal.h"
 
 namespace vap {
@@ -51,28 +53,6 @@ __device__ __forceinline__ double block_sum(double x, double* s_red) {
   return t;
 }
 
-// Exclusive workgroup scan of one double per thread; `total` receives the sum.
-__device__ __forceinline__ double block_exclusive_scan(double x, double* s_red, double& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  double incl = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) s_red[wv] = incl;
-  __syncthreads();
-  double before = 0.0;
-  total = 0.0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) {
-    if (i < wv) before += s_red[i];
-    total += s_red[i];
-  }
-  __syncthreads();
-  return before + incl - x;
-}
-
 // unnormalised residual weight max(0, p - c q) of one token (c = 0: p itself)
 __device__ __forceinline__ double weight(float p, float q, double c) {
   return fmax(0.0, fma(-c, (double)q, (double)p));
@@ -88,10 +68,6 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
   __shared__ int s_accept;
   __shared__ int s_ids[kMaxNodes];
   __shared__ int s_path[kMaxNodes];
-  __shared__ int s_found;
-  __shared__ int s_slice;
-  __shared__ double s_base;
-  __shared__ double s_chunk[kThreads];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -114,7 +90,9 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
     s_cd[0] = 0.0;
     s_cd[1] = 1.0;
   }
+  __syncthreads();
   int u = 0, n = 0, last = 0;
+  double c_end = -1.0, c_end_prev = 0.0;   // set when the walk ends in a rejection
   while (true) {
     // next untested child of u (children have larger indices than their parent)
     if (tid < 64) {
@@ -124,7 +102,11 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
     }
     __syncthreads();
     const int c = s_next;
-    if (c < 0) break;
+    if (c < 0) {
+      c_end = s_cd[0];
+      c_end_prev = s_cd[0];
+      break;
+    }
     const float* prow = P.p + (row0 + u) * (long long)V;
     const float* qrow = P.q + (row0 + u) * (long long)V;
     if (tid == 0) {
@@ -152,8 +134,21 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
       __syncthreads();
       continue;
     }
-    // rejection: the next residual, c' = c + D and D' = sum_x max(0, p - c' q)
+    // rejection: the next residual, c' = c + D and D' = sum_x max(0, p - c' q).  When u has no
+    // child left to test, D' is not needed: the walk ends here and the draw kernel takes the
+    // weights max(0, p - c' q), falling back to max(0, p - c q) if they are all zero (the zero
+    // sum that keeps (c, D) in the walk).
     const double cn = s_cd[0] + s_cd[1];
+    if (tid < 64) {
+      const unsigned long long more = __ballot(tid < N && tid > c && s_par[tid] == u);
+      if (tid == 0) s_next = more ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_next) {
+      c_end = cn;
+      c_end_prev = s_cd[0];
+      break;
+    }
     double part = 0.0;
     const bool vec4 = P.vec4;
     if (vec4) {
@@ -185,136 +180,16 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
     last = c;
     __syncthreads();
   }
-  const double cf = s_cd[0];
-
-  // final draw from the weights max(0, p - cf q) of node u, in ascending token id.
-  // Level 1: the vocabulary is cut into chunks of CH = 1024 m tokens (at most 1024 chunks); a
-  // wave sums a chunk with coalesced 16-byte loads (two chunks in flight), a block scan places
-  // the chunks.  Level 2: one wave walks the chunk holding t, 256 tokens (a float4 per lane)
-  // at a time in ascending order, with a running carry.
-  const float* prow = P.p + (row0 + u) * (long long)V;
-  const float* qrow = P.q + (row0 + u) * (long long)V;
-  const int m = (V + kThreads * kThreads - 1) / (kThreads * kThreads);
-  const int CH = kThreads * m;
-  const int nch = (V + CH - 1) / CH;
-  const int lane = tid & 63, wv = tid >> 6;
-  // weights of the 4 tokens at x .. x+3 (0 past the end); scalar loads when rows are not
-  // 16-byte aligned or V is not a multiple of 4
-  auto weights4 = [&](int x, double (&w)[4]) {
-    if (P.vec4 && x + 3 < V) {
-      const float4 pv = *reinterpret_cast<const float4*>(prow + x);
-      const float4 qv = *reinterpret_cast<const float4*>(qrow + x);
-      w[0] = weight(pv.x, qv.x, cf); w[1] = weight(pv.y, qv.y, cf);
-      w[2] = weight(pv.z, qv.z, cf); w[3] = weight(pv.w, qv.w, cf);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int xe = min(x + e, V - 1);
-        const float pe = prow[xe], qe = qrow[xe];
-        w[e] = (x + e < V) ? weight(pe, qe, cf) : 0.0;
-      }
-    }
-  };
-  double lastw_pos = -1.0;
-  for (int k0 = wv; k0 < nch; k0 += 2 * (kThreads / 64)) {
-    double acc[2] = {0.0, 0.0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + h * (kThreads / 64);
-      if (k < nch) {
-        for (int i = 0; i < CH / 256; ++i) {
-          const int x = k * CH + 256 * i + 4 * lane;
-          if (x < V) {
-            double w[4];
-            weights4(x, w);
-            acc[h] += (w[0] + w[1]) + (w[2] + w[3]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (w[e] > 0.0) lastw_pos = fmax(lastw_pos, (double)(x + e));
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + h * (kThreads / 64);
-      const double cs = wave_sum(acc[h]);
-      if (k < nch && lane == 0) s_chunk[k] = cs;
-    }
-  }
-  __syncthreads();
-  const double cs = tid < nch ? s_chunk[tid] : 0.0;
-  double Zf;
-  const double before = block_exclusive_scan(cs, s_red, Zf);
-  if (tid == 0) {
-    s_found = INT_MAX;
-    s_slice = INT_MAX;
-  }
-  __syncthreads();
-  int token = 0;
-  if (Zf > 0.0) {
-    const double t = (double)s_u[0] * Zf;
-    // the chunk holding t (rounding can let two neighbours claim it: the first one wins)
-    if (tid < nch && before <= t && before + cs > t) atomicMin(&s_slice, tid);
-    __syncthreads();
-    if (tid == s_slice) s_base = before;
-    __syncthreads();
-    const int T = s_slice == INT_MAX ? -1 : s_slice;
-    if (T >= 0 && tid < 64) {
-      double carry = s_base;
-      for (int i = 0; i < CH / 256; ++i) {
-        const int x = T * CH + 256 * i + 4 * lane;
-        double w[4] = {0.0, 0.0, 0.0, 0.0};
-        if (x < V) weights4(x, w);
-        const double l0 = w[0], l1 = l0 + w[1], l2 = l1 + w[2], l3 = l2 + w[3];
-        double incl = l3;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const double y = __shfl_up(incl, d);
-          if (lane >= d) incl += y;
-        }
-        const double pre = carry + incl - l3;        // running sum before this lane's 4 tokens
-        int hit = INT_MAX;
-        if (pre + l0 > t) hit = x;
-        else if (pre + l1 > t) hit = x + 1;
-        else if (pre + l2 > t) hit = x + 2;
-        else if (pre + l3 > t) hit = x + 3;
-        if (hit >= V) hit = INT_MAX;
-        const unsigned long long mk = __ballot(hit != INT_MAX);
-        if (mk) {
-          const int src = __ffsll((long long)mk) - 1;
-          const int h = __shfl(hit, src);
-          if (lane == 0) s_found = h;
-          break;
-        }
-        carry += __shfl(incl, 63);
-      }
-    }
-    __syncthreads();
-    token = s_found;
-    if (token == INT_MAX) {                 // rounding left t at or past the total
-      if (tid == 0) s_found = -1;
-      __syncthreads();
-      if (lastw_pos >= 0.0) atomicMax(&s_found, (int)lastw_pos);
-      __syncthreads();
-      token = max(s_found, 0);
-    }
-  } else if (tid == 0) {
-    atomicOr(P.err, VAP_DERR_EMPTY_ROW);
-  }
-
+  // the walk ends at node u after n acceptances: the final draw (tree_draw_kernel, spread over
+  // the GPU) takes max(0, p - c q) of u with this c, and writes its token at out_ids[n]
   if (tid < N) {
-    int id = -1, node = -1;
-    if (tid < n) {
-      id = s_ids[tid];
-      node = s_path[tid];
-    } else if (tid == n) {
-      id = token;
-    }
-    P.out_ids[row0 + tid] = id;
-    P.out_path[row0 + tid] = node;
+    P.out_ids[row0 + tid] = tid < n ? s_ids[tid] : -1;
+    P.out_path[row0 + tid] = tid < n ? s_path[tid] : -1;
   }
-  if (tid == 0) P.n_accepted[b] = n;
+  if (tid == 0) {
+    P.draws[b] = TreeDraw{c_end, c_end_prev, u, n, {0, 0}};
+    P.n_accepted[b] = n;
+  }
 }
 
 }  // namespace

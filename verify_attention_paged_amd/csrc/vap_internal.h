@@ -111,6 +111,29 @@ hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStre
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxTreeNodes = 64;
 
+// Where the walk of one sequence ended: the final draw is from max(0, p - c q) of node `node`
+// (c = 0: p itself), or, if those weights are all zero, from max(0, p - c_prev q) (a walk that
+// ends in a rejection skips the pass that would have checked this); its token goes to
+// out_ids[b][n].
+struct TreeDraw {
+  double c;
+  double c_prev;
+  int32_t node;
+  int32_t n;
+  int32_t pad[2];
+};
+
+// ---------------------------------------------------------------------------------------
+// Tree verification workspace layout.
+//   [0, 256)                 header: err word
+//   [256, 256 + 32B)         TreeDraw [B], written by the walk, read by the draw kernel
+//   [256 + 32B, +2048B)      chunk_sums: double [B][kMaxChunks]
+//   [..., end)               tickets: int32, sequence b at end - 4(b+1); they return to 0
+// Every call checks bytes >= 256 + 2084 B, so a call's tickets never overlap data an earlier
+// call (any B) left behind (the same argument as for the verification workspace).
+// ---------------------------------------------------------------------------------------
+inline size_t tree_verify_bytes(long long B) { return align256(256 + (size_t)B * (32 + kMaxChunks * 8 + 4)); }
+
 struct TreeVerifyParams {
   const float* p;           // [B][N][V] target rows per node
   const float* q;           // [B][N][V] draft rows per node (the children's proposal)
@@ -123,9 +146,24 @@ struct TreeVerifyParams {
   int32_t B, N, V;
   bool vec4;                // V % 4 == 0 and p, q 16-byte aligned
   int32_t* err;
+  TreeDraw* draws;          // [B], written at the end of the walk
+};
+
+struct TreeDrawParams {
+  const float* p;
+  const float* q;
+  const float* uniforms;    // [B][N]: uniforms[b][0] drives the final draw
+  int32_t* out_ids;         // [B][N]: entry n of sequence b receives the drawn token
+  const TreeDraw* draws;
+  int32_t B, N, V;
+  int32_t C, CS;            // chunks per row and their length (multiple of 4, <= 4096)
+  double* chunk_sums;       // [B][C]
+  int32_t* tickets_end;     // ticket of sequence b is tickets_end[-(b + 1)]
+  int32_t* err;
 };
 
 hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream, KTimer t = {});
+hipError_t launch_tree_draw(const TreeDrawParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 
 // ---- KV append / commit ----------------------------------------------------------------------
 
