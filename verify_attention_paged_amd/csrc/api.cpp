@@ -106,13 +106,24 @@ void timer_commit(int kind, const KTimer& t, hipError_t launch) {
 
 // ---- attention shape checks ---------------------------------------------------------------
 
-// Fixed cost of starting a unit of work, in work blocks: about four 16-token tiles of
-// streaming time (its query rows and block-table window are dependent loads that the tile
-// pipeline cannot hide).  Counting it balances waves that start many short units.
-#ifndef VAP_UNIT_SETUP_TILES
-#define VAP_UNIT_SETUP_TILES 4
+// Fixed cost of starting a unit of work, in work blocks: a few 16-token tiles of streaming
+// time (its query rows and block-table window are dependent loads that the tile pipeline
+// cannot hide).  Counting it balances waves that start many short units.  Measured best:
+// 2 tiles for one-tile (decode) units over bf16 K/V, 4 over the 8-bit cache (its tiles cost
+// more math), 12 for units of several row tiles (verify rows, trees, prefill chunks).
+#ifndef VAP_UNIT_SETUP_TILES_1RT
+#define VAP_UNIT_SETUP_TILES_1RT 2
 #endif
-int unit_setup_blocks(int block_size) { return VAP_UNIT_SETUP_TILES * 16 / block_size; }
+#ifndef VAP_UNIT_SETUP_TILES_KV8
+#define VAP_UNIT_SETUP_TILES_KV8 4
+#endif
+#ifndef VAP_UNIT_SETUP_TILES_NRT
+#define VAP_UNIT_SETUP_TILES_NRT 12
+#endif
+int unit_setup_blocks(int block_size, int nrt, bool kv8) {
+  const int tiles = kv8 ? VAP_UNIT_SETUP_TILES_KV8 : (nrt == 1 ? VAP_UNIT_SETUP_TILES_1RT : VAP_UNIT_SETUP_TILES_NRT);
+  return std::max(1, tiles * 16 / block_size);
+}
 
 struct AttnPlanChoice {
   int D, BS, NRT, RG, G;
@@ -154,7 +165,7 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
   if ((long long)s->total_q * s->num_q_heads >= (1LL << 31))
     return fail(VAP_EINVAL, "total_q*num_q_heads exceeds 2^31");
   const long long rows_groups = ((long long)c->G * s->total_q + c->RG - 1) / c->RG + s->num_seqs;
-  if ((long long)s->num_kv_heads * (s->max_blocks_per_seq + unit_setup_blocks(c->BS)) * rows_groups >= (1LL << 31) - 1)
+  if ((long long)s->num_kv_heads * (s->max_blocks_per_seq + std::max(unit_setup_blocks(c->BS, c->NRT, false), unit_setup_blocks(c->BS, c->NRT, true))) * rows_groups >= (1LL << 31) - 1)
     return fail(VAP_EINVAL, "work of the step may exceed 2^31 blocks");
   return VAP_OK;
 }
@@ -164,9 +175,15 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
 // saturated for this access pattern, so more waves only add latency to every dependent load
 // (and partials to merge).  Batches averaging 8 or more query rows per sequence (prefill
 // chunks) make the MFMA work per byte large enough that a second wave per SIMD pays.
+#ifndef VAP_WAVES_PER_SIMD_DECODE
+#define VAP_WAVES_PER_SIMD_DECODE 1
+#endif
+#ifndef VAP_WAVES_PER_SIMD_PREFILL
+#define VAP_WAVES_PER_SIMD_PREFILL 2
+#endif
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 1 ? 0 : (c.NRT == 2 ? 1 : 2)][c.kv8 ? 1 : 0];
-  const int per_cu = c.rows_per_seq >= 8 ? 2 : 1;
+  const int per_cu = c.rows_per_seq >= 8 ? VAP_WAVES_PER_SIMD_PREFILL : VAP_WAVES_PER_SIMD_DECODE;
   return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * kWavesPerWG);
 }
 
@@ -289,7 +306,7 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
   P.W = W;
   P.RG = c.RG;
   P.BS = c.BS;
-  P.UH = unit_setup_blocks(c.BS);
+  P.UH = unit_setup_blocks(c.BS, c.NRT, kv8);
   const float scale = s.scale > 0.f ? s.scale : 1.0f / std::sqrt((float)s.head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.hdr = reinterpret_cast<AttnHeader*>(ws);
