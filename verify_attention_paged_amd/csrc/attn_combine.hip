@@ -10,7 +10,8 @@
 //
 // Layout of the work (the step is latency-bound: every partial was written by the previous
 // kernel, so each dependent round trip to L2/MALL costs more than the bytes):
-//  * one workgroup (NW = 8 waves, 16 for 64-row units) per descriptor; wave w's descriptor is valid when w holds the
+//  * one workgroup (NW = 2 waves for 16-row units, 8 for 32-row and 16 for 64-row units) per
+//    descriptor; wave w's descriptor is valid when w holds the
 //    first block of a split unit, and then names the last wave wb holding part of it;
 //  * 16 lanes per row, each lane D/16 consecutive dims (float4 loads), so a wave covers a
 //    quad of 4 rows;
@@ -46,7 +47,7 @@ __device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const f
   s.M = Mn;
 }
 
-// NW waves per workgroup: 8 for units of up to 32 rows, 16 for 64-row units (16 quads).
+// NW waves per workgroup: 2 for 16-row units, 8 for 32-row units, 16 for 64-row units (16 quads).
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P) {
   constexpr int kCombineWaves = NW;
@@ -168,14 +169,19 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
 }  // namespace
 
 hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream) {
-  const bool wide = p.RG > 32;
-  const dim3 grid((unsigned)p.W), block(wide ? 1024 : 512);
+  // waves per workgroup: 2 for 16-row units (decode), 8 for 32-row units, 16 for 64-row units.
+  // Most workgroups read an empty descriptor and leave; for decode batches the smaller
+  // workgroups measured faster (less to dispatch, and four quads need no more waves).
+  const int nw = p.RG > 32 ? 16 : (p.RG > 16 ? 8 : 2);
+  const dim3 grid((unsigned)p.W), block(64 * nw);
   if (D == 64) {
-    if (wide) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, 2>), grid, block, 0, stream, p);
   } else if (D == 128) {
-    if (wide) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_combine_kernel<128, 2>), grid, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
