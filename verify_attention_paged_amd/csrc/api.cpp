@@ -170,21 +170,29 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
   return VAP_OK;
 }
 
-// Worker waves: one per SIMD (one workgroup of four per CU) for decode- and verify-shaped
-// batches.  Each wave keeps two tiles in flight; at that depth the memory system is already
-// saturated for this access pattern, so more waves only add latency to every dependent load
-// (and partials to merge).  Batches averaging 8 or more query rows per sequence (prefill
-// chunks) make the MFMA work per byte large enough that a second wave per SIMD pays.
+// Worker waves: one workgroup per CU for decode- and verify-shaped batches.  Each wave keeps
+// two tiles in flight; at that depth the memory system is already saturated for this access
+// pattern, so more waves only add latency to every dependent load (and partials to merge).
+// Batches averaging 8 or more query rows per sequence (prefill chunks) make the MFMA work per
+// byte large enough that a second workgroup per CU pays.
 #ifndef VAP_WAVES_PER_SIMD_DECODE
 #define VAP_WAVES_PER_SIMD_DECODE 1
 #endif
 #ifndef VAP_WAVES_PER_SIMD_PREFILL
 #define VAP_WAVES_PER_SIMD_PREFILL 2
 #endif
+// Waves per attention workgroup: three for decode- and verify-shaped batches over bf16 K/V,
+// four otherwise.  With two tiles in flight per wave, three waves per CU already saturate HBM
+// for the bf16 gather: against four, the kernel was about 1 us faster and the step 1.5-2 us
+// faster (a quarter fewer partials to merge).  The 8-bit cache's heavier tile math and
+// prefill batches want the fourth wave (8-bit decode 43.5 against 50.6 us, mixed batch 346
+// against 364 us).
+int attn_wg_waves(const AttnPlanChoice& c) { return (!c.kv8 && c.rows_per_seq < 8) ? 3 : kWavesPerWG; }
+
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 1 ? 0 : (c.NRT == 2 ? 1 : 2)][c.kv8 ? 1 : 0];
   const int per_cu = c.rows_per_seq >= 8 ? VAP_WAVES_PER_SIMD_PREFILL : VAP_WAVES_PER_SIMD_DECODE;
-  return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * kWavesPerWG);
+  return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * attn_wg_waves(c));
 }
 
 // Shape and pointer checks shared by kv_append and kv_commit.
@@ -231,7 +239,13 @@ size_t vap_attn_workspace_bytes(const vap_attn_shape* shape) {
   AttnPlanChoice c;
   if (check_attn_shape(shape, &c) != VAP_OK) return 0;
   const DevInfo* d = device_info();
-  const int W = d ? worker_waves(d, c) : 256 * kWavesPerWG * 2;
+  // one workspace serves the bf16 and the 8-bit cache: size it for the larger launch
+  int W = 256 * kWavesPerWG * 2;
+  if (d) {
+    AttnPlanChoice c8 = c;
+    c8.kv8 = true;
+    W = std::max(worker_waves(d, c), worker_waves(d, c8));
+  }
   return attn_layout(shape->num_seqs, W, c.RG, c.D).total;
 }
 
@@ -279,7 +293,8 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
     }
     W = lo;
   }
-  W = (W / kWavesPerWG) * kWavesPerWG;
+  const int wg_waves = attn_wg_waves(c);
+  W = std::max(wg_waves, (W / wg_waves) * wg_waves);
   const AttnLayout lay = attn_layout(s.num_seqs, W, c.RG, c.D);
   char* ws = static_cast<char*>(workspace);
 
@@ -326,7 +341,7 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
     if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
   }
   const KTimer t = timer_slot(0);
-  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / kWavesPerWG, stream, t);
+  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / wg_waves, wg_waves, stream, t);
   timer_commit(0, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
   e = launch_attn_combine(P, c.D, stream);
@@ -467,7 +482,7 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   S.err = reinterpret_cast<int32_t*>(ws);
   // persistent statistics waves: kStatWavesPerCU per CU, no more than there are items
   const long long stat_waves = std::min(R * C1, (long long)d->num_cus * kStatWavesPerCU);
-  const int stat_wg = (int)((stat_waves + kWavesPerWG - 1) / kWavesPerWG);
+  const int stat_wg = (int)((stat_waves + kStatWavesPerWG - 1) / kStatWavesPerWG);
 
   // verification chunks: as spec_verify
   long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;

@@ -8,7 +8,7 @@ namespace vap {
 
 constexpr int kMaxSeqs = 8192;      // plan kernel keeps per-sequence work offsets in LDS
 constexpr int kPlanThreads = 1024;
-constexpr int kAttnThreads = 256;   // 4 independent worker waves per workgroup
+constexpr int kAttnThreads = 256;   // at most 4 independent worker waves per workgroup
 constexpr int kWavesPerWG = kAttnThreads / 64;
 
 
@@ -91,8 +91,8 @@ struct AttnParams {
 
 // launchers (attn_plan.hip, attn_paged.hip, attn_combine.hip); return hipError_t of the launch
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream,
-                            KTimer t = {});
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, int wg_waves,
+                            hipStream_t stream, KTimer t = {});
 hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);

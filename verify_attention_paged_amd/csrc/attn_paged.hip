@@ -25,8 +25,9 @@
 //    and batches averaging 48 or more rows per KV head such as token trees and prefill
 //    chunks).  Every K and V byte a unit needs is loaded once from HBM, straight into MFMA
 //    operand registers (16 bytes per lane per load), and serves all those rows.  A wave keeps
-//    two 16-token tiles in flight (a two-stage register pipeline); one wave per SIMD (two for
-//    prefill-heavy batches) already saturates the memory system for this access pattern.
+//    two 16-token tiles in flight (a two-stage register pipeline); three waves per CU (twice
+//    that for prefill-heavy batches) already saturate the memory system for this access
+//    pattern.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the K tile is
 //    the A operand (lane = token, 16 contiguous bytes per lane), the query rows the B operand.
 //    Each lane then holds one query row and four tokens, so a row's softmax statistics live
@@ -87,6 +88,7 @@ __device__ __forceinline__ void stage_fence() { __builtin_amdgcn_sched_barrier(0
 template <typename T>
 __device__ __forceinline__ T wg_exclusive_scan(T x, T* s_tmp, T& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;        // waves in this workgroup (at most kWavesPerWG)
   T incl = x;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -99,8 +101,10 @@ __device__ __forceinline__ T wg_exclusive_scan(T x, T* s_tmp, T& total) {
   total = 0;
 #pragma unroll
   for (int i = 0; i < kWavesPerWG; ++i) {
-    if (i < wv) before += s_tmp[i];
-    total += s_tmp[i];
+    if (i < nw) {
+      if (i < wv) before += s_tmp[i];
+      total += s_tmp[i];
+    }
   }
   __syncthreads();
   return before + incl - x;
@@ -115,7 +119,7 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
   long long carry_q = 0;
   int carry_w = 0;
   int err = 0;
-  for (int base = 0; base < P.B; base += kAttnThreads) {
+  for (int base = 0; base < P.B; base += (int)blockDim.x) {
     const int s = base + tid;
     int Q = 0, L = 0;
     if (s < P.B) {
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
   extern __shared__ int s_mem[];
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int w = uniform(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+  const int w = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
 
   // per-sequence tables: in this workgroup's LDS (ds_read, counted apart from the vector loads
   // in flight) or, for very large batches, in global memory written by the plan kernel
@@ -833,9 +837,9 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
 }
 
 template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
-hipError_t launch_main_t(const AttnParams& p, int num_wg, hipStream_t stream, KTimer t) {
+hipError_t launch_main_t(const AttnParams& p, int num_wg, int wg_waves, hipStream_t stream, KTimer t) {
   const size_t lds = LDS_PLAN ? attn_main_lds_bytes(p.B) : 0;
-  hipExtLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(kAttnThreads),
+  hipExtLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(64 * wg_waves),
                         (uint32_t)lds, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -848,16 +852,17 @@ size_t attn_main_lds_bytes(int B) { return size_t(4 * B + 1) * sizeof(int); }
   X(64, 16, 1) X(64, 16, 2) X(64, 16, 4) X(64, 32, 1) X(64, 32, 2) X(64, 32, 4) \
   X(128, 16, 1) X(128, 16, 2) X(128, 16, 4) X(128, 32, 1) X(128, 32, 2) X(128, 32, 4)
 
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, hipStream_t stream,
-                            KTimer t) {
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, int wg_waves,
+                            hipStream_t stream, KTimer t) {
+  if (wg_waves < 1 || wg_waves > kWavesPerWG) return hipErrorInvalidValue;
   const bool lds = p.B <= kLdsPlanMaxSeqs;
 #define X(d, bs, nrt)                                                                         \
   if (D == d && BS == bs && NRT == nrt) {                                                     \
     if (kv8)                                                                                  \
-      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, stream, t)                   \
-                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, stream, t);                 \
-    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, stream, t)                    \
-               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, stream, t);                  \
+      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, wg_waves, stream, t)                   \
+                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, wg_waves, stream, t);                 \
+    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, wg_waves, stream, t)                    \
+               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, wg_waves, stream, t);                  \
   }
   VAP_ATTN_VARIANTS(X)
 #undef X

@@ -70,6 +70,7 @@ constexpr int kStatMaxChunks = 512;     // V <= 2^20
 #define VAP_STAT_WAVES_PER_CU 8
 #endif
 constexpr int kStatWavesPerCU = VAP_STAT_WAVES_PER_CU;   // persistent statistics waves
+constexpr int kStatWavesPerWG = 4;                       // 256-thread statistics workgroups
 
 struct LogitsLayout {
   size_t part, chunk_sums, data_end, tickets, total;
