@@ -72,6 +72,10 @@ extern "C" {
                                    a tree of more than 64 rows (the row is then repaired: own
                                    bit set, later bits cleared; or kept causal)              */
 #define VAP_DERR_TEMP 0x40      /* temperature negative or not finite (the sequence is greedy)  */
+#define VAP_DERR_SYNC 0x80      /* spec_verify_tree: the workgroups sharing a sequence's walk did not
+                                   all run at once (the GPU was held by other work for a quarter
+                                   of a second); that sequence's outputs are unspecified and the
+                                   workspace must be zero-filled again before its next use      */
 
 /*
  * Shape of one attention step.
@@ -266,9 +270,13 @@ size_t vap_tree_verify_workspace_bytes(int32_t num_seqs);
  * it with p_cur = its target row.  With no child left, one token is drawn from p_cur (inverse
  * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
  * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
- * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk (one
- * workgroup per sequence), then the final draw spread over the GPU.  The workspace (zero-filled
- * before first use) serves spec_verify_tree calls only.
+ * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk, then
+ * the final draw spread over the GPU.  For vocabularies of 16384 or more, the walk runs up to 16
+ * workgroups per sequence (as many as keep the whole launch resident, one per CU) that share
+ * each residual pass and exchange partial sums through the workspace; if other work holds the
+ * GPU so long that they cannot all run, the wait ends after a quarter of a second with
+ * VAP_DERR_SYNC.
+ * The workspace (zero-filled before first use) serves spec_verify_tree calls only.
  */
 int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
                      const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,

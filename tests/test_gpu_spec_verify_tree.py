@@ -157,3 +157,26 @@ def test_monte_carlo_first_token_follows_the_root_target():
     exp = B * p_nodes[0].astype(np.float64) / p_nodes[0].sum()
     chi2 = float(((counts - exp) ** 2 / exp).sum())
     assert chi2 < stats.chi2.ppf(0.999, V - 1), f"chi2 {chi2}"
+
+
+def test_one_workspace_across_part_counts():
+    """Several workgroups per sequence share each residual pass (16 at B = 3, 4 at B = 64 on
+    this GPU, 1 for small vocabularies); their arrival counters must be back at zero for the
+    next call.  One workspace serves five calls of different shapes, each bit-exact, with no
+    device error (in particular no VAP_DERR_SYNC)."""
+    ws = vap.tree_verify_workspace(64, DEV)
+    shapes = [(3, 16, 50000, 31), (64, 8, 20000, 32), (3, 16, 50000, 33), (5, 12, 3001, 34), (16, 16, 32768, 35)]
+    for B, N, V, seed in shapes:
+        rng = np.random.default_rng(seed)
+        pl = 3.0 * rng.standard_normal((B, N, V))
+        ql = pl + 0.7 * rng.standard_normal((B, N, V))
+        soft = lambda z: np.exp(z - z.max(-1, keepdims=True)) / np.exp(z - z.max(-1, keepdims=True)).sum(-1, keepdims=True)
+        parents = np.stack([workloads.random_tree_parents(rng, N) for _ in range(B)])
+        tin = workloads.make_tree_verify_from_probs(seed, soft(pl).astype(np.float32), soft(ql).astype(np.float32),
+                                                    parents)
+        p, q, par, tok, u = _margin(tin, seed)
+        ref = OT.tree_verify(p, q, par, tok, u.astype(np.float64))
+        got = _gpu(p, q, par, tok, u, workspace=ws)
+        for name, a, b in zip(("ids", "path", "n_accepted"), got, ref):
+            assert np.array_equal(a, b), f"B={B} N={N} V={V}: {name} differ\n{a}\n{b}"
+        assert vap.get_device_error(ws) == 0, f"B={B} N={N} V={V}: device error"

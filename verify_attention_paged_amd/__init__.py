@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     DERR_EMPTY_ROW,
     DERR_TREE,
     DERR_TEMP,
+    DERR_SYNC,
     TIMER_ATTENTION,
     TIMER_VERIFY,
     TIMER_TREE_VERIFY,

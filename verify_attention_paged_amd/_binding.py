@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libv
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vap.h")
 
 VAP_OK, VAP_EINVAL, VAP_ENOSPC, VAP_EHIP, VAP_ENODEV = 0, -1, -2, -3, -4
-DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE, DERR_TEMP = (
-    0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40)
+DERR_BLOCK_ID, DERR_LENS, DERR_TOTAL_Q, DERR_DRAFT_ID, DERR_EMPTY_ROW, DERR_TREE, DERR_TEMP, DERR_SYNC = (
+    0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40, 0x80)
 TIMER_ATTENTION, TIMER_VERIFY, TIMER_TREE_VERIFY, TIMER_KV_APPEND, TIMER_KV_COMMIT = 0, 1, 2, 3, 4
 TIMER_LOGIT_STATS, TIMER_VERIFY_LOGITS, TIMER_TREE_DRAW = 5, 6, 7
 

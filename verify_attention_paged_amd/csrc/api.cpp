@@ -562,6 +562,12 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   P.err = reinterpret_cast<int32_t*>(ws);
   P.draws = reinterpret_cast<TreeDraw*>(ws + 256);
+  // Workgroups per sequence in the walk: as many as keep every workgroup of the launch resident
+  // at once (one per CU), at most kMaxTreeParts, and only for vocabularies large enough that a
+  // residual pass is worth splitting.
+  P.S = vocab >= 16384 ? std::max(1, std::min(kMaxTreeParts, d->num_cus / num_seqs)) : 1;
+  P.xch = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
+  P.xch_stride = kMaxChunks;
 
   // draw chunks: as spec_verify (about two workgroups per CU over the batch)
   long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
@@ -584,6 +590,7 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   D.CS = (int)CS;
   D.chunk_sums = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
   D.tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
+  P.tickets_end = D.tickets_end;
   D.err = P.err;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);

@@ -663,8 +663,9 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // the walk's parts arrived on this ticket first (d.arrivals times)
     const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (ticket == C - 1);
+    s_last = (ticket == d.arrivals + C - 1);
   }
   __syncthreads();
   if (!s_last) return;

@@ -108,9 +108,10 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------
-// Tree verification: one workgroup per sequence, no workspace beyond the error word.
+// Tree verification: S workgroups per sequence walk it in lockstep (S = 1 for large batches).
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxTreeNodes = 64;
+constexpr int kMaxTreeParts = 16;   // workgroups per sequence in the walk
 
 // Where the walk of one sequence ended: the final draw is from max(0, p - c q) of node `node`
 // (c = 0: p itself), or, if those weights are all zero, from max(0, p - c_prev q) (a walk that
@@ -121,14 +122,18 @@ struct TreeDraw {
   double c_prev;
   int32_t node;
   int32_t n;
-  int32_t pad[2];
+  int32_t arrivals; // the walk's arrivals on the sequence's ticket (S * passes when S > 1, else 0)
+  int32_t pad;
 };
 
 // ---------------------------------------------------------------------------------------
 // Tree verification workspace layout.
 //   [0, 256)                 header: err word
 //   [256, 256 + 32B)         TreeDraw [B], written by the walk, read by the draw kernel
-//   [256 + 32B, +2048B)      chunk_sums: double [B][kMaxChunks]
+//   [256 + 32B, +2048B)      chunk_sums: double [B][kMaxChunks]; during the walk, the first
+//                            2 * kMaxTreeParts of each sequence's row hold the parts' partial sums
+// A sequence's ticket first counts the walk's arrivals (its parts arrive once per residual
+// pass), then the draw kernel's chunks; the draw's last chunk resets it to 0.
 //   [..., end)               tickets: int32, sequence b at end - 4(b+1); they return to 0
 // Every call checks bytes >= 256 + 2084 B, so a call's tickets never overlap data an earlier
 // call (any B) left behind (the same argument as for the verification workspace).
@@ -148,6 +153,10 @@ struct TreeVerifyParams {
   bool vec4;                // V % 4 == 0 and p, q 16-byte aligned
   int32_t* err;
   TreeDraw* draws;          // [B], written at the end of the walk
+  int32_t S;                // workgroups per sequence (1 .. kMaxTreeParts)
+  double* xch;              // partial-sum slots: sequence b at xch + b * xch_stride, [2][S]
+  int32_t xch_stride;
+  int32_t* tickets_end;     // sequence b's ticket is tickets_end[-(b + 1)] (zero at the start of a call)
 };
 
 struct TreeDrawParams {
