@@ -588,10 +588,13 @@ def run_default(args, dev):
                                "block 16, ctx lognormal(1024, 1) in [16, 8192], pool 1.2x live blocks",
                    "tokens": int(inp.ctx_lens.sum()), "bytes_per_step": nbytes, "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s_per_layer": round(inp.num_seqs / (ms * 1e-3), 1),
         "verified_tokens_per_s": round(verify_tok_s, 1),
         "verify_step": {"workload": "spec_verify_step: 16 seqs, q_len 5, 32/8 heads, head_dim 128, ctx "
                                     "uniform [512, 4096]; spec_verify vocab 128256, k 4",
                         "ms_per_step": round(vms, 5), "tokens_emitted": emitted,
+                        "acceptance_rate": round(float(n_host.sum()) / (ver.k * ver.num_seqs), 4),
+                        "sampler_tokens_per_s": round(emitted / (sv_kernel_ms * 1e-3), 1),
                         "attention_kernel_ms": round(vattn_ms / max(1, c0), 5),
                         "attention_GB_per_s": round(vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9, 2),
                         "spec_verify_kernel_ms": round(sv_kernel_ms, 5),
