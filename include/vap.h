@@ -271,9 +271,9 @@ size_t vap_tree_verify_workspace_bytes(int32_t num_seqs);
  * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
  * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
  * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk, then
- * the final draw spread over the GPU.  For vocabularies of 16384 or more, the walk runs up to 16
- * workgroups per sequence (as many as keep the whole launch resident, one per CU) that share
- * each residual pass and exchange partial sums through the workspace; if other work holds the
+ * the final draw spread over the GPU.  For vocabularies above 32768, the walk runs up to 16
+ * workgroups per sequence (one per 32768 tokens, no more than keep the whole launch resident, one
+ * per CU) that share each residual pass and exchange partial sums through the workspace; if other work holds the
  * GPU so long that they cannot all run, the wait ends after a quarter of a second with
  * VAP_DERR_SYNC.
  * The workspace (zero-filled before first use) serves spec_verify_tree calls only.

@@ -160,12 +160,12 @@ def test_monte_carlo_first_token_follows_the_root_target():
 
 
 def test_one_workspace_across_part_counts():
-    """Several workgroups per sequence share each residual pass (16 at B = 3, 4 at B = 64 on
-    this GPU, 1 for small vocabularies); their arrival counters must be back at zero for the
-    next call.  One workspace serves five calls of different shapes, each bit-exact, with no
-    device error (in particular no VAP_DERR_SYNC)."""
+    """Several workgroups per sequence share each residual pass (one per 32768 tokens: 10 at
+    V = 300000, 5 at V = 140000, 1 for small vocabularies); the arrival counts on each
+    sequence's ticket must be back at zero for the next call.  One workspace serves five calls
+    of different shapes, each bit-exact, with no device error (in particular no VAP_DERR_SYNC)."""
     ws = vap.tree_verify_workspace(64, DEV)
-    shapes = [(3, 16, 50000, 31), (64, 8, 20000, 32), (3, 16, 50000, 33), (5, 12, 3001, 34), (16, 16, 32768, 35)]
+    shapes = [(3, 16, 300000, 31), (32, 8, 140000, 32), (3, 16, 300000, 33), (5, 12, 3001, 34), (16, 16, 32768, 35)]
     for B, N, V, seed in shapes:
         rng = np.random.default_rng(seed)
         pl = 3.0 * rng.standard_normal((B, N, V))

@@ -562,10 +562,13 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   P.err = reinterpret_cast<int32_t*>(ws);
   P.draws = reinterpret_cast<TreeDraw*>(ws + 256);
-  // Workgroups per sequence in the walk: as many as keep every workgroup of the launch resident
-  // at once (one per CU), at most kMaxTreeParts, and only for vocabularies large enough that a
-  // residual pass is worth splitting.
-  P.S = vocab >= 16384 ? std::max(1, std::min(kMaxTreeParts, d->num_cus / num_seqs)) : 1;
+  // Workgroups per sequence in the walk: the fewest that give each one a single load round of a
+  // residual pass (more parts only add arrivals to wait for: at V = 128256, 4 parts walked in
+  // 21.8 us against 23.5 with 8, 27 with 16 and 27.4 with 3, which needs a second round),
+  // bounded by kMaxTreeParts and by keeping every workgroup of the launch resident at once (one
+  // per CU).
+  const int parts = (int)(((long long)vocab + kTreeRoundTokens - 1) / kTreeRoundTokens);
+  P.S = std::max(1, std::min({parts, kMaxTreeParts, d->num_cus / num_seqs}));
   P.xch = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
   P.xch_stride = kMaxChunks;
 

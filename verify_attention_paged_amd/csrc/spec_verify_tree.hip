@@ -37,6 +37,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kMaxNodes = 64;
 constexpr int kIt = 8;     // float4 pairs per thread in flight per round of a residual pass
+static_assert(4 * kIt * kThreads == kTreeRoundTokens, "the host sizes walk parts by this round");
 
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll

@@ -112,6 +112,7 @@ hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStre
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxTreeNodes = 64;
 constexpr int kMaxTreeParts = 16;   // workgroups per sequence in the walk
+constexpr int kTreeRoundTokens = 4 * 8 * 1024;   // tokens one walk workgroup loads per round of a pass
 
 // Where the walk of one sequence ended: the final draw is from max(0, p - c q) of node `node`
 // (c = 0: p itself), or, if those weights are all zero, from max(0, p - c_prev q) (a walk that
