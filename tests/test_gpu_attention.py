@@ -190,6 +190,27 @@ def test_split_partition_invariance(ws_kind):
     H.assert_close_rows(out, H.oracle_rows(inp), f"split {ws_kind}")
 
 
+def test_one_workspace_across_calls_and_shapes():
+    """Each call leaves the workspace ready for the next: repeated calls, and calls of other
+    shapes, on one workspace give bitwise the results of calls on fresh workspaces."""
+    import ctypes
+    cases = {"decode": H.config_inputs("llama3_8b_decode"),
+             "small": _case(21, [4096, 17, 1500, 33, 800, 2], [1, 5, 1, 2, 5, 1], 32, 8, 128, 16),
+             "mixed": H.config_inputs("mixed_step")}
+    lib = vap.load_library()
+    nbytes = max(lib.vap_attn_workspace_bytes(ctypes.byref(vap.attn_shape(i.q, i.kv_pool, i.block_tables)))
+                 for i in cases.values())
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=H.device())
+    ref = {}
+    for name, inp in cases.items():
+        ref[name], _ = _run(inp)
+    for name in ["decode", "small", "decode", "mixed", "decode", "small", "mixed"]:
+        print("shared workspace:", name, flush=True)
+        out, _ = _run(cases[name], workspace=ws)
+        assert torch.equal(out, ref[name]), name
+    assert vap.get_device_error(ws) == 0
+
+
 def test_explicit_scale():
     inp = _case(10, [50, 200], [5, 1], 8, 2, 64, 16)
     out, _ = _run(inp, scale=0.3)

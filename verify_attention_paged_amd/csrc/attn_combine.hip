@@ -11,7 +11,7 @@
 // Layout of the work (the step is latency-bound: every partial was written by the previous
 // kernel, so each dependent round trip to L2/MALL costs more than the bytes):
 //  * one workgroup (NW = 2 waves for 16-row units, 8 for 32-row and 16 for 64-row units) per
-//    descriptor; wave w's descriptor is valid when w holds the
+//    K consecutive descriptors, loaded together; wave w's descriptor is valid when w holds the
 //    first block of a split unit, and then names the last wave wb holding part of it;
 //  * 16 lanes per row, each lane D/16 consecutive dims (float4 loads), so a wave covers a
 //    quad of 4 rows;
@@ -19,6 +19,8 @@
 //    quads (wave, wave + NW, ...); with nq < NW the partial list is split too: S = NW / nq
 //    waves per quad take partials p, p+S, p+2S, ... and merge in LDS in wave order;
 //  * up to kBatch partials are loaded before any is folded (one round trip per batch).
+#include <algorithm>
+
 #include "attn_internal.h"
 
 namespace vap {
@@ -48,23 +50,14 @@ __device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const f
 }
 
 // NW waves per workgroup: 2 for 16-row units, 8 for 32-row units, 16 for 64-row units (16 quads).
+// Merge the split unit that wave w's descriptor (d0, d1) opens; every wave of the workgroup
+// calls it with the same descriptor.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P) {
+__device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0, int4 d1,
+                                             float (&s_ml)[NW][64][2], float4 (&s_acc)[NW][D / 64][64]) {
   constexpr int kCombineWaves = NW;
   constexpr int DPL = D / 16;   // dims per lane
   constexpr int NV4 = DPL / 4;  // float4 loads per lane and partial
-  __shared__ float s_ml[kCombineWaves][64][2];
-  __shared__ float4 s_acc[kCombineWaves][NV4][64];
-
-  // every worker wave w < W writes its descriptor on every call (zeroed when it has no split
-  // unit to open, including the waves past the step's work), so no other check is needed
-  const int w = blockIdx.x;
-  const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * w;
-  const int4 d1 = dp[1];
-  const int4 d0 = dp[0];
-  // whole workgroup leaves: no barrier is pending.  (kvh = d0.x is never negative; testing it
-  // keeps the loads of both descriptor halves ahead of the branch, one round trip instead of two)
-  if (d1.z == 0 || d0.x < 0) return;
   const int kvh = d0.x, rg = d0.y, qoff = d0.z, Q = d0.w;
   const int wb = d1.x, slot_a = d1.y;
   const int G = P.G, RG = P.RG;
@@ -132,6 +125,7 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
   }
 
   // fewer quads than waves: S waves per quad split its partials and merge in LDS in wave order
+  __syncthreads();                        // the previous unit's LDS reads are done
   const int quad = wave % nq;
   const int sub = wave / nq;
   const int r_raw = 4 * quad + (lane >> 4);
@@ -149,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
   for (int t = 0; t < NV4; ++t)
     s_acc[wave][t][lane] = make_float4(st.a[4 * t], st.a[4 * t + 1], st.a[4 * t + 2], st.a[4 * t + 3]);
   __syncthreads();
-  if (sub != 0) return;
+  if (sub != 0) return;                   // (no barrier follows within this unit)
   for (int t2 = 1; t2 < S; ++t2) {
     const int ow = quad + t2 * nq;
     float v[DPL];
@@ -166,22 +160,53 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
   write_row(st, r_raw);
 }
 
+// One workgroup per K consecutive descriptors (K chosen so that the whole grid is resident
+// at once): lanes 0 .. K-1 load them in one round trip, then the workgroup merges the units
+// that valid ones open, in order.  Every worker wave w < W writes its descriptor on every call
+// (zeroed when it opens no split unit, including the waves past the step's work), so no other
+// check is needed.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P, int K) {
+  __shared__ float s_ml[NW][64][2];
+  __shared__ float4 s_acc[NW][D / 64][64];
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * K;
+  const int nd = min(K, P.W - w0);
+  int4 e0 = make_int4(0, 0, 0, 0), e1 = make_int4(0, 0, 0, 0);
+  if (lane < nd) {
+    const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * (w0 + lane);
+    e0 = dp[0];
+    e1 = dp[1];
+  }
+  for (int i = 0; i < nd; ++i) {
+    if (__builtin_amdgcn_readlane(e1.z, i) == 0) continue;
+    const int4 d0 = make_int4(__builtin_amdgcn_readlane(e0.x, i), __builtin_amdgcn_readlane(e0.y, i),
+                              __builtin_amdgcn_readlane(e0.z, i), __builtin_amdgcn_readlane(e0.w, i));
+    const int4 d1 = make_int4(__builtin_amdgcn_readlane(e1.x, i), __builtin_amdgcn_readlane(e1.y, i), 1, 0);
+    combine_unit<D, NW>(P, w0 + i, d0, d1, s_ml, s_acc);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream) {
+hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStream_t stream) {
   // waves per workgroup: 2 for 16-row units (decode), 8 for 32-row units, 16 for 64-row units.
-  // Most workgroups read an empty descriptor and leave; for decode batches the smaller
-  // workgroups measured faster (less to dispatch, and four quads need no more waves).
+  // Most descriptors are empty; for decode batches the smaller workgroups measured faster
+  // (less to dispatch, and four quads need no more waves).  K descriptors per workgroup keep
+  // the grid within one residency round at 16 waves per CU (the D = 128 kernel's register
+  // budget allows 4 waves per SIMD), so no workgroup waits for another to leave.
   const int nw = p.RG > 32 ? 16 : (p.RG > 16 ? 8 : 2);
-  const dim3 grid((unsigned)p.W), block(64 * nw);
+  const long long resident = (long long)std::max(1, num_cus) * 16;
+  const int K = (int)std::min<long long>(64, std::max<long long>(1, ((long long)p.W * nw + resident - 1) / resident));
+  const dim3 grid((unsigned)((p.W + K - 1) / K)), block(64 * nw);
   if (D == 64) {
-    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p);
-    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, 2>), grid, block, 0, stream, p);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p, K);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p, K);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, 2>), grid, block, 0, stream, p, K);
   } else if (D == 128) {
-    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p);
-    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_combine_kernel<128, 2>), grid, block, 0, stream, p);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p, K);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p, K);
+    else hipLaunchKernelGGL((attn_combine_kernel<128, 2>), grid, block, 0, stream, p, K);
   } else {
     return hipErrorInvalidValue;
   }

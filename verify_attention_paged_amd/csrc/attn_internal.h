@@ -93,7 +93,7 @@ struct AttnParams {
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, int wg_waves,
                             hipStream_t stream, KTimer t = {});
-hipError_t launch_attn_combine(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);
 
