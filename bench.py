@@ -218,12 +218,15 @@ def time_loop(fn, steps, warmup):
     return e0.elapsed_time(e1) / max(steps, 1), wall
 
 
-def graph_loop(step, variants, steps, warmup):
+def graph_loop(step, variants, steps, warmup, skip=False):
     """Milliseconds per step when each step is one HIP graph replay: step(j) is captured once
     for each of the `variants` rotating input copies (kernel timers off, after one eager call
     of each on a side stream) and step i replays graph i % variants.  Nothing in a step
-    allocates or clears memory with memset nodes, so replays do exactly the eager work."""
+    allocates or clears memory with memset nodes, so replays do exactly the eager work.  None
+    when `skip`."""
     import torch
+    if skip:
+        return None
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -392,13 +395,13 @@ def run_default(args, dev):
         raise RuntimeError("device reported a data error on the decode batch")
     kernel_ms = kms_total / max(1, kcount)
     vap.timer_enable(False)
-    gms = graph_loop(step, len(pools), args.steps, args.warmup)
+    gms = graph_loop(step, len(pools), args.steps, args.warmup, args.no_graphs)
     vap.timer_enable(True)
     value = nbytes / (ms * 1e-3) / 1e9
     kernel_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     log(f"decode step {ms * 1e3:.1f} us -> {value:.1f} GB/s; attention kernel {kernel_ms * 1e3:.1f} us "
-        f"-> {kernel_gbs:.1f} GB/s ({wall:.2f} s wall for {args.steps} steps); as HIP graph replays "
-        f"{gms * 1e3:.1f} us -> {nbytes / (gms * 1e-3) / 1e9:.1f} GB/s")
+        f"-> {kernel_gbs:.1f} GB/s ({wall:.2f} s wall for {args.steps} steps)"
+        + (f"; as HIP graph replays {gms * 1e3:.1f} us -> {nbytes / (gms * 1e-3) / 1e9:.1f} GB/s" if gms else ""))
 
     # ---- speculative verify step: attention (q_len 5) + spec_verify (vocab 128256)
     vinp, vd, vpools, vout, vws, vnbytes = setup_attention("spec_verify_step", dev)
@@ -423,13 +426,14 @@ def run_default(args, dev):
     vattn_ms, c0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     sv_ms, c1 = vap.timer_read(vap.TIMER_VERIFY, reset=True)
     vap.timer_enable(False)
-    vgms = graph_loop(vstep, max(len(vpools), len(ps)), args.steps, args.warmup)
+    vgms = graph_loop(vstep, max(len(vpools), len(ps)), args.steps, args.warmup, args.no_graphs)
     n_host = n_acc.cpu().numpy()
     emitted = int((n_host + 1).sum())
     sv_bytes = verify_bytes(n_host, ver.k, ver.vocab)
     sv_kernel_ms = sv_ms / max(1, c1)
     verify_tok_s = emitted / (vms * 1e-3)
-    log(f"verify step {vms * 1e3:.1f} us, as HIP graph replays {vgms * 1e3:.1f} us ({emitted} tokens emitted, acceptance "
+    log(f"verify step {vms * 1e3:.1f} us" + (f", as HIP graph replays {vgms * 1e3:.1f} us" if vgms else "") +
+        f" ({emitted} tokens emitted, acceptance "
         f"{float(n_host.sum()) / (ver.k * ver.num_seqs):.3f}); spec_verify kernel {sv_kernel_ms * 1e3:.2f} us "
         f"-> {sv_bytes / (sv_kernel_ms * 1e-3) / 1e9:.1f} GB/s; verify attention kernel "
         f"{vattn_ms / max(1, c0) * 1e3:.1f} us -> {vnbytes / (vattn_ms / max(1, c0) * 1e-3) / 1e9:.1f} GB/s")
@@ -462,7 +466,7 @@ def run_default(args, dev):
     tsv_ms, tc1 = vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
     tdr_ms, tc2 = vap.timer_read(vap.TIMER_TREE_DRAW, reset=True)
     vap.timer_enable(False)
-    tgms = graph_loop(tstep, max(len(tpools), len(tps)), args.steps, args.warmup)
+    tgms = graph_loop(tstep, max(len(tpools), len(tps)), args.steps, args.warmup, args.no_graphs)
     tn_host = t_n.cpu().numpy()
     t_emitted = int((tn_host + 1).sum())
     tsv_bytes = tree_verify_bytes(tver.parents.numpy(), t_path.cpu().numpy(), tn_host, tver.vocab)
@@ -470,7 +474,8 @@ def run_default(args, dev):
     tsv_draw_ms = tdr_ms / max(1, tc2)
     tsv_kernel_ms = tsv_walk_ms + tsv_draw_ms
     tree_tok_s = t_emitted / (tms * 1e-3)
-    log(f"tree verify step {tms * 1e3:.1f} us, as HIP graph replays {tgms * 1e3:.1f} us ({t_emitted} tokens emitted, {tn_host.mean():.2f} accepted per "
+    log(f"tree verify step {tms * 1e3:.1f} us" + (f", as HIP graph replays {tgms * 1e3:.1f} us" if tgms else "") +
+        f" ({t_emitted} tokens emitted, {tn_host.mean():.2f} accepted per "
         f"sequence); tree attention kernel {tattn_ms / max(1, tc0) * 1e3:.1f} us; spec_verify_tree walk "
         f"{tsv_walk_ms * 1e3:.1f} us + draw {tsv_draw_ms * 1e3:.1f} us -> "
         f"{tsv_bytes / (tsv_kernel_ms * 1e-3) / 1e9:.1f} GB/s")
@@ -611,7 +616,7 @@ def run_default(args, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "graph_ms_per_step": round(gms, 5),
+        "graph_ms_per_step": round(gms, 5) if gms else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -623,10 +628,10 @@ def run_default(args, dev):
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(inp.num_seqs / (ms * 1e-3), 1),
         "verified_tokens_per_s": round(verify_tok_s, 1),
-        "verified_tokens_per_s_graph": round(emitted / (vgms * 1e-3), 1),
+        "verified_tokens_per_s_graph": round(emitted / (vgms * 1e-3), 1) if vgms else None,
         "verify_step": {"workload": "spec_verify_step: 16 seqs, q_len 5, 32/8 heads, head_dim 128, ctx "
                                     "uniform [512, 4096]; spec_verify vocab 128256, k 4",
-                        "ms_per_step": round(vms, 5), "graph_ms_per_step": round(vgms, 5),
+                        "ms_per_step": round(vms, 5), "graph_ms_per_step": round(vgms, 5) if vgms else None,
                         "tokens_emitted": emitted,
                         "acceptance_rate": round(float(n_host.sum()) / (ver.k * ver.num_seqs), 4),
                         "sampler_tokens_per_s": round(emitted / (sv_kernel_ms * 1e-3), 1),
@@ -638,11 +643,11 @@ def run_default(args, dev):
         "tree_verify_step": {"workload": "tree_verify_step: 16 seqs verifying 16-node random token trees "
                                          "(tree-masked attention, 32/8 heads, head_dim 128, ctx uniform "
                                          "[512, 4096]) then spec_verify_tree over vocab 128256",
-                             "ms_per_step": round(tms, 5), "graph_ms_per_step": round(tgms, 5),
+                             "ms_per_step": round(tms, 5), "graph_ms_per_step": round(tgms, 5) if tgms else None,
                              "tokens_emitted": t_emitted,
                              "mean_accepted": round(float(tn_host.mean()), 3),
                              "verified_tokens_per_s": round(tree_tok_s, 1),
-                             "verified_tokens_per_s_graph": round(t_emitted / (tgms * 1e-3), 1),
+                             "verified_tokens_per_s_graph": round(t_emitted / (tgms * 1e-3), 1) if tgms else None,
                              "attention_kernel_ms": round(tattn_ms / max(1, tc0), 5),
                              "spec_verify_tree_kernel_ms": round(tsv_kernel_ms, 5),
                              "spec_verify_tree_walk_ms": round(tsv_walk_ms, 5),
@@ -675,6 +680,7 @@ def main():
     ap.add_argument("--kv-format", choices=["bf16", "u8"], default="bf16", help="KV cache format (attn-only mode)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true", help="skip the HIP graph timings (eager steps only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
