@@ -49,9 +49,9 @@ __device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const f
   s.M = Mn;
 }
 
-// NW waves per workgroup: 2 for 16-row units, 8 for 32-row units, 16 for 64-row units (16 quads).
 // Merge the split unit that wave w's descriptor (d0, d1) opens; every wave of the workgroup
-// calls it with the same descriptor.
+// calls it with the same descriptor.  NW waves per workgroup: 2 for 16-row units, 8 for
+// 32-row units, 16 for 64-row units (16 quads).
 template <int D, int NW>
 __device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0, int4 d1,
                                              float (&s_ml)[NW][64][2], float4 (&s_acc)[NW][D / 64][64]) {
