@@ -195,6 +195,25 @@ int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   return std::min(kMaxWaves, d->num_cus * std::min(occ, per_cu) * attn_wg_waves(c));
 }
 
+// Pool of the attention step: the last VAP_POOL_PCT percent of the work, in pieces of
+// VAP_POOL_PIECE work blocks, is left out of the worker waves' static shares; waves that
+// finish their share early take the pieces one at a time, so slow waves end sooner.  At most
+// one piece per two worker waves.  The kernel uses it for bf16 steps of 16-row units with at
+// least 32 work blocks per wave: with fewer blocks per wave, with the 8-bit cache's cheaper
+// blocks, or with 32- and 64-row units (whose restart loads more query rows and leaves a
+// larger partial to merge), a piece's restart cost as much as the balance gained or more.
+#ifndef VAP_POOL_PCT
+#define VAP_POOL_PCT 10
+#endif
+#ifndef VAP_POOL_PIECE
+#define VAP_POOL_PIECE 12
+#endif
+int pool_max(int W) { return VAP_POOL_PCT > 0 ? W / 2 : 0; }
+
+AttnLayout layout_of(int B, int W, const AttnPlanChoice& c) {
+  return attn_layout(B, W, c.RG, c.D, W + pool_max(W));
+}
+
 // Shape and pointer checks shared by kv_append and kv_commit.
 int check_kv_call(const vap_attn_shape* shape, const void* kv, const float* kv_scales, const void* workspace,
                   size_t workspace_bytes) {
@@ -246,13 +265,13 @@ size_t vap_attn_workspace_bytes(const vap_attn_shape* shape) {
     c8.kv8 = true;
     W = std::max(worker_waves(d, c), worker_waves(d, c8));
   }
-  return attn_layout(shape->num_seqs, W, c.RG, c.D).total;
+  return layout_of(shape->num_seqs, W, c).total;
 }
 
 size_t vap_attn_workspace_min_bytes(const vap_attn_shape* shape) {
   AttnPlanChoice c;
   if (check_attn_shape(shape, &c) != VAP_OK) return 0;
-  return attn_layout(shape->num_seqs, kWavesPerWG, c.RG, c.D).total;
+  return layout_of(shape->num_seqs, kWavesPerWG, c).total;
 }
 
 }  // extern "C"
@@ -282,20 +301,20 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
 
   // worker waves: as many as stay resident, fewer if the workspace is smaller
   int W = worker_waves(d, c);
-  if (attn_layout(s.num_seqs, W, c.RG, c.D).total > workspace_bytes) {
+  if (layout_of(s.num_seqs, W, c).total > workspace_bytes) {
     int lo = kWavesPerWG, hi = W;
-    if (attn_layout(s.num_seqs, lo, c.RG, c.D).total > workspace_bytes)
+    if (layout_of(s.num_seqs, lo, c).total > workspace_bytes)
       return fail(VAP_ENOSPC, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
-                  attn_layout(s.num_seqs, lo, c.RG, c.D).total);
+                  layout_of(s.num_seqs, lo, c).total);
     while (lo < hi) {
       const int mid = (lo + hi + 1) / 2;
-      if (attn_layout(s.num_seqs, mid, c.RG, c.D).total <= workspace_bytes) lo = mid; else hi = mid - 1;
+      if (layout_of(s.num_seqs, mid, c).total <= workspace_bytes) lo = mid; else hi = mid - 1;
     }
     W = lo;
   }
   const int wg_waves = attn_wg_waves(c);
   W = std::max(wg_waves, (W / wg_waves) * wg_waves);
-  const AttnLayout lay = attn_layout(s.num_seqs, W, c.RG, c.D);
+  const AttnLayout lay = layout_of(s.num_seqs, W, c);
   char* ws = static_cast<char*>(workspace);
 
   AttnParams P;
@@ -322,6 +341,10 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
   P.RG = c.RG;
   P.BS = c.BS;
   P.UH = unit_setup_blocks(c.BS, c.NRT, kv8);
+  P.pool_max = pool_max(W);
+  P.NH = W + P.pool_max;
+  P.pool_pct = VAP_POOL_PCT;
+  P.pool_piece = VAP_POOL_PIECE;
   const float scale = s.scale > 0.f ? s.scale : 1.0f / std::sqrt((float)s.head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.hdr = reinterpret_cast<AttnHeader*>(ws);

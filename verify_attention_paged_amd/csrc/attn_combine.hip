@@ -11,8 +11,9 @@
 // Layout of the work (the step is latency-bound: every partial was written by the previous
 // kernel, so each dependent round trip to L2/MALL costs more than the bytes):
 //  * one workgroup (NW = 2 waves for 16-row units, 8 for 32-row and 16 for 64-row units) per
-//    K consecutive descriptors, loaded together; wave w's descriptor is valid when w holds the
-//    first block of a split unit, and then names the last wave wb holding part of it;
+//    K consecutive descriptors, loaded together; holder w's descriptor (a worker wave's share
+//    or a pool piece) is valid when w holds the first block of a split unit, and then names
+//    the last holder wb of part of it (holders are numbered in work order);
 //  * 16 lanes per row, each lane D/16 consecutive dims (float4 loads), so a wave covers a
 //    quad of 4 rows;
 //  * nq = ceil(rows/4) quads (up to 16 for 64-row units); with nq >= NW each wave merges whole
@@ -49,7 +50,7 @@ __device__ __forceinline__ void fold(RowState<DPL>& s, float m, float l, const f
   s.M = Mn;
 }
 
-// Merge the split unit that wave w's descriptor (d0, d1) opens; every wave of the workgroup
+// Merge the split unit that holder w's descriptor (d0, d1) opens; every wave of the workgroup
 // calls it with the same descriptor.  NW waves per workgroup: 2 for 16-row units, 8 for
 // 32-row units, 16 for 64-row units (16 quads).
 template <int D, int NW>
@@ -62,7 +63,7 @@ __device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0
   const int wb = d1.x, slot_a = d1.y;
   const int G = P.G, RG = P.RG;
   const int nrows = min(RG, G * Q - rg * RG);
-  const int n = wb - w + 1;              // partials of this unit, in wave order
+  const int n = wb - w + 1;              // partials of this unit, in holder (work) order
   const int nq = (nrows + 3) >> 2;
   const int S = nq >= kCombineWaves ? 1 : kCombineWaves / nq;
 
@@ -162,16 +163,18 @@ __device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0
 
 // One workgroup per K consecutive descriptors (K chosen so that the whole grid is resident
 // at once): lanes 0 .. K-1 load them in one round trip, then the workgroup merges the units
-// that valid ones open, in order.  Every worker wave w < W writes its descriptor on every call
-// (zeroed when it opens no split unit, including the waves past the step's work), so no other
-// check is needed.
+// that valid ones open, in order.  Every holder's descriptor (worker waves' shares, then pool
+// pieces) is written on every call, zeroed when it opens no split unit (including the waves
+// past the step's work and the pool pieces the step does not use), so no other check is
+// needed.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P, int K) {
   __shared__ float s_ml[NW][64][2];
   __shared__ float4 s_acc[NW][D / 64][64];
   const int lane = threadIdx.x & 63;
   const int w0 = blockIdx.x * K;
-  const int nd = min(K, P.W - w0);
+  const int nd = min(K, P.NH - w0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) P.hdr->pool_next = 0;   // the next step starts with a full pool
   int4 e0 = make_int4(0, 0, 0, 0), e1 = make_int4(0, 0, 0, 0);
   if (lane < nd) {
     const int4* dp = reinterpret_cast<const int4*>(P.desc) + 2 * (w0 + lane);
@@ -194,11 +197,12 @@ hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStrea
   // Most descriptors are empty; for decode batches the smaller workgroups measured faster
   // (less to dispatch, and four quads need no more waves).  K descriptors per workgroup keep
   // the grid within one residency round at 16 waves per CU (the D = 128 kernel's register
-  // budget allows 4 waves per SIMD), so no workgroup waits for another to leave.
+  // budget allows 4 waves per SIMD), so no workgroup waits for another to leave; two-wave
+  // workgroups take at least 2 (fewer workgroups to dispatch measured slightly faster).
   const int nw = p.RG > 32 ? 16 : (p.RG > 16 ? 8 : 2);
   const long long resident = (long long)std::max(1, num_cus) * 16;
-  const int K = (int)std::min<long long>(64, std::max<long long>(1, ((long long)p.W * nw + resident - 1) / resident));
-  const dim3 grid((unsigned)((p.W + K - 1) / K)), block(64 * nw);
+  const int K = (int)std::min<long long>(64, std::max<long long>(nw == 2 ? 2 : 1, ((long long)p.NH * nw + resident - 1) / resident));
+  const dim3 grid((unsigned)((p.NH + K - 1) / K)), block(64 * nw);
   if (D == 64) {
     if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p, K);
     else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p, K);

@@ -557,7 +557,7 @@ __device__ __forceinline__ void unit_rows(const AttnParams& P, int kvh, int rg, 
 }
 
 template <int D, int BS, int NRT, bool KV8, bool ONCE>
-__device__ void process_segment(const AttnParams& P, const Segment& sg, int w, int W, int TB,
+__device__ void process_segment(const AttnParams& P, const Segment& sg, int h, int W, int T1, int PS,
                                 int lane, int c, int g, SplitDesc& desc) {
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
@@ -729,7 +729,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
   for (int rt = 0; rt < NRT; ++rt) {
     const int r_in_unit = rt * 16 + c;
     if (r_in_unit < nrows) {
-      const long long prow = ((long long)w * 2 + sg.slot) * RG + r_in_unit;
+      const long long prow = ((long long)h * 2 + sg.slot) * RG + r_in_unit;
       float* pp = P.part_acc + prow * D + (D / 4) * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -742,13 +742,14 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int w, i
     }
   }
   if (sg.ub == 0) {
-    // this wave opens the unit: waves w .. wb hold its segments, this one in slot sg.slot
+    // this holder opens the unit: holders h .. wb hold its segments, this one in slot sg.slot;
+    // wb holds the unit's last block x = U1 - 1 (a wave's share below T1, a pool piece above)
     const long long U1 = (long long)sg.soff + (long long)(sg.unit + 1) * (P.UH + sg.nb);
     desc.kvh = sg.kvh;
     desc.rg = sg.rg;
     desc.qoff = sg.qoff;
     desc.Q = sg.Q;
-    desc.wb = (int)((U1 * W - 1) / TB);
+    desc.wb = (U1 <= T1) ? (int)((U1 * W - 1) / T1) : W + (int)((U1 - 1 - T1) / PS);
     desc.slot_a = sg.slot;
     desc.valid = 1;
   }
@@ -772,67 +773,91 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
   const int TB = uniform(plan_off(P.B));
   const int W = min(P.W, TB);
   if (LDS_PLAN && blockIdx.x == 0 && threadIdx.x == 0) P.hdr->total_work = TB;
+  // Pool: the last NP pieces of PS work blocks, for bf16 steps of 16-row units with at least
+  // 32 work blocks per wave (then W = P.W and the pool holders W .. W+NP-1 follow the last
+  // share's holder directly)
+  const int PS = max(1, P.pool_piece);
+  int NP = 0;
+  if (LDS_PLAN && !KV8 && NRT == 1 && P.pool_max > 0 && TB >= 32 * P.W)
+    NP = min(P.pool_max, (int)((long long)TB * P.pool_pct / 100) / PS);
+  const int T1 = TB - NP * PS;
+  // descriptors of the pool holders this step leaves unused (every holder's is written)
+  for (int hh = P.W + NP + w; hh < P.NH; hh += P.W)
+    if (lane == 0) reinterpret_cast<int4*>(P.desc)[2 * hh + 1] = make_int4(0, 0, 0, 0);
   if (w >= W) {                          // no workgroup barrier below this point
     if (lane == 0) reinterpret_cast<int4*>(P.desc)[2 * w + 1] = make_int4(0, 0, 0, 0);
     return;
   }
-  const long long b0 = (long long)w * TB / W;
-  const long long b1 = (long long)(w + 1) * TB / W;
 
-  int s;
-  if constexpr (LDS_PLAN) {
-    int lo = 0, hi = P.B;                // largest s with off[s] <= b0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (plan_off(mid) <= b0) lo = mid; else hi = mid - 1;
+  // This wave's own share (holder w), then pool pieces (holder W + k) while any are left: one
+  // range per pass, so the segment code is instantiated once.
+  int h = w;
+  long long b0 = (long long)w * T1 / W;
+  long long b1 = (long long)(w + 1) * T1 / W;
+  while (true) {
+    int s;
+    if constexpr (LDS_PLAN) {
+      int lo = 0, hi = P.B;              // largest s with off[s] <= b0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (plan_off(mid) <= b0) lo = mid; else hi = mid - 1;
+      }
+      s = uniform(lo);
+    } else {
+      s = uniform(P.wave_seq[w]);        // (no pool on this path: b0 is this wave's share)
     }
-    s = uniform(lo);
-  } else {
-    s = uniform(P.wave_seq[w]);
-  }
 
-  SplitDesc desc = {0, 0, 0, 0, 0, 0, 0, 0};
-  int pos = (int)b0;
-  bool first = true;
-  while (pos < b1) {
-    const int soff = uniform(plan_off(s));
-    const int send = uniform(plan_off(s + 1));
-    if (pos >= send) { ++s; continue; }
-    Segment sg;
-    sg.s = s;
-    sg.L = uniform(plan_L(s));
-    sg.Q = uniform(plan_Q(s));
-    sg.qoff = uniform(plan_qoff(s));
-    sg.soff = soff;
-    sg.nb = (sg.L + BS - 1) / BS;
-    const int ns = P.UH + sg.nb;          // work blocks per unit
-    const int nrg = (P.G * sg.Q + 16 * NRT - 1) / (16 * NRT);
-    const int local = pos - soff;
-    sg.unit = local / ns;
-    const int uoff = local - sg.unit * ns;
-    if (uoff < P.UH) {                    // inside the unit's virtual blocks: start at its KV
-      pos += P.UH - uoff;
-      continue;
+    SplitDesc desc = {0, 0, 0, 0, 0, 0, 0, 0};
+    int pos = (int)b0;
+    bool first = true;
+    while (pos < b1) {
+      const int soff = uniform(plan_off(s));
+      const int send = uniform(plan_off(s + 1));
+      if (pos >= send) { ++s; continue; }
+      Segment sg;
+      sg.s = s;
+      sg.L = uniform(plan_L(s));
+      sg.Q = uniform(plan_Q(s));
+      sg.qoff = uniform(plan_qoff(s));
+      sg.soff = soff;
+      sg.nb = (sg.L + BS - 1) / BS;
+      const int ns = P.UH + sg.nb;        // work blocks per unit
+      const int nrg = (P.G * sg.Q + 16 * NRT - 1) / (16 * NRT);
+      const int local = pos - soff;
+      sg.unit = local / ns;
+      const int uoff = local - sg.unit * ns;
+      if (uoff < P.UH) {                  // inside the unit's virtual blocks: start at its KV
+        pos += P.UH - uoff;
+        continue;
+      }
+      sg.ub = uoff - P.UH;
+      sg.seg = min(sg.nb - sg.ub, (int)(b1 - pos));
+      sg.kvh = sg.unit / nrg;
+      sg.rg = sg.unit - sg.kvh * nrg;
+      sg.whole = (sg.ub == 0) && (sg.seg == sg.nb);
+      sg.slot = first ? 0 : 1;
+      if constexpr (KV8)
+        process_segment<D, BS, NRT, true, false>(P, sg, h, W, T1, PS, lane, c, g, desc);
+      else if (nrg > 1)                   // K/V read again by the sequence's other row groups
+        process_segment<D, BS, NRT, false, false>(P, sg, h, W, T1, PS, lane, c, g, desc);
+      else
+        process_segment<D, BS, NRT, false, true>(P, sg, h, W, T1, PS, lane, c, g, desc);
+      pos += sg.seg;
+      first = false;
     }
-    sg.ub = uoff - P.UH;
-    sg.seg = min(sg.nb - sg.ub, (int)(b1 - pos));
-    sg.kvh = sg.unit / nrg;
-    sg.rg = sg.unit - sg.kvh * nrg;
-    sg.whole = (sg.ub == 0) && (sg.seg == sg.nb);
-    sg.slot = first ? 0 : 1;
-    if constexpr (KV8)
-      process_segment<D, BS, NRT, true, false>(P, sg, w, W, TB, lane, c, g, desc);
-    else if (nrg > 1)                     // K/V read again by the sequence's other row groups
-      process_segment<D, BS, NRT, false, false>(P, sg, w, W, TB, lane, c, g, desc);
-    else
-      process_segment<D, BS, NRT, false, true>(P, sg, w, W, TB, lane, c, g, desc);
-    pos += sg.seg;
-    first = false;
-  }
-  if (lane == 0) {
-    int4* dp = reinterpret_cast<int4*>(P.desc) + 2 * w;
-    dp[0] = make_int4(desc.kvh, desc.rg, desc.qoff, desc.Q);
-    dp[1] = make_int4(desc.wb, desc.slot_a, desc.valid, 0);
+    if (lane == 0) {
+      int4* dp = reinterpret_cast<int4*>(P.desc) + 2 * h;
+      dp[0] = make_int4(desc.kvh, desc.rg, desc.qoff, desc.Q);
+      dp[1] = make_int4(desc.wb, desc.slot_a, desc.valid, 0);
+    }
+    if (NP == 0) return;
+    int k = 0;
+    if (lane == 0) k = __hip_atomic_fetch_add(&P.hdr->pool_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    k = uniform(__shfl(k, 0));
+    if (k >= NP) return;
+    h = W + k;
+    b0 = T1 + (long long)k * PS;
+    b1 = b0 + PS;
   }
 }
 
