@@ -33,8 +33,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  All work
  *     is enqueued on it, in order.
  *   - Return value: VAP_OK (0) or a negative VAP_E* code for an error detected on the host,
- *     in which case nothing was enqueued.  vap_last_error_message() describes the last host
- *     error of the calling thread.
+ *     in which case nothing was enqueued -- except VAP_EHIP, a kernel launch that failed after
+ *     the call's earlier kernels were enqueued; the workspace must then be zero-filled again
+ *     before its next use (a step leaves per-call state there, such as claim counters, that
+ *     only its last kernel resets).  vap_last_error_message() describes the last host error
+ *     of the calling thread.
  *   - Errors found in the data on the device (a block id outside the pool, inconsistent
  *     lengths, a draft id outside the vocabulary) never fault: the kernels clamp, OR a
  *     VAP_DERR_* bit into a sticky word at the start of the workspace, and leave the affected
