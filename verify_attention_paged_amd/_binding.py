@@ -8,6 +8,7 @@ missing or the device is not gfx950, calls raise.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -111,6 +112,14 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(device: torch.device):
+    """Context making `device` current for a library call (no switch when it already is: the
+    switch costs more host time than the call's own work)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -118,7 +127,7 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None, device=Non
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -188,7 +197,7 @@ def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, sca
     if workspace is None:
         workspace = attn_workspace(shape, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         if tree_mask is not None:
             rc = lib.paged_attn_step_tree(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr() if kv8 else None,
                                           block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
@@ -251,7 +260,7 @@ def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
     _need(workspace, "workspace", torch.uint8, 1, dev)
     qp = q.data_ptr() if k > 0 else None
     ip = draft_ids.data_ptr() if k > 0 else None
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.spec_verify(p.data_ptr(), qp, ip, uniforms.data_ptr(), out_ids.data_ptr(),
                              n_accepted.data_ptr(), B, k, V, workspace.data_ptr(),
                              workspace.numel(), _stream(stream))
@@ -298,7 +307,7 @@ def spec_verify_logits(target_logits, draft_logits, draft_ids, uniforms, tempera
     if workspace is None:
         workspace = verify_logits_workspace(B, k, V, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.spec_verify_logits(target_logits.data_ptr(), draft_logits.data_ptr() if k > 0 else None,
                                     draft_ids.data_ptr() if k > 0 else None, uniforms.data_ptr(),
                                     temperatures.data_ptr(), out_ids.data_ptr(), n_accepted.data_ptr(), B, k, V,
@@ -345,7 +354,7 @@ def spec_verify_tree(p, q, parents, tokens, uniforms, out_ids=None, out_path=Non
     if workspace is None:
         workspace = tree_verify_workspace(B, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.spec_verify_tree(p.data_ptr(), q.data_ptr(), parents.data_ptr(), tokens.data_ptr(),
                                   uniforms.data_ptr(), out_ids.data_ptr(), out_path.data_ptr(),
                                   n_accepted.data_ptr(), B, N, V, workspace.data_ptr(), workspace.numel(),
@@ -402,7 +411,7 @@ def kv_append(k_new, v_new, kv_pool, block_tables, ctx_lens, q_lens, *, kv_scale
     if workspace is None:
         workspace = kv_workspace(dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.kv_append(k_new.data_ptr(), v_new.data_ptr(), kv_pool.data_ptr(),
                            kv_scales.data_ptr() if kv_scales is not None else None, block_tables.data_ptr(),
                            ctx_lens.data_ptr(), q_lens.data_ptr(), ctypes.byref(shape), workspace.data_ptr(),
@@ -439,7 +448,7 @@ def kv_commit(kv_pool, block_tables, ctx_lens, q_lens, n_accepted, *, path=None,
     if workspace is None:
         workspace = kv_workspace(dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.kv_commit(kv_pool.data_ptr(), kv_scales.data_ptr() if kv_scales is not None else None,
                            block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
                            path.data_ptr() if path is not None else None, stride, n_accepted.data_ptr(),
