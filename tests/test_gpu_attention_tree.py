@@ -72,6 +72,23 @@ def test_random_trees_full_parity(case, kv_format):
     H.assert_close_rows(out, _oracle(inp), f"tree fuzz {case} {kv_format}")
 
 
+def test_small_trees_with_the_pool_of_tail_pieces():
+    """Trees of up to 4 nodes at G = 4 make 16-row units; on the minimum workspace (few worker
+    waves, far more than 32 work blocks each) the last tenth of the work runs as pool pieces, so
+    ranges start and end inside masked units: full parity, bitwise-equal rerun, no error."""
+    import ctypes
+    inp = _tree_case(470, [3000, 1500, 4000, 800, 2048, 129, 640, 17], 8, 2, 128, 16,
+                     [4, 3, 2, 4, 1, 3, 4, 2])
+    shape = vap.attn_shape(inp.q, inp.kv_pool, inp.block_tables)
+    lo = vap.load_library().vap_attn_workspace_min_bytes(ctypes.byref(shape))
+    ws = torch.zeros(lo, dtype=torch.uint8, device=H.device())
+    out, d = _run(inp, workspace=ws)
+    H.assert_close_rows(out, _oracle(inp), "small trees, pool")
+    again, _ = _run(inp, workspace=ws)
+    assert torch.equal(out, again)
+    assert vap.get_device_error(ws) == 0
+
+
 def test_chain_masks_match_the_causal_kernel():
     inp = workloads.make_attention_inputs(21, ctx_lens=[40, 300, 1000], q_lens=[5, 17, 64], num_q_heads=32,
                                           num_kv_heads=8, head_dim=128, block_size=16)
