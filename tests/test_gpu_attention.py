@@ -211,23 +211,23 @@ def test_one_workspace_across_calls_and_shapes():
     assert vap.get_device_error(ws) == 0
 
 
-@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("G, D, bs", [(4, 128, 16), (8, 128, 16), (4, 64, 32), (8, 128, 32)])
 @pytest.mark.parametrize("ws_kind", ["min", "small"])
-def test_pool_of_tail_pieces_full_parity(G, ws_kind):
+def test_pool_of_tail_pieces_full_parity(G, D, bs, ws_kind):
     """Decode batches on small workspaces (few worker waves) have far more than 32 work blocks per
     wave, so the last tenth of their work runs as pool pieces that finished waves claim: full
     parity with the oracle, bitwise-equal reruns on the same workspace, no device error."""
     import ctypes
-    inp = _case(31 + G, [3000, 17, 1500, 33, 800, 2, 640, 129, 2048, 4000], [1] * 10, 2 * G, 2, 128, 16)
+    inp = _case(31 + G + D + bs, [3000, 17, 1500, 33, 800, 2, 640, 129, 2048, 4000], [1] * 10, 2 * G, 2, D, bs)
     shape = vap.attn_shape(inp.q, inp.kv_pool, inp.block_tables)
     lib = vap.load_library()
     lo = lib.vap_attn_workspace_min_bytes(ctypes.byref(shape))
     hi = lib.vap_attn_workspace_bytes(ctypes.byref(shape))
     nbytes = {"min": lo, "small": (lo + hi) // 9 // 256 * 256}[ws_kind]
     ws = torch.zeros(max(lo, nbytes), dtype=torch.uint8, device=H.device())
-    print("pool case G", G, ws_kind, "workspace", ws.numel(), flush=True)
+    print("pool case G", G, "D", D, "bs", bs, ws_kind, "workspace", ws.numel(), flush=True)
     out, d = _run(inp, workspace=ws)
-    H.assert_close_rows(out, H.oracle_rows(inp), f"pool G={G} {ws_kind}")
+    H.assert_close_rows(out, H.oracle_rows(inp), f"pool G={G} D={D} bs={bs} {ws_kind}")
     for _ in range(2):
         again = vap.paged_attn_step(d["q"], d["kv_pool"], d["block_tables"], d["ctx_lens"], d["q_lens"],
                                     workspace=ws)
