@@ -43,10 +43,13 @@
  *     VAP_DERR_* bit into a sticky word at the start of the workspace, and leave the affected
  *     outputs unspecified (but written only inside the output arrays).
  *   - A workspace must be zero-filled before its first use (vap_workspace_init, or any
- *     zero-filled allocation); every call leaves it reusable.  Calls that share a workspace
- *     must be ordered (same stream, or synchronised).  A workspace serves one kind of call:
- *     either paged_attn_step or spec_verify, never both; kv_append and kv_commit touch only the
- *     sticky error word and may share either.
+ *     zero-filled allocation); every call leaves it reusable by later calls of the same entry
+ *     point with any sizes and any workspace_bytes at or above what each call needs (per-call
+ *     state such as arrival tickets sits at offsets that depend on neither).  Calls that share
+ *     a workspace must be ordered (same stream, or synchronised).  A workspace serves one kind
+ *     of call (the paged_attn_step family, spec_verify, spec_verify_logits or
+ *     spec_verify_tree); kv_append and kv_commit touch only the sticky error word and may
+ *     share any of them.
  */
 #ifndef VAP_H_
 #define VAP_H_
@@ -75,10 +78,10 @@ extern "C" {
                                    a tree of more than 64 rows (the row is then repaired: own
                                    bit set, later bits cleared; or kept causal)              */
 #define VAP_DERR_TEMP 0x40      /* temperature negative or not finite (the sequence is greedy)  */
-#define VAP_DERR_SYNC 0x80      /* spec_verify_tree: the workgroups sharing a sequence's walk did not
-                                   all run at once (the GPU was held by other work for a quarter
-                                   of a second); that sequence's outputs are unspecified and the
-                                   workspace must be zero-filled again before its next use      */
+#define VAP_DERR_SYNC 0x80      /* the verifiers: a workgroup reading a value that another
+                                   workgroup of the same call has already stored waited past a
+                                   guard of about a quarter of a second (never expected: the
+                                   guard only keeps every wait finite)                          */
 
 /*
  * Shape of one attention step.
@@ -226,7 +229,7 @@ size_t vap_verify_logits_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vo
  *
  * Two kernels on `stream`: row statistics (max, argmax, sum of exponentials) of all rows,
  * then the verification.  The workspace (vap_verify_logits_workspace_bytes) serves
- * spec_verify_logits calls only; pass the same workspace_bytes on every call.
+ * spec_verify_logits calls only.
  */
 int spec_verify_logits(const float* target_logits, const float* draft_logits, const int32_t* draft_ids,
                        const float* uniforms, const float* temperatures, int32_t* out_ids, int32_t* n_accepted,
@@ -273,13 +276,9 @@ size_t vap_tree_verify_workspace_bytes(int32_t num_seqs);
  * it with p_cur = its target row.  With no child left, one token is drawn from p_cur (inverse
  * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
  * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
- * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk, then
- * the final draw spread over the GPU.  For vocabularies above 32768, the walk runs up to 16
- * workgroups per sequence (one per 32768 tokens, no more than keep the whole launch resident, one
- * per CU) that share each residual pass and exchange partial sums through the workspace; if other work holds the
- * GPU so long that they cannot all run, the wait ends after a quarter of a second with
- * VAP_DERR_SYNC.
- * The workspace (zero-filled before first use) serves spec_verify_tree calls only.
+ * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk (one
+ * workgroup per sequence, which streams every residual sum itself), then the final draw spread
+ * over the GPU.  The workspace (zero-filled before first use) serves spec_verify_tree calls only.
  */
 int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
                      const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,

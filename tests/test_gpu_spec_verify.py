@@ -222,3 +222,104 @@ def test_monte_carlo_emitted_distribution():
         rate = (n[reached] > i).mean()
         sd = np.sqrt(alpha[i] * (1 - alpha[i]) / reached.sum())
         assert abs(rate - alpha[i]) < 5 * sd
+
+
+# ---- the draw's fallback branches (the oracle's readings for an empty residual, an all-zero
+# ---- row and a threshold at or past the total), each bit-exact against the oracle
+
+def _softmax_rows(rng, shape, scale=2.0):
+    z = scale * rng.standard_normal(shape)
+    e = np.exp(z - z.max(-1, keepdims=True))
+    return (e / e.sum(-1, keepdims=True)).astype(np.float32)
+
+
+@pytest.mark.parametrize("V", [128256, 3001])
+def test_empty_residual_falls_back_to_the_target_row(V):
+    """p_i = q_i / 2 (used as given) makes every residual max(0, p - q) empty: a rejection at n
+    draws from p_n itself, the last workgroup recomputing its chunk sums; V = 3001 runs the
+    scalar load path."""
+    rng = np.random.default_rng(40 + V)
+    B, k = 24, 4
+    q = _softmax_rows(rng, (B, k, V))
+    p = np.empty((B, k + 1, V), np.float32)
+    p[:, :k] = 0.5 * q                                # exact in fp32
+    p[:, k] = _softmax_rows(rng, (B, V))
+    ids = np.array([[rng.choice(V, p=q[b, i].astype(np.float64) / q[b, i].astype(np.float64).sum())
+                     for i in range(k)] for b in range(B)], dtype=np.int32)
+    u0 = workloads.open_uniforms(rng, (B, k + 1))
+    u = OS.uniforms_with_margin(p.astype(np.float64), q.astype(np.float64), ids, u0, rng)
+    ws = vap.verify_workspace(B, k, V, DEV)
+    n = _compare(p.astype(np.float64), q.astype(np.float64), ids, u, f"empty residual V={V}", workspace=ws)
+    assert np.any(n < k), "no sequence took the fallback"
+    assert vap.get_device_error(ws) == 0
+    print("accepted", n.tolist(), flush=True)
+
+
+@pytest.mark.parametrize("V", [128256, 1000])
+def test_all_zero_row_emits_token_zero_and_flags(V):
+    """A rejection on an all-zero target row (residual and fallback both empty), and a bonus
+    draw from an all-zero row: token 0 and VAP_DERR_EMPTY_ROW; the other sequences are
+    unaffected."""
+    rng = np.random.default_rng(50 + V)
+    B, k = 6, 3
+    q = _softmax_rows(rng, (B, k, V))
+    p = _softmax_rows(rng, (B, k + 1, V))
+    ids = np.argmax(q, axis=-1).astype(np.int32)
+    p[1, 0] = 0.0                                     # draft 0 of sequence 1: P = 0, rejected
+    p[3, :k] = q[3]                                   # sequence 3 accepts every draft ...
+    p[3, k] = 0.0                                     # ... and its bonus row is empty
+    u0 = workloads.open_uniforms(rng, (B, k + 1))
+    keep = np.ones(B, bool)
+    keep[[1, 3]] = False
+    u = u0.copy()
+    u[keep] = OS.uniforms_with_margin(p[keep].astype(np.float64), q[keep].astype(np.float64), ids[keep],
+                                      u0[keep], rng)
+    ws = vap.verify_workspace(B, k, V, DEV)
+    n = _compare(p.astype(np.float64), q.astype(np.float64), ids, u, f"all-zero rows V={V}", workspace=ws)
+    assert n[1] == 0 and n[3] == k
+    out, _ = _gpu(p, q, ids, u, ws)
+    assert out[1, 0] == 0 and out[3, k] == 0
+    assert vap.get_device_error(ws, clear=True) & vap.DERR_EMPTY_ROW
+    assert vap.get_device_error(ws) == 0
+
+
+def test_threshold_past_the_total_takes_the_last_positive_token():
+    """An infinite weight makes t = u * Z infinite, so no running sum exceeds it: both sides
+    take the largest token with positive weight (the reading for t at or past the total).  The
+    drafts are accepted (p = q), so the bonus row is drawn from."""
+    rng = np.random.default_rng(60)
+    B, k, V = 5, 2, 128256
+    q = _softmax_rows(rng, (B, k, V))
+    p = np.empty((B, k + 1, V), np.float32)
+    p[:, :k] = q
+    p[:, k] = _softmax_rows(rng, (B, V))
+    last = [V - 1, 70000, 4095, 4096, 128000]
+    for b in range(B):
+        p[b, k, 1000 + 37 * b] = np.inf
+        p[b, k, last[b] + 1:] = 0.0                   # the last positive token of the row
+    ids = np.argmax(q, axis=-1).astype(np.int32)
+    u = workloads.open_uniforms(rng, (B, k + 1))
+    ref_out, ref_n = OS.spec_verify(p.astype(np.float64), q.astype(np.float64), ids, u.astype(np.float64))
+    assert np.all(ref_n == k) and ref_out[:, k].tolist() == last
+    out, n = _gpu(p, q, ids, u)
+    assert np.array_equal(n, ref_n) and np.array_equal(out, ref_out), (out[:, k], last)
+
+
+def test_one_buffer_with_changing_workspace_sizes():
+    """One buffer, each call passing exactly the bytes its own batch needs (so the size passed
+    changes from call to call, and a large call's chunk sums lie where a small call's workspace
+    ends): bit-exact every time, no device error."""
+    big = vap.load_library().vap_verify_workspace_bytes(256, 4, 128256)
+    buf = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    lib = vap.load_library()
+    for B, V, seed in [(64, 128256, 1), (4, 128256, 2), (1, 32000, 3), (256, 128256, 4), (16, 128256, 5),
+                       (4, 5003, 6), (64, 128256, 7)]:
+        rng = np.random.default_rng(seed)
+        pl = 3.0 * rng.standard_normal((B, 5, V))
+        ql = pl[:, :4] + 0.7 * rng.standard_normal((B, 4, V))
+        vin = workloads.make_verify_inputs(seed, p_logits=pl, q_logits=ql, rng=rng)
+        p, q, ids, u = _margin_inputs(vin, seed)
+        nbytes = lib.vap_verify_workspace_bytes(B, 4, V)
+        print("workspace bytes", nbytes, "B", B, "V", V, flush=True)
+        _compare(p, q, ids, u, f"B={B} V={V} bytes={nbytes}", workspace=buf[:nbytes])
+    assert vap.get_device_error(buf) == 0

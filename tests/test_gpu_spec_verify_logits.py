@@ -171,3 +171,45 @@ def test_monte_carlo_first_token_at_temperature():
     exp = B * sp_softmax(zp1[0].astype(np.float64) / T)
     chi2 = float(((counts - exp) ** 2 / exp).sum())
     assert chi2 < stats.chi2.ppf(0.999, V - 1), f"chi2 {chi2}"
+
+
+@pytest.mark.parametrize("V", [128256, 3001])
+def test_empty_residual_falls_back_to_the_target_row(V):
+    """Draft rows equal to the target rows give p = q bit for bit on both sides, so the residual
+    after a rejection is empty; an out-of-range draft id forces that rejection.  The token is
+    then drawn from p_n (the fallback reading), bit-exact, and VAP_DERR_DRAFT_ID is set."""
+    rng = np.random.default_rng(70 + V)
+    B, k = 12, 4
+    zp = (2.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zq = zp[:, :k].copy()
+    temps = np.where(np.arange(B) % 3 == 0, 0.7, 1.0)
+    ids = np.stack([np.array([rng.choice(V, p=sp_softmax(zq[b, i].astype(np.float64) / temps[b]))
+                              for i in range(k)]) for b in range(B)]).astype(np.int32)
+    bad = rng.integers(0, k, size=B)
+    for b in range(0, B, 2):
+        ids[b, bad[b]] = V + 5 if b % 4 == 0 else -1    # rejected there, with p = q
+    inp = workloads.make_logits_verify_inputs(71, zp, zq, temps)
+    u = OL.uniforms_with_margin(zp, zq, ids, inp.uniforms.numpy(), temps, np.random.default_rng(72))
+    ws = vap.verify_logits_workspace(B, k, V, DEV)
+    ref = _compare(zp, zq, ids, u, temps, f"empty residual V={V}", workspace=ws)
+    assert np.all(ref[1][0::2] <= bad[0::2]) and np.any(ref[1][0::2] == bad[0::2])
+    assert vap.get_device_error(ws, clear=True) & vap.DERR_DRAFT_ID
+    assert vap.get_device_error(ws) == 0
+
+
+def test_one_buffer_with_changing_workspace_sizes():
+    """Each call passes exactly the bytes its own shape needs, so where the tickets lie moves
+    from call to call over data earlier calls left behind: bit-exact every time."""
+    lib = vap.load_library()
+    shapes = [(16, 4, 128256), (2, 1, 5000), (64, 4, 32000), (1, 0, 7), (3, 12, 4099), (16, 4, 128256), (40, 2, 1000)]
+    buf = torch.zeros(max(lib.vap_verify_logits_workspace_bytes(*s) for s in shapes), dtype=torch.uint8, device=DEV)
+    for i, (B, k, V) in enumerate(shapes):
+        rng = np.random.default_rng(300 + i)
+        zp = (2.5 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+        zq = (zp[:, :k] + 0.6 * rng.standard_normal((B, k, V))).astype(np.float32)
+        temps = rng.choice([0.0, 0.8, 1.0], size=B)
+        inp = workloads.make_logits_verify_inputs(400 + i, zp, zq, temps)
+        nbytes = lib.vap_verify_logits_workspace_bytes(B, k, V)
+        print("workspace bytes", nbytes, (B, k, V), flush=True)
+        _compare(*_margin(inp, 20 + i), f"call {i} {(B, k, V)}", workspace=buf[:nbytes])
+    assert vap.get_device_error(buf) == 0

@@ -159,11 +159,10 @@ def test_monte_carlo_first_token_follows_the_root_target():
     assert chi2 < stats.chi2.ppf(0.999, V - 1), f"chi2 {chi2}"
 
 
-def test_one_workspace_across_part_counts():
-    """Several workgroups per sequence share each residual pass (one per 32768 tokens: 10 at
-    V = 300000, 5 at V = 140000, 1 for small vocabularies); the arrival counts on each
-    sequence's ticket must be back at zero for the next call.  One workspace serves five calls
-    of different shapes, each bit-exact, with no device error (in particular no VAP_DERR_SYNC)."""
+def test_one_workspace_across_shapes():
+    """One workspace serves five calls of different shapes (vocabularies 300000, 140000, 3001 and
+    32768; 8 to 16 nodes): each call leaves the tickets and published slots at zero for the next,
+    each is bit-exact, and no device error is set (in particular no VAP_DERR_SYNC)."""
     ws = vap.tree_verify_workspace(64, DEV)
     shapes = [(3, 16, 300000, 31), (32, 8, 140000, 32), (3, 16, 300000, 33), (5, 12, 3001, 34), (16, 16, 32768, 35)]
     for B, N, V, seed in shapes:
@@ -180,3 +179,101 @@ def test_one_workspace_across_part_counts():
         for name, a, b in zip(("ids", "path", "n_accepted"), got, ref):
             assert np.array_equal(a, b), f"B={B} N={N} V={V}: {name} differ\n{a}\n{b}"
         assert vap.get_device_error(ws) == 0, f"B={B} N={N} V={V}: device error"
+
+
+# ---- the draw's fallback branches, bit-exact against the oracle
+
+def _soft(rng, shape, scale=2.0):
+    z = scale * rng.standard_normal(shape)
+    e = np.exp(z - z.max(-1, keepdims=True))
+    return (e / e.sum(-1, keepdims=True)).astype(np.float32)
+
+
+def _draw_uniform_with_margin(p, q, parents, tokens, u, rng):
+    """Keep the accept-test uniforms as given; redraw only u_0 until the walk's every threshold
+    is at least 1e-6 away."""
+    u = u.copy()
+    for b in range(u.shape[0]):
+        while OT.tree_decision_margin(p[b], q[b], parents[b], tokens[b], u[b]) < 1e-6:
+            u[b, 0] = workloads.open_uniforms(rng, (1,))[0]
+    return u
+
+
+@pytest.mark.parametrize("V", [128256, 3001])
+def test_empty_residual_keeps_the_current_distribution(V):
+    """The root's target row is half its draft row (used as given), so every residual at the
+    root is empty and the walk keeps p_cur = p[root] (the reading for an empty residual).  When
+    every child of the root is rejected, the draw kernel finds the weights max(0, p - c' q)
+    empty and falls back to the previous c."""
+    rng = np.random.default_rng(80 + V)
+    B = 16
+    parents = np.tile(np.array([-1, 0, 0, 0, 1, 1]), (B, 1))
+    N = parents.shape[1]
+    q = _soft(rng, (B, N, V))
+    p = _soft(rng, (B, N, V))
+    p[:, 0] = 0.5 * q[:, 0]                            # exact in fp32
+    tokens = np.full((B, N), -1)
+    for b in range(B):
+        for i in range(1, N):
+            w = q[b, parents[b, i]].astype(np.float64)
+            tokens[b, i] = rng.choice(V, p=w / w.sum())
+    u = workloads.open_uniforms(rng, (B, N))
+    u[: B // 2, 1:4] = 0.75                            # the root's three children are rejected
+    u[B // 2:, 1] = 0.25                               # child 1 accepted: the walk goes on under it
+    u = _draw_uniform_with_margin(p, q, parents, tokens, u, rng)
+    ws = vap.tree_verify_workspace(B, DEV)
+    ref = OT.tree_verify(p, q, parents, tokens, u.astype(np.float64))
+    got = _gpu(p, q, parents, tokens, u, workspace=ws)
+    for name, a, b_ in zip(("ids", "path", "n_accepted"), got, ref):
+        assert np.array_equal(a, b_), f"V={V}: {name} differ\n{a}\n{b_}"
+    assert np.all(ref[2][: B // 2] == 0) and np.all(ref[2][B // 2:] >= 1)
+    assert vap.get_device_error(ws) == 0
+
+
+def test_all_zero_row_emits_token_zero_and_flags():
+    """An all-zero target row at the node where the walk ends: the residual and the fallback are
+    both empty, so the token is 0 and VAP_DERR_EMPTY_ROW is set.  Sequences 0 and 1 reject every
+    child of an all-zero root (P = 0); sequence 2 is an ordinary chain."""
+    rng = np.random.default_rng(90)
+    V = 128256
+    parents = np.array([[-1, 0, 0], [-1, 0, 0], [-1, 0, 1]])
+    q = _soft(rng, (3, 3, V))
+    p = _soft(rng, (3, 3, V))
+    p[0, 0] = 0.0
+    p[1, 0] = 0.0
+    tokens = np.array([[-1, 5, 9], [-1, 3, 4], [-1, int(np.argmax(q[2, 0])), int(np.argmax(q[2, 1]))]])
+    u = workloads.open_uniforms(rng, (3, 3))
+    u = _draw_uniform_with_margin(p, q, parents, tokens, u, rng)
+    ws = vap.tree_verify_workspace(3, DEV)
+    ref = OT.tree_verify(p, q, parents, tokens, u.astype(np.float64))
+    got = _gpu(p, q, parents, tokens, u, workspace=ws)
+    for name, a, b_ in zip(("ids", "path", "n_accepted"), got, ref):
+        assert np.array_equal(a, b_), f"{name} differ\n{a}\n{b_}"
+    assert got[0][0, 0] == 0 and got[0][1, 0] == 0 and got[2][0] == 0 and got[2][1] == 0
+    assert vap.get_device_error(ws, clear=True) & vap.DERR_EMPTY_ROW
+    assert vap.get_device_error(ws) == 0
+
+
+def test_one_buffer_with_changing_workspace_sizes():
+    """Each call passes exactly the bytes its own batch needs, so the size passed changes from
+    call to call: bit-exact every time, no device error."""
+    lib = vap.load_library()
+    shapes = [(24, 8, 140000, 41), (2, 12, 300000, 42), (1, 5, 70000, 43), (32, 8, 140000, 44), (4, 16, 3001, 45),
+              (24, 8, 140000, 46)]
+    buf = torch.zeros(max(lib.vap_tree_verify_workspace_bytes(s[0]) for s in shapes), dtype=torch.uint8, device=DEV)
+    for B, N, V, seed in shapes:
+        rng = np.random.default_rng(seed)
+        pl = 3.0 * rng.standard_normal((B, N, V))
+        ql = pl + 0.7 * rng.standard_normal((B, N, V))
+        soft = lambda z: np.exp(z - z.max(-1, keepdims=True)) / np.exp(z - z.max(-1, keepdims=True)).sum(-1, keepdims=True)
+        parents = np.stack([workloads.random_tree_parents(rng, N) for _ in range(B)])
+        tin = workloads.make_tree_verify_from_probs(seed, soft(pl).astype(np.float32), soft(ql).astype(np.float32),
+                                                    parents)
+        p, q, par, tok, u = _margin(tin, seed)
+        nbytes = lib.vap_tree_verify_workspace_bytes(B)
+        print("workspace bytes", nbytes, (B, N, V), flush=True)
+        ref = OT.tree_verify(p, q, par, tok, u.astype(np.float64))
+        got = _gpu(p, q, par, tok, u, workspace=buf[:nbytes])
+        for name, a, b_ in zip(("ids", "path", "n_accepted"), got, ref):
+            assert np.array_equal(a, b_), f"B={B} N={N} V={V}: {name} differ\n{a}\n{b_}"
+    assert vap.get_device_error(buf) == 0

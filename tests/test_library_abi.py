@@ -124,10 +124,23 @@ def test_verify_logits_rejected_on_host(lib):
     # workspace too small
     assert f(fake, fake, fake, fake, fake, fake, fake, 4, 4, 10, fake, 64, None) == B.VAP_ENOSPC
     assert f(None, None, None, None, None, None, None, 0, 4, 10, None, 0, None) == B.VAP_OK
-    # the layout keeps data and tickets in separate halves
-    n1 = lib.vap_verify_logits_workspace_bytes(1, 4, 1 << 20)
-    n2 = lib.vap_verify_logits_workspace_bytes(1000, 0, 4)
-    assert n1 % 512 == 0 and n2 % 512 == 0
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_verifier_workspace_layouts(lib):
+    """Header, then one record per sequence (its ticket first, then its data: 256 fp64 chunk
+    sums; for a tree also the walk's end state); the logits workspace puts the statistics
+    partials (16 bytes per row and 2048-token chunk) before the records."""
+    rec = 16 + 8 * 256
+    for B in (1, 7, 1000, 1 << 22):
+        assert lib.vap_verify_workspace_bytes(B, 4, 128256) == _a256(256 + B * rec)
+        assert lib.vap_tree_verify_workspace_bytes(B) == _a256(256 + B * (rec + 32))
+    for B, k, V in ((1, 4, 1 << 20), (1000, 0, 4), (16, 4, 128256), (3, 64, 2049)):
+        part = B * (2 * k + 1) * ((V + 2047) // 2048) * 16
+        assert lib.vap_verify_logits_workspace_bytes(B, k, V) == _a256(_a256(256 + part) + B * rec)
 
 
 def test_workspace_sizes_are_consistent(lib):

@@ -449,8 +449,7 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
   P.C = (int)C;
   P.CS = (int)CS;
   P.err = reinterpret_cast<int32_t*>(ws);
-  P.tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
-  P.chunk_sums = reinterpret_cast<double*>(ws + 256);
+  P.rec = SeqRecords{ws + 256, (long long)kVerifyRec};
   const bool vec4 = (vocab % 4 == 0) &&
                     ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(k ? q : p)) & 15) == 0;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -490,7 +489,7 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
 
   char* ws = static_cast<char*>(workspace);
-  int32_t* tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
+  const SeqRecords rec{ws + lay.records, (long long)kVerifyRec};
   const bool vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(target_logits) |
                                            reinterpret_cast<uintptr_t>(k ? draft_logits : target_logits)) & 15) == 0;
   LogitStatsParams S;
@@ -503,6 +502,7 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   S.V = vocab;
   S.C = (int)C1;
   S.err = reinterpret_cast<int32_t*>(ws);
+  S.rec = rec;
   // persistent statistics waves: kStatWavesPerCU per CU, no more than there are items
   const long long stat_waves = std::min(R * C1, (long long)d->num_cus * kStatWavesPerCU);
   const int stat_wg = (int)((stat_waves + kStatWavesPerWG - 1) / kStatWavesPerWG);
@@ -528,8 +528,8 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   P.C = (int)C;
   P.CS = (int)CS;
   P.err = reinterpret_cast<int32_t*>(ws);
-  P.tickets_end = tickets_end;
-  P.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk_sums);
+  P.rec = rec;
+  S.VC = (int)C;
   P.temps = temperatures;
   P.part = S.part;
   P.C1 = (int)C1;
@@ -584,16 +584,7 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.V = vocab;
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   P.err = reinterpret_cast<int32_t*>(ws);
-  P.draws = reinterpret_cast<TreeDraw*>(ws + 256);
-  // Workgroups per sequence in the walk: the fewest that give each one a single load round of a
-  // residual pass (more parts only add arrivals to wait for: at V = 128256, 4 parts walked in
-  // 21.8 us against 23.5 with 8, 27 with 16 and 27.4 with 3, which needs a second round),
-  // bounded by kMaxTreeParts and by keeping every workgroup of the launch resident at once (one
-  // per CU).
-  const int parts = (int)(((long long)vocab + kTreeRoundTokens - 1) / kTreeRoundTokens);
-  P.S = std::max(1, std::min({parts, kMaxTreeParts, d->num_cus / num_seqs}));
-  P.xch = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
-  P.xch_stride = kMaxChunks;
+  P.rec = SeqRecords{ws + 256, (long long)kTreeRec};
 
   // draw chunks: as spec_verify (about two workgroups per CU over the batch)
   long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
@@ -608,15 +599,12 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   D.q = q;
   D.uniforms = uniforms;
   D.out_ids = out_ids;
-  D.draws = P.draws;
   D.B = num_seqs;
   D.N = num_nodes;
   D.V = vocab;
   D.C = (int)C;
   D.CS = (int)CS;
-  D.chunk_sums = reinterpret_cast<double*>(ws + 256 + (size_t)num_seqs * sizeof(TreeDraw));
-  D.tickets_end = reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~size_t(3)));
-  P.tickets_end = D.tickets_end;
+  D.rec = P.rec;
   D.err = P.err;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);

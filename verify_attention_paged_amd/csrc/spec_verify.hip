@@ -80,6 +80,9 @@ struct LogitWeight {
   double mp, mq, c, inv_sp, inv_sq;   // row maxima, log2(e) / T, reciprocals of the row sums
   const double* tab;                  // 2^(j/64) table in LDS
   __device__ __forceinline__ double operator()(float zp, float zq) const {
+    // p and q are each rounded before the difference: fusing q's product into the
+    // subtraction would leave p's rounding error behind where p = q (an empty residual)
+#pragma clang fp contract(off)
     const double p = exp2_f64(((double)zp - mp) * c, tab) * inv_sp;
     return residual ? fmax(0.0, p - exp2_f64(((double)zq - mq) * c, tab) * inv_sq) : p;
   }
@@ -299,14 +302,26 @@ __device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool
   }
 }
 
+// One workgroup's chunk sum is published to its slot, then the workgroup arrives on the
+// sequence's ticket (thread 0 only).  The workgroup that takes the last ticket (value `last`)
+// resets the ticket for the next call and returns true; it then reads every chunk's slot,
+// waiting for any not yet visible (read_slot), and clears them.
+__device__ __forceinline__ bool publish_and_arrive(unsigned long long* slot, double value, int32_t* ticket, int last) {
+  publish_slot(slot, value);
+  const int t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t != last) return false;
+  __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // Step 4 of a draw by the last workgroup of a sequence: with every chunk's sum of w published
-// (chunk_sums[0 .. C)), find the chunk holding t = u Z (one wave; each lane holds up to four
-// consecutive chunks, C <= 256), then the token inside it.  If Z = 0 the weights `fallback`
+// (slots[0 .. C), read and cleared here), find the chunk holding t = u Z (one wave; each lane
+// holds up to four consecutive chunks, C <= 256), then the token inside it.  If Z = 0 the weights `fallback`
 // are drawn from instead (their chunk sums computed here); if those are all zero too,
 // VAP_DERR_EMPTY_ROW and token 0.  If rounding leaves t at or past the total, the last token
 // with positive weight.
 template <bool VEC4, class W>
-__device__ int finish_draw(const double* chunk_sums, int C, int CS, int V, float uk, const float* prow,
+__device__ int finish_draw(unsigned long long* slots, int C, int CS, int V, float uk, const float* prow,
                            const float* qrow, const W& w, const W& fallback, int32_t* err, double* s_loc,
                            int& s_cstar, double* s_red, int* s_int) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -315,14 +330,16 @@ __device__ int finish_draw(const double* chunk_sums, int C, int CS, int V, float
   double Z = 0.0;
   if (tid < 64) {
     double cs[4];
+    bool late = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = 4 * lane + j;
-      cs[j] = ci < C ? __longlong_as_double((long long)__hip_atomic_load(
-                           reinterpret_cast<const unsigned long long*>(chunk_sums) + ci, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT))
-                     : 0.0;
+      cs[j] = ci < C ? read_slot(slots + ci, &late) : 0.0;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * lane + j < C) clear_slot(slots + 4 * lane + j);
+    if (late) atomicOr(err, VAP_DERR_SYNC);
     const double mine = (cs[0] + cs[1]) + (cs[2] + cs[3]);
     double incl = mine;
 #pragma unroll
@@ -495,27 +512,15 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const int x0 = cidx * P.CS;
   const int x1 = min(V, x0 + P.CS);
   double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
-  if (tid == 0) {
-    // publish the chunk sum with an agent-coherent (write-through) store, wait until it has
-    // completed, then arrive; the L2-wide writeback/invalidate of an agent-scope fence is not
-    // needed because every cross-workgroup value goes through agent-scope accesses
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + cidx,
-                       (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (ticket == C - 1);
-  }
+  unsigned long long* sums = P.rec.at<unsigned long long>(b, kVerifyRecSums);
+  if (tid == 0) s_last = publish_and_arrive(sums + cidx, part, P.rec.ticket(b), C - 1);
   __syncthreads();
   if (!s_last) return;
 
   // 4. last workgroup of sequence b: the chunk holding t, then the token inside it
-  if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   W p_only = w;   // an empty residual falls back to the row p_n itself
   p_only.residual = false;
-  const int token = finish_draw<VEC4>(P.chunk_sums + (long long)b * C, C, P.CS, V, s_uk, prow, qrow, w, p_only,
+  const int token = finish_draw<VEC4>(sums, C, P.CS, V, s_uk, prow, qrow, w, p_only,
                                       P.err, s_loc, s_cstar, s_red, s_int);
 
   // 5. outputs
@@ -606,6 +611,15 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
     if (lane == 0) P.part[it] = LogitRowStat{S, m, mi};
   };
 
+  // this call's verification tickets and chunk-sum slots start at zero whatever an earlier call
+  // of another shape left there (the verification kernel runs after this one, in stream order)
+  const long long words = (long long)P.B * (P.VC + 1);
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < words; e += (long long)gridDim.x * kThreads) {
+    const long long b = e / (P.VC + 1);
+    const int j = (int)(e - b * (P.VC + 1));
+    if (j == 0) *P.rec.ticket(b) = 0;
+    else P.rec.at<unsigned long long>(b, kVerifyRecSums)[j - 1] = 0ull;
+  }
   int it = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6));
   if (it >= items) return;
   float va[kEl], vb[kEl];
@@ -647,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
   const int b = blockIdx.x / C;
   const int cidx = blockIdx.x - b * C;
   const int tid = threadIdx.x;
-  const TreeDraw d = P.draws[b];
+  const TreeDraw d = *P.rec.at<const TreeDraw>(b, kTreeRecDraw);
   const long long row = (long long)b * P.N + d.node;
   const float* prow = P.p + row * P.V;
   const float* qrow = P.q + row * P.V;
@@ -655,24 +669,13 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
   const int x0 = cidx * P.CS;
   const int x1 = min(P.V, x0 + P.CS);
   const double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
-  if (tid == 0) {
-    // publish the chunk sum write-through, wait for it, then arrive (as in spec_verify_kernel)
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(P.chunk_sums) + (long long)b * C + cidx,
-                       (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // the walk's parts arrived on this ticket first (d.arrivals times)
-    const int ticket = __hip_atomic_fetch_add(P.tickets_end - (b + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (ticket == d.arrivals + C - 1);
-  }
+  unsigned long long* sums = P.rec.at<unsigned long long>(b, kTreeRecSums);
+  if (tid == 0) s_last = publish_and_arrive(sums + cidx, part, P.rec.ticket(b), C - 1);
   __syncthreads();
   if (!s_last) return;
-  if (tid == 0) __hip_atomic_store(P.tickets_end - (b + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float uk = P.uniforms[(long long)b * P.N];
   const TreeDrawWeight prev{d.c_prev > 0.0, d.c_prev};
-  const int token = finish_draw<VEC4>(P.chunk_sums + (long long)b * C, C, P.CS, P.V, uk, prow, qrow, w, prev,
+  const int token = finish_draw<VEC4>(sums, C, P.CS, P.V, uk, prow, qrow, w, prev,
                                       P.err, s_loc, s_cstar, s_red, s_int);
   if (tid == 0) P.out_ids[(long long)b * P.N + d.n] = token;
 }

@@ -13,13 +13,11 @@
 //   * when no child is left, one token is drawn from p_cur: t = u_0 * sum(p_cur), the smallest x
 //     whose running sum exceeds t.
 //
-// How: S workgroups of 1024 threads per sequence walk it in lockstep (the walk is sequential,
-// every rejection needs a vocabulary-wide fp64 sum).  Each takes 1/S of the vocabulary in a
-// residual pass; the S partial sums are exchanged through the workspace (write-through stores,
-// an arrival counter, a bounded wait) and added in part order, so every part holds the same sum
-// and takes the same decisions.  S is chosen on the host so that all B*S workgroups fit on the
-// GPU at once (at most one per CU).  p_cur is never stored.  After j rejections at node u (all
-// against the same draft row q = q[u]) the residual has the closed form
+// How: one workgroup of 1024 threads walks each sequence (the walk is sequential, and every
+// rejection with children left to test needs a vocabulary-wide fp64 sum, which the workgroup
+// streams itself: no workgroup ever waits for another).  p_cur is never stored.  After j
+// rejections at node u (all against the same draft row q = q[u]) the residual has the closed
+// form
 //     p_cur(x) = max(0, p(x) - c_j q(x)) / D_j,   c_0 = 0, D_0 = 1,
 //     c_{j+1} = c_j + D_j,   D_{j+1} = sum_x max(0, p(x) - c_{j+1} q(x))
 // (induction on max(0, max(0, p - c q) / D - q) = max(0, p - (c + D) q) / D), and a zero sum keeps
@@ -37,7 +35,6 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kMaxNodes = 64;
 constexpr int kIt = 8;     // float4 pairs per thread in flight per round of a residual pass
-static_assert(4 * kIt * kThreads == kTreeRoundTokens, "the host sizes walk parts by this round");
 
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
@@ -63,52 +60,6 @@ __device__ __forceinline__ double weight(float p, float q, double c) {
   return fmax(0.0, fma(-c, (double)q, (double)p));
 }
 
-// Wait bound of the exchange between the parts of a sequence: about a quarter of a second.  The
-// parts are all resident (the host sizes the grid for that), so the bound is only reached if
-// something else holds the CUs; the sum is then incomplete, VAP_DERR_SYNC is set and the part
-// stops waiting for the rest of its walk (so such a call still ends quickly).
-constexpr int kSpinMax = 1 << 18;
-
-// Sum of the S parts' partial sums of pass r of sequence b (every part calls this with its own
-// partial).  Slots alternate between two banks by pass parity: a part can be at most one pass
-// ahead of another, so a bank is never rewritten before every part has read it.
-__device__ __forceinline__ double exchange_sum(const TreeVerifyParams& P, int b, int part, int r, double partial,
-                                               double* s_val, int* s_timeout) {
-  const int S = P.S;
-  unsigned long long* slots = reinterpret_cast<unsigned long long*>(P.xch) + (long long)b * P.xch_stride + (r & 1) * S;
-  int32_t* cnt = P.tickets_end - (b + 1);   // the sequence's ticket, zero at the start of the call
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(slots + part, (unsigned long long)__double_as_longlong(partial), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);        // the slot is written before this part arrives
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int target = S * (r + 1);
-    int it = 0;
-    if (!*s_timeout) {
-      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target && ++it < kSpinMax)
-        __builtin_amdgcn_s_sleep(2);
-    }
-    if (it >= kSpinMax) {
-      atomicOr(P.err, VAP_DERR_SYNC);
-      *s_timeout = 1;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const double v = lane < S ? __longlong_as_double((long long)__hip_atomic_load(slots + lane, __ATOMIC_RELAXED,
-                                                                                    __HIP_MEMORY_SCOPE_AGENT))
-                              : 0.0;
-    double t = 0.0;
-    for (int j = 0; j < S; ++j) t += __shfl(v, j);   // part order, the same in every part
-    if (lane == 0) *s_val = t;
-  }
-  __syncthreads();
-  return *s_val;
-}
-
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyParams P) {
   __shared__ int s_par[kMaxNodes];
   __shared__ int s_tok[kMaxNodes];
@@ -119,14 +70,9 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
   __shared__ int s_accept;
   __shared__ int s_ids[kMaxNodes];
   __shared__ int s_path[kMaxNodes];
-  __shared__ double s_sum;
-  __shared__ int s_timeout;
 
-  const int S = P.S;
-  const int b = blockIdx.x / S;
-  const int part = blockIdx.x - b * S;  // this workgroup's share of every residual pass
+  const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  int r = 0;                            // residual passes taken so far (the same in every part)
   const int N = P.N, V = P.V;
   const long long row0 = (long long)b * N;
   if (tid < N) {
@@ -145,7 +91,6 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
   if (tid == 0) {
     s_cd[0] = 0.0;
     s_cd[1] = 1.0;
-    s_timeout = 0;
   }
   __syncthreads();
   int u = 0, n = 0, last = 0;
@@ -210,8 +155,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
     const bool vec4 = P.vec4;
     if (vec4) {
       const int V4 = V >> 2;
-      const int e0 = (int)((long long)V4 * part / S), e1 = (int)((long long)V4 * (part + 1) / S);
-      for (int base = e0; base < e1; base += kIt * kThreads) {
+      for (int base = 0; base < V4; base += kIt * kThreads) {
         float4 pv[kIt], qv[kIt];
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
@@ -221,19 +165,16 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
         }
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
-          if (base + i * kThreads + tid < e1) {
+          if (base + i * kThreads + tid < V4) {
             acc += (weight(pv[i].x, qv[i].x, cn) + weight(pv[i].y, qv[i].y, cn)) +
                    (weight(pv[i].z, qv[i].z, cn) + weight(pv[i].w, qv[i].w, cn));
           }
         }
       }
     } else {
-      const int x0 = (int)((long long)V * part / S), x1 = (int)((long long)V * (part + 1) / S);
-      for (int x = x0 + tid; x < x1; x += kThreads) acc += weight(prow[x], qrow[x], cn);
+      for (int x = tid; x < V; x += kThreads) acc += weight(prow[x], qrow[x], cn);
     }
-    double D = block_sum(acc, s_red);
-    if (S > 1) D = exchange_sum(P, b, part, r, D, &s_sum, &s_timeout);
-    ++r;
+    const double D = block_sum(acc, s_red);
     if (tid == 0 && D > 0.0) {
       s_cd[0] = cn;
       s_cd[1] = D;
@@ -243,14 +184,12 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
   }
   // the walk ends at node u after n acceptances: the final draw (tree_draw_kernel, spread over
   // the GPU) takes max(0, p - c q) of u with this c, and writes its token at out_ids[n]
-  if (part != 0) return;
   if (tid < N) {
     P.out_ids[row0 + tid] = tid < n ? s_ids[tid] : -1;
     P.out_path[row0 + tid] = tid < n ? s_path[tid] : -1;
   }
   if (tid == 0) {
-    // the draw kernel's chunks arrive on the same ticket after the parts' S * r arrivals
-    P.draws[b] = TreeDraw{c_end, c_end_prev, u, n, S > 1 ? S * r : 0, 0};
+    *P.rec.at<TreeDraw>(b, kTreeRecDraw) = TreeDraw{c_end, c_end_prev, u, n};
     P.n_accepted[b] = n;
   }
 }
@@ -258,8 +197,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
 }  // namespace
 
 hipError_t launch_tree_verify(const TreeVerifyParams& p, hipStream_t stream, KTimer t) {
-  hipExtLaunchKernelGGL(tree_verify_kernel, dim3((unsigned)(p.B * p.S)), dim3(kThreads), 0, stream, t.start, t.stop, 0,
-                        p);
+  hipExtLaunchKernelGGL(tree_verify_kernel, dim3((unsigned)p.B), dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
 

@@ -7,21 +7,68 @@
 namespace vap {
 
 // ---------------------------------------------------------------------------------------
-// Verification workspace layout.
-//   [0, 256)            header: err word
-//   [256, ...)          chunk_sums: double [B][C], per-chunk residual / bonus row sums
-//   [..., end)          tickets: int32, ticket of sequence b at end - 4*(b+1) (growing down
-//                       from the end, so its place does not depend on B).  Arrival counters
-//                       return to 0 at the end of every call.  Because every call checks
-//                       bytes >= 256 + B*(256*8 + 4), a call's tickets never overlap the chunk
-//                       sums an earlier call (any B) left behind.
+// Per-sequence records of the verification workspaces.  Sequence b owns the record at
+// base + b * stride; its first 4 bytes are the sequence's arrival ticket, which only the ticket
+// logic ever writes and which is zero between calls (the last arrival of a call resets it).
+// A ticket's place depends on b alone, and no call writes data over any record's ticket, so a
+// zero-filled workspace serves calls of any batch size, k, vocabulary and workspace_bytes
+// (at or above what each call needs), in stream order, without being cleared again.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxChunks = 256;
 constexpr long long kMaxVerifySeqs = 1LL << 22;
 
-inline size_t verify_bytes(long long B) {
-  return align256(256 + (size_t)B * (kMaxChunks * 8 + 4));
+struct SeqRecords {
+  char* base;
+  long long stride;
+  __host__ __device__ int32_t* ticket(long long b) const { return reinterpret_cast<int32_t*>(base + b * stride); }
+  // data of record b, `off` bytes in (off >= 16 keeps it clear of the ticket)
+  template <typename T>
+  __host__ __device__ T* at(long long b, int off) const { return reinterpret_cast<T*>(base + b * stride + off); }
+};
+
+// Publishing an fp64 value to other workgroups through a workspace slot.  The slot holds the
+// complement of the value's bits and is zero between calls, so a reader can tell a value that
+// is not yet visible (zero) from any value: no value published here has all 64 bits set (the
+// values are sums of non-negative weights converted from fp32, and the low 29 bits of a NaN
+// that comes from fp32 are zero).  Writer and reader use agent-scope atomic accesses to the
+// slot itself and nothing else: the reader spins until the slot is nonzero, which per-location
+// coherence guarantees it eventually sees once the writer has stored, and no ordering between
+// different locations is assumed (so no cache-wide writeback or invalidate is needed).  The
+// spin is bounded as a guard; it never runs out while the writer has already stored (the
+// callers only read slots whose writer has arrived or is resident).
+constexpr int kSlotSpinMax = 1 << 18;
+
+__device__ __forceinline__ void publish_slot(unsigned long long* slot, double v) {
+  __hip_atomic_store(slot, ~(unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The published value, waiting until it is visible; *timed_out is set if the guard ran out
+// (the value then reads 0).
+__device__ __forceinline__ double read_slot(unsigned long long* slot, bool* timed_out) {
+  unsigned long long x = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; x == 0ull; ++it) {
+    if (it >= kSlotSpinMax) {
+      *timed_out = true;
+      return 0.0;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    x = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __longlong_as_double((long long)~x);
+}
+
+__device__ __forceinline__ void clear_slot(unsigned long long* slot) {
+  __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// spec_verify workspace:
+//   [0, 256)   header: err word
+//   records    [B] of kVerifyRec bytes: ticket, then at +16 the published chunk sums [C]
+//              (C <= kMaxChunks) of the row the sequence draws from (zero between calls)
+constexpr int kVerifyRecSums = 16;
+constexpr size_t kVerifyRec = kVerifyRecSums + 8 * kMaxChunks;
+
+inline size_t verify_bytes(long long B) { return align256(256 + (size_t)B * kVerifyRec); }
 
 // Statistics of (a chunk of) one logit row z at temperature T > 0: m = max z, argmax = its first
 // index, S = sum_x 2^((z_x - m) * log2(e) / T) (fp64).  At T = 0 only m and argmax are set.
@@ -42,8 +89,7 @@ struct VerifyParams {
   int32_t C;        // chunks per row
   int32_t CS;       // elements per chunk (multiple of 4)
   int32_t* err;
-  int32_t* tickets_end;   // ticket of sequence b is tickets_end[-(b + 1)]
-  double* chunk_sums;
+  SeqRecords rec;   // sequence b: ticket, and its chunk sums at +kVerifyRecSums
   // verification from logits: p and q hold target and draft logits, temps the per-sequence
   // temperature, part the statistics kernel's per-chunk partials ([B(2k+1)][C1])
   const float* temps = nullptr;
@@ -57,12 +103,10 @@ struct VerifyParams {
 //   part            LogitRowStat [R][C1]: per-chunk (max, first argmax, sum of exponentials
 //                   relative to the chunk's max), written by the statistics kernel and merged
 //                   by every verification workgroup for its own sequence
-//   chunk_sums      double [B][kMaxChunks]
-//   tickets         int32 [B], growing down from the end (sequence b at end - 4(b+1)); they
-//                   return to 0 at the end of every call.
-// The data lies in the first half of the workspace and the tickets in the second half (the
-// size required is twice the larger of the two), so no call's tickets ever overlap data an
-// earlier call of another shape left behind.
+//   records         [B] of kVerifyRec bytes, as for spec_verify (ticket, chunk sums)
+// The records' place depends on k and V, so an earlier call of another shape may have left
+// data under this call's tickets and slots: the statistics kernel, which runs first, zeroes
+// the ones this call uses.
 // ---------------------------------------------------------------------------------------
 constexpr int kStatChunk = 2048;        // tokens per statistics item (32 per lane of a wave)
 constexpr int kStatMaxChunks = 512;     // V <= 2^20
@@ -73,7 +117,7 @@ constexpr int kStatWavesPerCU = VAP_STAT_WAVES_PER_CU;   // persistent statistic
 constexpr int kStatWavesPerWG = 4;                       // 256-thread statistics workgroups
 
 struct LogitsLayout {
-  size_t part, chunk_sums, data_end, tickets, total;
+  size_t part, records, total;
 };
 
 inline LogitsLayout logits_layout(long long B, int k, int V) {
@@ -81,11 +125,9 @@ inline LogitsLayout logits_layout(long long B, int k, int V) {
   const long long R = B * (2 * k + 1);
   const long long C1 = (V + kStatChunk - 1) / kStatChunk;
   size_t o = 256;
-  L.part = o;        o = align256(o + (size_t)(R * C1) * sizeof(LogitRowStat));
-  L.chunk_sums = o;  o = align256(o + (size_t)B * kMaxChunks * 8);
-  L.data_end = o;
-  L.tickets = (size_t)B * 4;
-  L.total = 2 * align256(L.data_end > L.tickets ? L.data_end : L.tickets);
+  L.part = o;     o = align256(o + (size_t)(R * C1) * sizeof(LogitRowStat));
+  L.records = o;  o = align256(o + (size_t)B * kVerifyRec);
+  L.total = o;
   return L;
 }
 
@@ -97,6 +139,8 @@ struct LogitStatsParams {
   int32_t B, k, V;
   int32_t C;                // chunks per row (ceil(V / kStatChunk) <= kStatMaxChunks)
   int32_t* err;
+  SeqRecords rec;           // the verification's records: their tickets and first VC slots are zeroed here
+  int32_t VC;               // verification chunks per row
 };
 
 // launchers (defined in the .hip files); return hipError_t of the launch
@@ -108,11 +152,9 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------
-// Tree verification: S workgroups per sequence walk it in lockstep (S = 1 for large batches).
+// Tree verification: one walk workgroup per sequence, then the final draw.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxTreeNodes = 64;
-constexpr int kMaxTreeParts = 16;   // workgroups per sequence in the walk
-constexpr int kTreeRoundTokens = 4 * 8 * 1024;   // tokens one walk workgroup loads per round of a pass
 
 // Where the walk of one sequence ended: the final draw is from max(0, p - c q) of node `node`
 // (c = 0: p itself), or, if those weights are all zero, from max(0, p - c_prev q) (a walk that
@@ -123,23 +165,25 @@ struct TreeDraw {
   double c_prev;
   int32_t node;
   int32_t n;
-  int32_t arrivals; // the walk's arrivals on the sequence's ticket (S * passes when S > 1, else 0)
-  int32_t pad;
+  int32_t pad[2];
 };
 
 // ---------------------------------------------------------------------------------------
 // Tree verification workspace layout.
-//   [0, 256)                 header: err word
-//   [256, 256 + 32B)         TreeDraw [B], written by the walk, read by the draw kernel
-//   [256 + 32B, +2048B)      chunk_sums: double [B][kMaxChunks]; during the walk, the first
-//                            2 * kMaxTreeParts of each sequence's row hold the parts' partial sums
-// A sequence's ticket first counts the walk's arrivals (its parts arrive once per residual
-// pass), then the draw kernel's chunks; the draw's last chunk resets it to 0.
-//   [..., end)               tickets: int32, sequence b at end - 4(b+1); they return to 0
-// Every call checks bytes >= 256 + 2084 B, so a call's tickets never overlap data an earlier
-// call (any B) left behind (the same argument as for the verification workspace).
+//   [0, 256)       header: err word
+//   records        [B] of kTreeRec bytes:
+//     +0              the sequence's ticket (the draw kernel's chunks arrive on it; its last
+//                     chunk resets it to 0)
+//     +kTreeRecDraw   TreeDraw, written by the walk, read by the draw kernel
+//     +kTreeRecSums   published slots [kMaxChunks]: the draw's chunk sums (zero between calls,
+//                     see publish_slot)
 // ---------------------------------------------------------------------------------------
-inline size_t tree_verify_bytes(long long B) { return align256(256 + (size_t)B * (32 + kMaxChunks * 8 + 4)); }
+constexpr int kTreeRecDraw = 16;
+constexpr int kTreeRecSums = kTreeRecDraw + (int)sizeof(TreeDraw);
+constexpr size_t kTreeRec = kTreeRecSums + 8 * kMaxChunks;
+static_assert(kTreeRecSums % 16 == 0, "tree record fields stay 16-byte aligned");
+
+inline size_t tree_verify_bytes(long long B) { return align256(256 + (size_t)B * kTreeRec); }
 
 struct TreeVerifyParams {
   const float* p;           // [B][N][V] target rows per node
@@ -153,11 +197,7 @@ struct TreeVerifyParams {
   int32_t B, N, V;
   bool vec4;                // V % 4 == 0 and p, q 16-byte aligned
   int32_t* err;
-  TreeDraw* draws;          // [B], written at the end of the walk
-  int32_t S;                // workgroups per sequence (1 .. kMaxTreeParts)
-  double* xch;              // partial-sum slots: sequence b at xch + b * xch_stride, [2][S]
-  int32_t xch_stride;
-  int32_t* tickets_end;     // sequence b's ticket is tickets_end[-(b + 1)] (zero at the start of a call)
+  SeqRecords rec;           // TreeDraw of each sequence, written at the end of its walk
 };
 
 struct TreeDrawParams {
@@ -165,11 +205,9 @@ struct TreeDrawParams {
   const float* q;
   const float* uniforms;    // [B][N]: uniforms[b][0] drives the final draw
   int32_t* out_ids;         // [B][N]: entry n of sequence b receives the drawn token
-  const TreeDraw* draws;
   int32_t B, N, V;
   int32_t C, CS;            // chunks per row and their length (multiple of 4, <= 4096)
-  double* chunk_sums;       // [B][C]
-  int32_t* tickets_end;     // ticket of sequence b is tickets_end[-(b + 1)]
+  SeqRecords rec;           // ticket, TreeDraw, chunk sums [C]
   int32_t* err;
 };
 
