@@ -13,8 +13,13 @@ Default run (one JSON line on stdout):
     torch's softmax followed by spec_verify;
   * kv_cache: kv_append of the decode batch's new rows (bf16 and 8-bit), append + attention
     back to back, and kv_commit of the tree step's accepted paths;
+  * attention_configs: every attention workload (decode, verify, 70B share, mixed step, tree
+    batch; bf16 and 8-bit KV) with its algorithmic bytes, step and kernel time, GB/s and
+    fraction of the HBM peak;
+  * spec_verify_sweep: spec_verify at vocabulary 128256 over batch sizes 16 .. 1024;
   * cpu_baseline: the fp64 CPU oracle on the same decode batch, on up to 16 host cores (forked
-    workers, before the GPU is touched), with the one-core rate beside it.
+    workers, before the GPU is touched; the host's core count beside it), with the one-core
+    rate, and the verifier oracle's tokens/s on one core.
 
 Inputs are resident in HBM before timing starts.  The KV pool (and the verifier's
 probability rows) are rotated over several device copies so that consecutive steps never
@@ -374,6 +379,114 @@ def run_attention_only(args, dev, name):
                       "kernel_GB_per_s": round(nbytes / (kms / max(cnt, 1) * 1e-3) / 1e9, 2)}))
 
 
+ATTN_CONFIG_NAMES = ["llama3_8b_decode", "spec_verify_step", "llama70b_share", "mixed_step", "tree_verify_step"]
+
+
+def measure_attention(name, dev, args, kv_format="bf16"):
+    """One attention workload in the benchmark's launch configuration: K steps back to back
+    (inputs resident, pools rotated past the MALL), the whole step (attention + combine
+    kernels) by stream events and the attention kernel by the library's kernel timer."""
+    import verify_attention_paged_amd as vap
+    inp, d, pools, out, ws, nbytes = setup_attention(name, dev, kv_format)
+    sc = d["scales"]
+    step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
+                                         d["q_lens"], out=out, workspace=ws,
+                                         kv_scales=None if sc is None else sc[i % len(pools)],
+                                         tree_mask=d["tree_mask"])
+    vap.timer_enable(True)
+    time_loop(step, 0, args.warmup)
+    vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    ms, _ = time_loop(step, args.steps, 0)
+    kms, cnt = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
+    vap.timer_enable(False)
+    if vap.get_device_error(ws):
+        raise RuntimeError(f"device reported a data error on {name} ({kv_format})")
+    kms /= max(1, cnt)
+    gbs, kgbs = nbytes / (ms * 1e-3) / 1e9, nbytes / (kms * 1e-3) / 1e9
+    flops = sum(4 * inp.head_dim * inp.num_q_heads * sum(int(L) - int(Q) + i + 1 for i in range(int(Q)))
+                for L, Q in zip(inp.ctx_lens.tolist(), inp.q_lens.tolist()))
+    log(f"{name} ({kv_format}): step {ms * 1e3:.1f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak); "
+        f"attention kernel {kms * 1e3:.1f} us -> {kgbs:.0f} GB/s ({kgbs / HBM_PEAK_GBS:.3f})")
+    del pools, sc
+    return {"kv_format": kv_format, "seqs": inp.num_seqs, "rows": inp.total_q, "tokens": int(inp.ctx_lens.sum()),
+            "bytes_per_step": nbytes, "flops_per_step": flops, "ms_per_step": round(ms, 5),
+            "GB_per_s": round(gbs, 2), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "attention_kernel_ms": round(kms, 5), "kernel_GB_per_s": round(kgbs, 2),
+            "kernel_frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4),
+            "rows_per_s": round(inp.total_q / (ms * 1e-3), 1)}
+
+
+SWEEP_BATCHES = (16, 64, 256, 1024)
+
+
+def spec_verify_sweep(dev, args):
+    """spec_verify at vocabulary 128256, k = 4, over batch sizes: the verify batch's 16 sequences
+    tiled B/16 times (same rows, so the same acceptance and bytes per sequence), probability
+    rows rotated past the MALL."""
+    import torch
+    import verify_attention_paged_amd as vap
+    import workloads
+    ver = workloads.verify_config("spec_verify_step")
+    res = {}
+    for B in SWEEP_BATCHES:
+        r = B // ver.num_seqs
+        p = ver.p.to(dev).repeat(r, 1, 1)
+        ps = rotating_copies(p, 768 << 20)
+        qs = [ver.q.to(dev).repeat(r, 1, 1) for _ in ps]
+        ids, uni = ver.draft_ids.to(dev).repeat(r, 1), ver.uniforms.to(dev).repeat(r, 1)
+        out_ids = torch.empty((B, ver.k + 1), dtype=torch.int32, device=dev)
+        n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = vap.verify_workspace(B, ver.k, ver.vocab, dev)
+        step = lambda i: vap.spec_verify(ps[i % len(ps)], qs[i % len(qs)], ids, uni, out_ids, n_acc, workspace=ws)
+        vap.timer_enable(True)
+        time_loop(step, 0, args.warmup)
+        vap.timer_read(vap.TIMER_VERIFY, reset=True)
+        ms, _ = time_loop(step, args.steps, 0)
+        kms, cnt = vap.timer_read(vap.TIMER_VERIFY, reset=True)
+        vap.timer_enable(False)
+        kms /= max(1, cnt)
+        n_host = n_acc.cpu().numpy()
+        nbytes = verify_bytes(n_host, ver.k, ver.vocab)
+        emitted = int((n_host + 1).sum())
+        kgbs = nbytes / (kms * 1e-3) / 1e9
+        log(f"spec_verify B={B}: kernel {kms * 1e3:.2f} us -> {kgbs:.0f} GB/s ({kgbs / HBM_PEAK_GBS:.3f} of peak), "
+            f"{emitted / (kms * 1e-3) / 1e6:.1f} M tokens/s; {ms * 1e3:.2f} us per call")
+        res[str(B)] = {"bytes": nbytes, "kernel_ms": round(kms, 5), "ms_per_call": round(ms, 5),
+                       "kernel_GB_per_s": round(kgbs, 2), "kernel_frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4),
+                       "tokens_emitted": emitted, "tokens_per_s": round(emitted / (kms * 1e-3), 1)}
+        del ps, qs, p
+        torch.cuda.synchronize()
+    return res
+
+
+def cpu_verifier_baseline(budget_s=5.0):
+    """The sequential fp64 verifier oracle on the verify batch (16 sequences, k 4, vocab 128256)
+    on one core: tokens emitted per second and GB/s-equivalent of the same algorithmic bytes."""
+    import numpy as np
+    import workloads
+    from threadpoolctl import threadpool_limits
+    from oracle import spec_verify as OS
+    ver = workloads.verify_config("spec_verify_step")
+    p = ver.p.numpy().astype(np.float64)
+    q = ver.q.numpy().astype(np.float64)
+    ids, u = ver.draft_ids.numpy(), ver.uniforms.numpy().astype(np.float64)
+    passes, emitted, nbytes = 0, 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            _, n = OS.spec_verify(p, q, ids, u)
+            passes += 1
+            emitted += int((n + 1).sum())
+            nbytes += verify_bytes(n, ver.k, ver.vocab)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"tokens_per_s": round(emitted / dt, 1), "GB_per_s": round(nbytes / dt / 1e9, 4), "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole spec_verify_step batch (16 sequences, k 4, vocab 128256, fp64 NumPy, 1 BLAS "
+                      f"thread), {passes} passes in {dt:.1f} s"}
+
+
 def run_default(args, dev):
     import numpy as np
     import torch
@@ -596,8 +709,19 @@ def run_default(args, dev):
                "decode_step_with_append_ms": round(as_ms, 5),
                "commit_tree_kernel_ms": round(ckern, 5), "commit_rows_moved": moved, "commit_bytes": cb}
 
+    # ---- every attention workload in one table (configs 2-5 and the tree batch; bf16 and 8-bit)
+    configs = {}
+    if not args.no_configs:
+        for nm in ATTN_CONFIG_NAMES:
+            configs[nm] = measure_attention(nm, dev, args)
+            if nm != "tree_verify_step":
+                configs[nm + " u8"] = measure_attention(nm, dev, args, kv_format="u8")
+    # ---- spec_verify over batch sizes (vocabulary 128256)
+    sweep = spec_verify_sweep(dev, args) if not args.no_configs else None
+
     # ---- CPU baseline (oracle), rank 0 at N = 1 only
     cpu = None
+    cpu_verify = None
     if not args.no_cpu_baseline:
         one = cpu_baseline(inp, nbytes, args.cpu_seconds)
         log(f"cpu oracle, 1 core: {one['value']} GB/s ({one['sample']})")
@@ -606,6 +730,10 @@ def run_default(args, dev):
             log(f"cpu oracle, {cpu['cores']} cores: {cpu['value']} GB/s ({cpu['sample']})")
             cpu["single_core_value"] = one["value"]
             cpu["single_core_sample"] = one["sample"]
+        cpu["host_cores"] = os.cpu_count()
+        cpu_verify = cpu_verifier_baseline(min(5.0, args.cpu_seconds))
+        log(f"cpu verifier oracle, 1 core: {cpu_verify['tokens_per_s']} tokens/s, {cpu_verify['GB_per_s']} GB/s")
+        cpu["verifier"] = cpu_verify
 
     traffic = read_traffic()
     line = {
@@ -661,6 +789,8 @@ def run_default(args, dev):
                             "speedup_vs_bf16_step": round(ms / qms, 3)},
         "kv_cache": kv_line,
         "logits_verify_step": logits_line,
+        "attention_configs": configs or None,
+        "spec_verify_sweep": sweep,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attn_main_kernel<128,16,1>",
@@ -681,6 +811,8 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="skip the HIP graph timings (eager steps only)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload attention table and the spec_verify batch sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
