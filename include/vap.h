@@ -204,6 +204,24 @@ int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const 
                 int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * spec_verify_static -- spec_verify without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ *   p, q, draft_ids, uniforms, out_ids, n_accepted, num_seqs, k, vocab  as for spec_verify,
+ *                  with 0 <= num_seqs <= 4096 (VAP_EINVAL above: use spec_verify).
+ *   device_error   NULL, or a caller-owned device int32 into which the kernel ORs the
+ *                  VAP_DERR_* bits of the call (it is not cleared first).
+ *
+ * The scratch is a static device array of the library (8,454,400 bytes, one per device), looked up
+ * and zero-filled at the first call on each device; nothing is allocated or freed by any call.
+ * Every call on a device uses the same array, so calls on one device must not overlap in time
+ * (one stream, or synchronised).  Results are those of spec_verify.
+ */
+int spec_verify_static(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
+                       int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
+                       int32_t* device_error, void* stream);
+
 /* Workspace bytes spec_verify_logits needs (0 on bad sizes). */
 size_t vap_verify_logits_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab);
 

@@ -6,6 +6,7 @@ memory and streams only.
 
     paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale=0.0)
     spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None)
+    spec_verify_static(p, q, draft_ids, uniforms, out_ids, n_accepted)   (no workspace)
     spec_verify_tree(p, q, parents, tokens, uniforms)
     spec_verify_logits(target_logits, draft_logits, draft_ids, uniforms, temperatures)
     kv_append(k_new, v_new, kv_pool, block_tables, ctx_lens, q_lens)
@@ -44,6 +45,7 @@ from ._binding import (  # noqa: F401
     load_library,
     paged_attn_step,
     spec_verify,
+    spec_verify_static,
     spec_verify_tree,
     spec_verify_logits,
     verify_logits_workspace,

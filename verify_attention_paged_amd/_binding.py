@@ -56,6 +56,7 @@ SIGNATURES = {
     "paged_attn_step_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "spec_verify_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "vap_verify_logits_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify_logits": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "vap_tree_verify_workspace_bytes": (_sz, [_i32]),
@@ -229,14 +230,8 @@ def verify_workspace(num_seqs: int, k: int, vocab: int, device=None) -> torch.Te
     return torch.zeros(n, dtype=torch.uint8, device=torch.device(device or "cuda"))
 
 
-def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
-                workspace: torch.Tensor | None = None, stream=None):
-    """Modified rejection sampling; see ``spec_verify`` in include/vap.h.
-
-    p fp32 [B, k+1, V]; q fp32 [B, k, V]; draft_ids int32 [B, k]; uniforms fp32 [B, k+1].
-    Returns (out_ids int32 [B, k+1], n_accepted int32 [B]).
-    """
-    lib = load_library()
+def _verify_args(p, q, draft_ids, uniforms, out_ids, n_accepted):
+    """Checks of spec_verify's tensors; returns (B, k, V, out_ids, n_accepted, q ptr, ids ptr)."""
     dev = p.device
     _need(p, "p", torch.float32, 3)
     B, k1, V = p.shape
@@ -255,15 +250,46 @@ def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
         n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     _need(out_ids, "out_ids", torch.int32, 2, dev)
     _need(n_accepted, "n_accepted", torch.int32, 1, dev)
+    qp = q.data_ptr() if k > 0 else None
+    ip = draft_ids.data_ptr() if k > 0 else None
+    return B, k, V, out_ids, n_accepted, qp, ip
+
+
+def spec_verify(p, q, draft_ids, uniforms, out_ids=None, n_accepted=None, *,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Modified rejection sampling; see ``spec_verify`` in include/vap.h.
+
+    p fp32 [B, k+1, V]; q fp32 [B, k, V]; draft_ids int32 [B, k]; uniforms fp32 [B, k+1].
+    Returns (out_ids int32 [B, k+1], n_accepted int32 [B]).
+    """
+    lib = load_library()
+    dev = p.device
+    B, k, V, out_ids, n_accepted, qp, ip = _verify_args(p, q, draft_ids, uniforms, out_ids, n_accepted)
     if workspace is None:
         workspace = verify_workspace(B, k, V, dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    qp = q.data_ptr() if k > 0 else None
-    ip = draft_ids.data_ptr() if k > 0 else None
     with _on(dev):
         rc = lib.spec_verify(p.data_ptr(), qp, ip, uniforms.data_ptr(), out_ids.data_ptr(),
                              n_accepted.data_ptr(), B, k, V, workspace.data_ptr(),
                              workspace.numel(), _stream(stream))
+    _check(rc)
+    return out_ids, n_accepted
+
+
+def spec_verify_static(p, q, draft_ids, uniforms, out_ids, n_accepted, *, device_error=None, stream=None):
+    """spec_verify without a workspace (the library's static device scratch); see
+    ``spec_verify_static`` in include/vap.h.  Outputs are given by the caller; ``device_error``
+    is an optional int32 [1] device tensor receiving the VAP_DERR_* bits."""
+    lib = load_library()
+    dev = p.device
+    B, k, V, out_ids, n_accepted, qp, ip = _verify_args(p, q, draft_ids, uniforms, out_ids, n_accepted)
+    ep = None
+    if device_error is not None:
+        _need(device_error, "device_error", torch.int32, 1, dev)
+        ep = device_error.data_ptr()
+    with _on(dev):
+        rc = lib.spec_verify_static(p.data_ptr(), qp, ip, uniforms.data_ptr(), out_ids.data_ptr(),
+                                    n_accepted.data_ptr(), B, k, V, ep, _stream(stream))
     _check(rc)
     return out_ids, n_accepted
 

@@ -19,7 +19,8 @@ OBJDIR = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIBRARY = os.path.join(LIBDIR, "libvap.so")
 
-SOURCES = ["api.cpp", "attn_plan.hip", "attn_paged.hip", "attn_combine.hip", "spec_verify.hip", "spec_verify_tree.hip", "kv_cache.hip", "util.hip"]
+SOURCES = ["api.cpp", "attn_plan.hip", "attn_paged.hip", "attn_combine.hip", "spec_verify.hip", "spec_verify_tree.hip",
+           "spec_verify_static.hip", "kv_cache.hip", "util.hip"]
 
 ARCH = "gfx950"
 # packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops); hipcc's host

@@ -239,6 +239,60 @@ const DevInfo* gfx950_or_null() {
 
 }  // namespace
 
+namespace vap {
+
+int host_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int verify_dispatch(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
+                    int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
+                    char* records, int32_t* err, hipStream_t stream) {
+  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs)
+    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
+  if (k < 0 || k > 64) return fail(VAP_EINVAL, "k=%d outside [0, 64]", k);
+  if (vocab < 1) return fail(VAP_EINVAL, "vocab=%d < 1", vocab);
+  if ((long long)vocab > (long long)kMaxChunks * 4096)
+    return fail(VAP_EINVAL, "vocab=%d above %d", vocab, kMaxChunks * 4096);
+  if (num_seqs == 0) return ok();
+  if (!p || !uniforms || !out_ids || !n_accepted || !records || !err || (k > 0 && (!q || !draft_ids)))
+    return fail(VAP_EINVAL, "NULL data pointer");
+  const DevInfo* d = device_info();
+  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
+
+  // chunks per row: about two workgroups per CU over the whole batch, at least 256 and at
+  // most 4096 elements per chunk (the selecting workgroup holds a chunk in registers)
+  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
+  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
+  C = std::max(1LL, std::min(C, cmax));
+  C = std::max(C, ((long long)vocab + 4095) / 4096);
+  long long CS = ((long long)vocab + C - 1) / C;
+  CS = (CS + 3) / 4 * 4;
+  C = ((long long)vocab + CS - 1) / CS;
+
+  VerifyParams P;
+  P.p = p;
+  P.q = q;
+  P.draft_ids = draft_ids;
+  P.uniforms = uniforms;
+  P.out_ids = out_ids;
+  P.n_accepted = n_accepted;
+  P.B = num_seqs;
+  P.k = k;
+  P.V = vocab;
+  P.C = (int)C;
+  P.CS = (int)CS;
+  P.err = err;
+  P.rec = SeqRecords{records, (long long)kVerifyRec};
+  const bool vec4 = (vocab % 4 == 0) &&
+                    ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(k ? q : p)) & 15) == 0;
+  const KTimer t = timer_slot(1);
+  hipError_t e = launch_spec_verify(P, vec4, stream, t);
+  timer_commit(1, t, e);
+  if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace vap
+
 extern "C" {
 
 const char* vap_strerror(int code) {
@@ -409,55 +463,15 @@ size_t vap_verify_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {
 int spec_verify(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
                 int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
                 void* workspace, size_t workspace_bytes, void* stream_) {
-  if (num_seqs < 0 || num_seqs > kMaxVerifySeqs)
-    return fail(VAP_EINVAL, "num_seqs=%d outside [0, %lld]", num_seqs, kMaxVerifySeqs);
-  if (k < 0 || k > 64) return fail(VAP_EINVAL, "k=%d outside [0, 64]", k);
-  if (vocab < 1) return fail(VAP_EINVAL, "vocab=%d < 1", vocab);
-  if (num_seqs == 0) return ok();
-  if (!p || !uniforms || !out_ids || !n_accepted || !workspace || (k > 0 && (!q || !draft_ids)))
-    return fail(VAP_EINVAL, "NULL data pointer");
-  if (workspace_bytes < vap_verify_workspace_bytes(num_seqs, k, vocab))
+  if (num_seqs > 0 && !workspace) return fail(VAP_EINVAL, "NULL data pointer");
+  if (num_seqs > 0 && num_seqs <= kMaxVerifySeqs && k >= 0 && k <= 64 && vocab >= 1 &&
+      workspace_bytes < vap_verify_workspace_bytes(num_seqs, k, vocab))
     return fail(VAP_ENOSPC, "workspace of %zu bytes is below %zu", workspace_bytes,
                 vap_verify_workspace_bytes(num_seqs, k, vocab));
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(VAP_EINVAL, "workspace must be 256-byte aligned");
-  const DevInfo* d = device_info();
-  if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
-
-  // chunks per row: about two workgroups per CU over the whole batch, at least 256 and at
-  // most 4096 elements per chunk (the selecting workgroup holds a chunk in registers)
-  if ((long long)vocab > (long long)kMaxChunks * 4096)
-    return fail(VAP_EINVAL, "vocab=%d above %d", vocab, kMaxChunks * 4096);
-  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
-  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
-  C = std::max(1LL, std::min(C, cmax));
-  C = std::max(C, ((long long)vocab + 4095) / 4096);
-  long long CS = ((long long)vocab + C - 1) / C;
-  CS = (CS + 3) / 4 * 4;
-  C = ((long long)vocab + CS - 1) / CS;
-
   char* ws = static_cast<char*>(workspace);
-  VerifyParams P;
-  P.p = p;
-  P.q = q;
-  P.draft_ids = draft_ids;
-  P.uniforms = uniforms;
-  P.out_ids = out_ids;
-  P.n_accepted = n_accepted;
-  P.B = num_seqs;
-  P.k = k;
-  P.V = vocab;
-  P.C = (int)C;
-  P.CS = (int)CS;
-  P.err = reinterpret_cast<int32_t*>(ws);
-  P.rec = SeqRecords{ws + 256, (long long)kVerifyRec};
-  const bool vec4 = (vocab % 4 == 0) &&
-                    ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(k ? q : p)) & 15) == 0;
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const KTimer t = timer_slot(1);
-  hipError_t e = launch_spec_verify(P, vec4, stream, t);
-  timer_commit(1, t, e);
-  if (e != hipSuccess) return fail(VAP_EHIP, "spec_verify launch: %s", hipGetErrorString(e));
-  return ok();
+  return vap::verify_dispatch(p, q, draft_ids, uniforms, out_ids, n_accepted, num_seqs, k, vocab, ws + 256,
+                              reinterpret_cast<int32_t*>(ws), static_cast<hipStream_t>(stream_));
 }
 
 size_t vap_verify_logits_workspace_bytes(int32_t num_seqs, int32_t k, int32_t vocab) {

@@ -148,6 +148,15 @@ hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stre
 hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t = {});
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
+
+// Host side of spec_verify with its records (kVerifyRec bytes per sequence, tickets and slots
+// zero) at `records` and its device error word at `err`: checks the call and launches the
+// kernel; returns a VAP_* code (api.cpp, shared by spec_verify and spec_verify_static).
+int verify_dispatch(const float* p, const float* q, const int32_t* draft_ids, const float* uniforms,
+                    int32_t* out_ids, int32_t* n_accepted, int32_t num_seqs, int32_t k, int32_t vocab,
+                    char* records, int32_t* err, hipStream_t stream);
+// Records a host-side error for vap_last_error_message(); returns `code`.
+int host_error(int code, const char* msg);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
