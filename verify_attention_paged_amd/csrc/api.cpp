@@ -258,16 +258,7 @@ int verify_dispatch(const float* p, const float* q, const int32_t* draft_ids, co
   const DevInfo* d = device_info();
   if (d == nullptr || !d->gfx950) return fail(VAP_ENODEV, "current device is not gfx950 (%s)", d ? d->arch : "none");
 
-  // chunks per row: about two workgroups per CU over the whole batch, at least 256 and at
-  // most 4096 elements per chunk (the selecting workgroup holds a chunk in registers)
-  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
-  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
-  C = std::max(1LL, std::min(C, cmax));
-  C = std::max(C, ((long long)vocab + 4095) / 4096);
-  long long CS = ((long long)vocab + C - 1) / C;
-  CS = (CS + 3) / 4 * 4;
-  C = ((long long)vocab + CS - 1) / CS;
-
+  const DrawChunks ch = draw_chunks(num_seqs, vocab, d->num_cus);
   VerifyParams P;
   P.p = p;
   P.q = q;
@@ -278,8 +269,9 @@ int verify_dispatch(const float* p, const float* q, const int32_t* draft_ids, co
   P.B = num_seqs;
   P.k = k;
   P.V = vocab;
-  P.C = (int)C;
-  P.CS = (int)CS;
+  P.C = ch.C;
+  P.CS = ch.CS;
+  P.WPS = ch.WPS;
   P.err = err;
   P.rec = SeqRecords{records, (long long)kVerifyRec};
   const bool vec4 = (vocab % 4 == 0) &&
@@ -522,13 +514,7 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   const int stat_wg = (int)((stat_waves + kStatWavesPerWG - 1) / kStatWavesPerWG);
 
   // verification chunks: as spec_verify
-  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
-  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
-  C = std::max(1LL, std::min(C, cmax));
-  C = std::max(C, ((long long)vocab + 4095) / 4096);
-  long long CS = ((long long)vocab + C - 1) / C;
-  CS = (CS + 3) / 4 * 4;
-  C = ((long long)vocab + CS - 1) / CS;
+  const DrawChunks ch = draw_chunks(num_seqs, vocab, d->num_cus);
   VerifyParams P;
   P.p = target_logits;
   P.q = draft_logits;
@@ -539,11 +525,12 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   P.B = num_seqs;
   P.k = k;
   P.V = vocab;
-  P.C = (int)C;
-  P.CS = (int)CS;
+  P.C = ch.C;
+  P.CS = ch.CS;
+  P.WPS = ch.WPS;
   P.err = reinterpret_cast<int32_t*>(ws);
   P.rec = rec;
-  S.VC = (int)C;
+  S.VC = ch.C;
   P.temps = temperatures;
   P.part = S.part;
   P.C1 = (int)C1;
@@ -600,14 +587,8 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.err = reinterpret_cast<int32_t*>(ws);
   P.rec = SeqRecords{ws + 256, (long long)kTreeRec};
 
-  // draw chunks: as spec_verify (about two workgroups per CU over the batch)
-  long long C = (2LL * d->num_cus + num_seqs - 1) / num_seqs;
-  const long long cmax = std::max(1LL, std::min((long long)kMaxChunks, ((long long)vocab + 255) / 256));
-  C = std::max(1LL, std::min(C, cmax));
-  C = std::max(C, ((long long)vocab + 4095) / 4096);
-  long long CS = ((long long)vocab + C - 1) / C;
-  CS = (CS + 3) / 4 * 4;
-  C = ((long long)vocab + CS - 1) / CS;
+  // draw chunks: as spec_verify
+  const DrawChunks ch = draw_chunks(num_seqs, vocab, d->num_cus);
   TreeDrawParams D;
   D.p = p;
   D.q = q;
@@ -616,8 +597,9 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   D.B = num_seqs;
   D.N = num_nodes;
   D.V = vocab;
-  D.C = (int)C;
-  D.CS = (int)CS;
+  D.C = ch.C;
+  D.CS = ch.CS;
+  D.WPS = ch.WPS;
   D.rec = P.rec;
   D.err = P.err;
 

@@ -12,13 +12,15 @@
 //   4. t = u_k * Z and the emitted token is the smallest x with C_x > t;
 //   5. out_ids = accepted drafts, the emitted token, then -1; n_accepted = n.
 //
-// How: one launch, one workgroup per (sequence, vocabulary chunk).  Every workgroup redoes the k gathers of
-// step 1 (2k scattered loads, cheaper than a second launch), streams its chunk of the row it
-// needs with 16-byte loads, and publishes the chunk's fp64 sum.  An arrival counter per
-// sequence elects the last workgroup, which scans the C chunk sums, finds the chunk that
-// holds t and rescans only that chunk to pick the token.  The counter returns to 0, so the
-// workspace is ready for the next call.  All bytes of the vocabulary are read once, in
-// parallel over about 2 x (number of CUs) workgroups.
+// How: one launch.  The vocabulary is cut into C chunks of at most 4096 tokens (about two per
+// CU over the batch), and each sequence gets WPS workgroups that take consecutive chunks (one
+// chunk each for small batches; for large batches a workgroup streams many chunks, so the
+// accept tests are not paid per chunk).  Every workgroup redoes the k gathers of step 1 (2k
+// scattered loads, cheaper than a second launch), streams its chunks of the row it needs with
+// 16-byte loads and publishes each chunk's fp64 sum.  An arrival counter per sequence elects
+// the last workgroup, which scans the C chunk sums, finds the chunk that holds t and rescans only
+// that chunk to pick the token.  The counter and the published sums return to 0, so the workspace
+// is ready for the next call.  All bytes of the vocabulary are read once.
 //
 // Verification from logits (tempatgunting.com article, section "Speculative Decoding: Turning
 // Verification Parallelism into Latency Wins": the verify pass yields logits and tokens are
@@ -170,7 +172,19 @@ __device__ __forceinline__ int block_max(int x, int* s_int) {
 // the chunk read a clamped in-bounds address and are discarded.
 constexpr int kMaxChunkLen = 4096;
 
-template <bool VEC4, class W>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load, non-temporal for NT: bytes that no other load of the call reads again, streamed by
+// workgroups that read many chunks, run closer to the HBM peak that way
+template <bool NT>
+__device__ __forceinline__ float4 ld_f4(const float* p) {
+  f32x4 v;
+  if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else v = *reinterpret_cast<const f32x4*>(p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool VEC4, class W, bool NT = false>
 __device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, const W& w, int x0, int x1) {
   const bool residual = w.residual;
   double acc = 0.0;
@@ -180,8 +194,8 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int x = min(x0 + 4 * ((int)threadIdx.x + i * kThreads), x1 - 4);
-      pv[i] = *reinterpret_cast<const float4*>(prow + x);
-      qv[i] = residual ? *reinterpret_cast<const float4*>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pv[i] = ld_f4<NT>(prow + x);
+      qv[i] = residual ? ld_f4<NT>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
@@ -302,16 +316,30 @@ __device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool
   }
 }
 
-// One workgroup's chunk sum is published to its slot, then the workgroup arrives on the
-// sequence's ticket (thread 0 only).  The workgroup that takes the last ticket (value `last`)
-// resets the ticket for the next call and returns true; it then reads every chunk's slot,
-// waiting for any not yet visible (read_slot), and clears them.
-__device__ __forceinline__ bool publish_and_arrive(unsigned long long* slot, double value, int32_t* ticket, int last) {
-  publish_slot(slot, value);
+// A workgroup that has published the sums of its chunks arrives on the sequence's ticket (thread
+// 0 only).  The workgroup that takes the last ticket (value `last`) resets the ticket for the next
+// call and returns true; it then reads every chunk's slot, waiting for any not yet visible
+// (read_slot), and clears them.
+__device__ __forceinline__ bool arrive(int32_t* ticket, int last) {
   const int t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (t != last) return false;
   __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+
+// Sums of w over this workgroup's chunks [c0, c1) of the row(s) at prow / qrow, each published to
+// its slot.  Launches whose workgroups take kNtChunks chunks or more (large batches, where the draw
+// streams at bandwidth) load them non-temporally (NT): 163 against 177 us at 1024 sequences of
+// vocabulary 128256, while small batches, bound by their round trips, measured slightly slower.
+
+template <bool VEC4, bool NT, class W>
+__device__ __forceinline__ void publish_chunk_sums(const float* prow, const float* qrow, const W& w, int c0, int c1,
+                                                   int CS, int V, unsigned long long* slots, double* s_red) {
+  for (int c = c0; c < c1; ++c) {
+    const int x0 = c * CS;
+    const double part = block_sum(chunk_partial<VEC4, W, NT>(prow, qrow, w, x0, min(V, x0 + CS)), s_red);
+    if (threadIdx.x == 0) publish_slot(slots + c, part);
+  }
 }
 
 // Step 4 of a draw by the last workgroup of a sequence: with every chunk's sum of w published
@@ -417,7 +445,7 @@ __device__ int finish_draw(unsigned long long* slots, int C, int CS, int V, floa
 // that is negative or not finite (reported), is greedy.
 __device__ __forceinline__ bool greedy_temperature(float T) { return !(T > 0.f && T <= FLT_MAX); }
 
-template <bool VEC4, bool LOGITS>
+template <bool VEC4, bool LOGITS, bool NT>
 __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParams P) {
   using W = std::conditional_t<LOGITS, LogitWeight, ProbWeight>;
   __shared__ int s_n;
@@ -432,9 +460,11 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   __shared__ uint4 s_stage[LOGITS ? kMergeStage : 1];           // staged chunk partials
   __shared__ double s_tab[LOGITS ? 64 : 1];                     // 2^(j/64)
 
-  const int C = P.C;
-  const int b = blockIdx.x / C;
-  const int cidx = blockIdx.x - b * C;
+  const int C = P.C, WPS = P.WPS;
+  const int b = blockIdx.x / WPS;
+  const int wg = blockIdx.x - b * WPS;            // this workgroup's chunks: [c0, c1)
+  const int G = (C + WPS - 1) / WPS;
+  const int c0 = wg * G, c1 = min(C, c0 + G);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int k = P.k, V = P.V;
@@ -444,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if constexpr (LOGITS) {
     const float T = P.temps[b];
     greedy = greedy_temperature(T);
-    if (!(T >= 0.f && T <= FLT_MAX) && cidx == 0 && tid == 0) atomicOr(P.err, VAP_DERR_TEMP);
+    if (!(T >= 0.f && T <= FLT_MAX) && wg == 0 && tid == 0) atomicOr(P.err, VAP_DERR_TEMP);
     cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
     fill_exp2_table(s_tab);   // visible after the merge's first barrier
     merge_row_stats(P.part + srow * P.C1, P.C1, greedy ? k + 1 : 2 * k + 1, greedy, cT, s_st, s_stage, s_tab);
@@ -457,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     if (lane < k) {
       const int x = P.draft_ids[(long long)b * k + lane];
       const bool inside = x >= 0 && x < V;
-      if (!inside && cidx == 0) atomicOr(P.err, VAP_DERR_DRAFT_ID);
+      if (!inside && wg == 0) atomicOr(P.err, VAP_DERR_DRAFT_ID);
       const double r = (double)P.uniforms[(long long)b * (k + 1) + lane];
       if constexpr (!LOGITS) {
         float pv = 0.f, qv = 0.f;
@@ -488,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const int n = s_n;
   if constexpr (LOGITS) {
     if (greedy) {   // exact matching: the emitted token is the argmax of target row n
-      if (cidx == 0) {
+      if (wg == 0) {
         if (tid <= k)
           P.out_ids[(long long)b * (k + 1) + tid] = tid < n ? s_ids[tid] : (tid == n ? s_st[n].argmax : -1);
         if (tid == 0) P.n_accepted[b] = n;
@@ -508,12 +538,10 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
     w = ProbWeight{residual};
   }
 
-  // 2-3. this chunk's sum of w
-  const int x0 = cidx * P.CS;
-  const int x1 = min(V, x0 + P.CS);
-  double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
+  // 2-3. the sums of w over this workgroup's chunks
   unsigned long long* sums = P.rec.at<unsigned long long>(b, kVerifyRecSums);
-  if (tid == 0) s_last = publish_and_arrive(sums + cidx, part, P.rec.ticket(b), C - 1);
+  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, V, sums, s_red);
+  if (tid == 0) s_last = arrive(P.rec.ticket(b), WPS - 1);
   __syncthreads();
   if (!s_last) return;
 
@@ -650,27 +678,27 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
 // one workgroup per (sequence, vocabulary chunk) sums its chunk of the weights max(0, p - c q)
 // of the node where the sequence's walk ended and publishes the sum; the last workgroup of the
 // sequence finds the token t = u_0 Z falls on, in ascending token id, as in spec_verify.
-template <bool VEC4>
+template <bool VEC4, bool NT>
 __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParams P) {
   __shared__ int s_last;
   __shared__ double s_loc[2];
   __shared__ int s_cstar;
   __shared__ double s_red[kThreads / 64];
   __shared__ int s_int[kThreads / 64];
-  const int C = P.C;
-  const int b = blockIdx.x / C;
-  const int cidx = blockIdx.x - b * C;
+  const int C = P.C, WPS = P.WPS;
+  const int b = blockIdx.x / WPS;
+  const int wg = blockIdx.x - b * WPS;            // this workgroup's chunks: [c0, c1)
+  const int G = (C + WPS - 1) / WPS;
+  const int c0 = wg * G, c1 = min(C, c0 + G);
   const int tid = threadIdx.x;
   const TreeDraw d = *P.rec.at<const TreeDraw>(b, kTreeRecDraw);
   const long long row = (long long)b * P.N + d.node;
   const float* prow = P.p + row * P.V;
   const float* qrow = P.q + row * P.V;
   const TreeDrawWeight w{d.c > 0.0, d.c};
-  const int x0 = cidx * P.CS;
-  const int x1 = min(P.V, x0 + P.CS);
-  const double part = block_sum(chunk_partial<VEC4>(prow, qrow, w, x0, x1), s_red);
   unsigned long long* sums = P.rec.at<unsigned long long>(b, kTreeRecSums);
-  if (tid == 0) s_last = publish_and_arrive(sums + cidx, part, P.rec.ticket(b), C - 1);
+  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, P.V, sums, s_red);
+  if (tid == 0) s_last = arrive(P.rec.ticket(b), WPS - 1);
   __syncthreads();
   if (!s_last) return;
   const float uk = P.uniforms[(long long)b * P.N];
@@ -682,24 +710,30 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
 
 }  // namespace
 
-hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
-  const dim3 grid((unsigned)((long long)p.C * p.B));
+// Workgroups that stream at least this many chunks load them non-temporally (see publish_chunk_sums).
+constexpr int kNtChunks = 8;
+
+template <bool LOGITS>
+hipError_t launch_verify_t(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
+  const dim3 grid((unsigned)((long long)p.WPS * p.B));
+  const bool nt = (p.C + p.WPS - 1) / p.WPS >= kNtChunks;
+#define VAP_LAUNCH_VERIFY(V4, N)                                                                       \
+  hipExtLaunchKernelGGL((spec_verify_kernel<V4, LOGITS, N>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p)
   if (vec4) {
-    hipExtLaunchKernelGGL((spec_verify_kernel<true, false>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (nt) VAP_LAUNCH_VERIFY(true, true); else VAP_LAUNCH_VERIFY(true, false);
   } else {
-    hipExtLaunchKernelGGL((spec_verify_kernel<false, false>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (nt) VAP_LAUNCH_VERIFY(false, true); else VAP_LAUNCH_VERIFY(false, false);
   }
+#undef VAP_LAUNCH_VERIFY
   return hipGetLastError();
 }
 
+hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
+  return launch_verify_t<false>(p, vec4, stream, t);
+}
+
 hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {
-  const dim3 grid((unsigned)((long long)p.C * p.B));
-  if (vec4) {
-    hipExtLaunchKernelGGL((spec_verify_kernel<true, true>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
-  } else {
-    hipExtLaunchKernelGGL((spec_verify_kernel<false, true>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
-  }
-  return hipGetLastError();
+  return launch_verify_t<true>(p, vec4, stream, t);
 }
 
 hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t) {
@@ -713,12 +747,16 @@ hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, 
 }
 
 hipError_t launch_tree_draw(const TreeDrawParams& p, bool vec4, hipStream_t stream, KTimer t) {
-  const dim3 grid((unsigned)((long long)p.C * p.B));
+  const dim3 grid((unsigned)((long long)p.WPS * p.B));
+  const bool nt = (p.C + p.WPS - 1) / p.WPS >= kNtChunks;
+#define VAP_LAUNCH_DRAW(V4, N)                                                                         \
+  hipExtLaunchKernelGGL((tree_draw_kernel<V4, N>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p)
   if (vec4) {
-    hipExtLaunchKernelGGL(tree_draw_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (nt) VAP_LAUNCH_DRAW(true, true); else VAP_LAUNCH_DRAW(true, false);
   } else {
-    hipExtLaunchKernelGGL(tree_draw_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (nt) VAP_LAUNCH_DRAW(false, true); else VAP_LAUNCH_DRAW(false, false);
   }
+#undef VAP_LAUNCH_DRAW
   return hipGetLastError();
 }
 

@@ -88,6 +88,7 @@ struct VerifyParams {
   int32_t B, k, V;
   int32_t C;        // chunks per row
   int32_t CS;       // elements per chunk (multiple of 4)
+  int32_t WPS;      // workgroups per sequence (each takes G = ceil(C / WPS) consecutive chunks)
   int32_t* err;
   SeqRecords rec;   // sequence b: ticket, and its chunk sums at +kVerifyRecSums
   // verification from logits: p and q hold target and draft logits, temps the per-sequence
@@ -148,6 +149,31 @@ hipError_t launch_spec_verify(const VerifyParams& p, bool vec4, hipStream_t stre
 hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t = {});
 hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t = {});
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
+
+// Vocabulary chunking of a verification draw over B sequences on a GPU of `cus` CUs: C chunks of
+// CS tokens per row (CS a multiple of 4 and at most 4096, since the selecting workgroup holds a
+// chunk in registers; about two chunks per CU over the batch), and WPS workgroups per sequence,
+// each taking ceil(C / WPS) consecutive chunks (about four workgroups per CU over the batch, so
+// large batches stream many chunks per workgroup instead of paying the accept tests per chunk).
+struct DrawChunks {
+  int C, CS, WPS;
+};
+
+inline DrawChunks draw_chunks(long long B, long long V, int cus) {
+  long long C = (2LL * cus + B - 1) / B;
+  const long long cmax = (V + 255) / 256 < kMaxChunks ? (V + 255) / 256 : kMaxChunks;
+  C = C < 1 ? 1 : (C > cmax ? cmax : C);
+  if (C < 1) C = 1;
+  if (C < (V + 4095) / 4096) C = (V + 4095) / 4096;
+  long long CS = (V + C - 1) / C;
+  CS = (CS + 3) / 4 * 4;
+  C = (V + CS - 1) / CS;
+  long long WPS = (4LL * cus + B - 1) / B;
+  WPS = WPS < 1 ? 1 : (WPS > C ? C : WPS);
+  const long long G = (C + WPS - 1) / WPS;
+  WPS = (C + G - 1) / G;          // no workgroup without a chunk
+  return DrawChunks{(int)C, (int)CS, (int)WPS};
+}
 
 // Host side of spec_verify with its records (kVerifyRec bytes per sequence, tickets and slots
 // zero) at `records` and its device error word at `err`: checks the call and launches the
@@ -216,6 +242,7 @@ struct TreeDrawParams {
   int32_t* out_ids;         // [B][N]: entry n of sequence b receives the drawn token
   int32_t B, N, V;
   int32_t C, CS;            // chunks per row and their length (multiple of 4, <= 4096)
+  int32_t WPS;              // workgroups per sequence (each takes G = ceil(C / WPS) consecutive chunks)
   SeqRecords rec;           // ticket, TreeDraw, chunk sums [C]
   int32_t* err;
 };
