@@ -29,6 +29,9 @@ What is computed (the plain definition; paging is only an address translation):
   quantisation and separate scales for K and V.  Read here as affine uint8 codes with one
   (scale, zero point) pair per token, KV head and plane: value = scale * (code - zero_point).
   Attention over such a cache is the plain definition above applied to the dequantised values.
+* FP8 KV [P3 §"Quantization and Precision Choices for KV" names FP8 beside INT8]: codes are
+  8-bit floats in the E4M3 format (OCP FP8), with the same per-token and per-head scale pairs:
+  value = scale * (e4m3(code) - zero_point), the zero point 0 for a symmetric cache.
 
 Reading taken where the pages are silent: the scale, the head grouping (contiguous groups) and
 "L counts the new tokens" are the plainest readings consistent with the pages; for 8-bit KV,
@@ -156,6 +159,36 @@ def gather_sequence_kv_u8(codes: np.ndarray, kv_scales: np.ndarray, table_row: n
     return dequantize_u8(kc, s[..., 0], s[..., 1]), dequantize_u8(vc, s[..., 2], s[..., 3])
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact float64 value of 8-bit floating-point codes in the E4M3 format (OCP FP8, "e4m3fn"):
+    bit 7 is the sign, bits 6..3 the exponent with bias 7, bits 2..0 the mantissa.  Exponent 0
+    holds subnormals m * 2^-9; exponent and mantissa all ones (0x7f, 0xff) is NaN; there are no
+    infinities, so the largest magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((e == 0xF) & (c & 0x7 == 0x7), np.nan, sign * mag)
+
+
+def dequantize_fp8(codes: np.ndarray, scale: np.ndarray, zero_point: np.ndarray) -> np.ndarray:
+    """FP8 KV values in float64: scale * (e4m3 value of the code - zero_point), one (scale, zero)
+    pair per token and KV head (zero points are 0 for a symmetric cache)."""
+    x = e4m3_to_f64(codes)
+    return np.asarray(scale, np.float64)[..., None] * (x - np.asarray(zero_point, np.float64)[..., None])
+
+
+def gather_sequence_kv_fp8(codes: np.ndarray, kv_scales: np.ndarray, table_row: np.ndarray, n_tokens: int):
+    """Dequantised contiguous K and V [n_tokens, Hkv, D] (float64) of one sequence from an FP8
+    cache: codes [2, NB, bs, Hkv, D] uint8 holding E4M3 bits, kv_scales as for the 8-bit cache."""
+    sc = np.transpose(np.asarray(kv_scales), (0, 2, 1, 3))     # [NB, bs, Hkv, 4]
+    s = gather_sequence_kv(sc, table_row, n_tokens)
+    kc = gather_sequence_kv(codes[0], table_row, n_tokens)
+    vc = gather_sequence_kv(codes[1], table_row, n_tokens)
+    return dequantize_fp8(kc, s[..., 0], s[..., 1]), dequantize_fp8(vc, s[..., 2], s[..., 3])
+
+
 def _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask=None) -> dict:
     """Attention of the requested (packed row, head) pairs; ``sequence_kv(s, L)`` returns the
     float64 [L, Hkv, D] keys and values of sequence s; ``tree_mask`` [T] per packed row."""
@@ -208,4 +241,14 @@ def paged_attention_u8(q_bits: np.ndarray, codes: np.ndarray, kv_scales: np.ndar
     kv_scales [NB, Hkv, bs, 4] float32, dequantised (``dequantize_u8``) as they are read."""
     def sequence_kv(s, L):
         return gather_sequence_kv_u8(codes, kv_scales, block_tables[s], L)
+    return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask)
+
+
+def paged_attention_fp8(q_bits: np.ndarray, codes: np.ndarray, kv_scales: np.ndarray,
+                        block_tables: np.ndarray, ctx_lens, q_lens, scale: float | None = None,
+                        rows=None, tree_mask=None) -> dict:
+    """``paged_attention_bf16`` over an FP8 (E4M3) KV cache: codes [2, NB, bs, Hkv, D] uint8 and
+    kv_scales [NB, Hkv, bs, 4] float32, dequantised (``dequantize_fp8``) as they are read."""
+    def sequence_kv(s, L):
+        return gather_sequence_kv_fp8(codes, kv_scales, block_tables[s], L)
     return _paged_rows(q_bits, ctx_lens, q_lens, scale, rows, sequence_kv, tree_mask)

@@ -12,6 +12,7 @@ from oracle import attention as A
 from oracle import spec_verify as S
 import tests.test_oracle_attention as TA
 import tests.test_oracle_kv8 as TK
+import tests.test_oracle_fp8 as TF
 import tests.test_oracle_kv_cache as TC
 import tests.test_oracle_logits_verify as TL
 from oracle import logits_verify as LV
@@ -381,6 +382,52 @@ def test_kv8_mutant_is_caught(name, monkeypatch):
     assert _any_pin_fails(KV8_PINS), f"no 8-bit KV pin caught: {name}"
 
 
+FP8_PINS = [
+    TF.test_e4m3_decode_matches_torch_on_every_code,
+    lambda: [TF.test_e4m3_hand_worked_codes(c, v) for c, v in ((0x3C, 1.5), (0x07, 7 * 2.0 ** -9), (0xB8, -1.0))],
+    TF.test_dequantize_fp8_scale_and_zero,
+    lambda: TF.test_fp8_attention_equals_bf16_attention_on_exact_values(
+        dict(ctx_lens=[1, 17, 40, 64], q_lens=[1, 1, 1, 1], Hq=8, Hkv=2, D=64, bs=16)),
+]
+
+
+def _e4m3_variant(bias=7, subnormals=True, mant_div=8.0, signed=True):
+    def e4m3_to_f64(codes):
+        c = np.asarray(codes).astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0) if signed else np.ones(c.shape)
+        e = (c >> 3) & 0xF
+        m = (c & 0x7).astype(np.float64)
+        normal = (1.0 + m / mant_div) * np.exp2(e.astype(np.float64) - bias)
+        mag = np.where(e == 0, m * 2.0 ** -9, normal) if subnormals else normal
+        return np.where((e == 0xF) & (c & 0x7 == 0x7), np.nan, sign * mag)
+    return e4m3_to_f64
+
+
+def _dequant_fp8_variant(zero_sign=-1.0, use_scale=True):
+    def dequantize_fp8(codes, scale, zero_point):
+        x = A.e4m3_to_f64(codes)
+        s = np.asarray(scale, np.float64)[..., None] if use_scale else 1.0
+        return s * (x + zero_sign * np.asarray(zero_point, np.float64)[..., None])
+    return dequantize_fp8
+
+
+FP8_MUTANTS = {
+    "exponent bias 8 (the FNUZ format)": ("e4m3_to_f64", _e4m3_variant(bias=8)),
+    "subnormals decoded as normals": ("e4m3_to_f64", _e4m3_variant(subnormals=False)),
+    "mantissa read as four bits": ("e4m3_to_f64", _e4m3_variant(mant_div=16.0)),
+    "sign bit ignored": ("e4m3_to_f64", _e4m3_variant(signed=False)),
+    "zero point added": ("dequantize_fp8", _dequant_fp8_variant(zero_sign=1.0)),
+    "scale not applied": ("dequantize_fp8", _dequant_fp8_variant(use_scale=False)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    assert _any_pin_fails(FP8_PINS), f"no FP8 KV pin caught: {name}"
+
+
 SPEC_PINS = [
     lambda: TS.test_golden_worked_cases(GOLDEN),
     TS.test_p_equal_q_accepts_every_draft,
@@ -495,3 +542,6 @@ def test_unmodified_wrappers_pass_every_pin(monkeypatch):
     monkeypatch.setattr(LV, "greedy_rows", _greedy_variant())
     monkeypatch.setattr(LV, "distributions", _distributions_variant())
     assert not _any_pin_fails(LOGITS_PINS)
+    monkeypatch.setattr(A, "e4m3_to_f64", _e4m3_variant())
+    monkeypatch.setattr(A, "dequantize_fp8", _dequant_fp8_variant())
+    assert not _any_pin_fails(FP8_PINS)

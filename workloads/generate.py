@@ -20,6 +20,12 @@ Unused block-table entries are -1.
 They are drawn directly in that shape (no quantiser runs here); the scales of unowned slots and
 of rows past L_s are poisoned instead of the codes.
 
+FP8 KV inputs (``kv_format="fp8"``) replace step 3 by
+  3a. codes for every pool slot: N(0, 1) values (fp32) rounded to the nearest E4M3 value (OCP
+      FP8, ties to even, by torch's float8_e4m3fn conversion), stored as their uint8 bits,
+  3b. per (block, KV head, token) (k_scale, 0, v_scale, 0): scales uniform in [0.5, 1.5] and
+      zero points 0 (a symmetric cache).
+
 New K/V rows of a step (``new_kv_rows``), in draw order: per (row, KV head) a spread
 sigma ~ U[0.05, 4] and an offset mu ~ N(0, 0.5) for K, then the same for V; then K and V values
 sigma * N(0, 1) + mu, rounded to bf16.  The varying ranges and signs exercise the 8-bit
@@ -76,10 +82,11 @@ class AttnInputs:
     block_size: int
     kv_scales: torch.Tensor | None = None
     tree_mask: torch.Tensor | None = None
+    fp8: bool = False               # kv_pool holds E4M3 codes (kv_scales set) rather than uint8 codes
 
     @property
     def kv_format(self) -> str:
-        return "bf16" if self.kv_scales is None else "u8"
+        return "bf16" if self.kv_scales is None else ("fp8" if self.fp8 else "u8")
 
     @property
     def num_seqs(self) -> int:
@@ -160,6 +167,26 @@ def _scales_u8(rng: np.random.Generator, shape) -> torch.Tensor:
     sc = rng.uniform(0.01, 0.03, size=(n, 2)).astype(np.float32)
     zp = rng.integers(112, 143, size=(n, 2), endpoint=True).astype(np.float32)
     out = np.stack([sc[:, 0], zp[:, 0], sc[:, 1], zp[:, 1]], axis=1)
+    return torch.from_numpy(out).view(*shape, 4)
+
+
+def _codes_fp8(rng: np.random.Generator, shape) -> torch.Tensor:
+    """uint8 bits of N(0, 1) values rounded to E4M3 (torch float8_e4m3fn), drawn in chunks."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.uint8)
+    for start in range(0, n, _CHUNK):
+        stop = min(n, start + _CHUNK)
+        x = torch.from_numpy(rng.standard_normal(stop - start, dtype=np.float32))
+        out[start:stop] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return out.view(*shape)
+
+
+def _scales_fp8(rng: np.random.Generator, shape) -> torch.Tensor:
+    """[..., 4] fp32 (k_scale, 0, v_scale, 0): scales U[0.5, 1.5], zero points 0."""
+    n = int(np.prod(shape))
+    sc = rng.uniform(0.5, 1.5, size=(n, 2)).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    out = np.stack([sc[:, 0], z, sc[:, 1], z], axis=1)
     return torch.from_numpy(out).view(*shape, 4)
 
 
@@ -254,6 +281,9 @@ def make_attention_inputs(
     elif kv_format == "u8":
         pool = _codes_u8(rng, (2, NB, bs, num_kv_heads, head_dim))
         scales = _scales_u8(rng, (NB, num_kv_heads, bs))
+    elif kv_format == "fp8":
+        pool = _codes_fp8(rng, (2, NB, bs, num_kv_heads, head_dim))
+        scales = _scales_fp8(rng, (NB, num_kv_heads, bs))
     else:
         raise ValueError(f"kv_format {kv_format!r}")
     perm = rng.permutation(NB)
@@ -292,6 +322,7 @@ def make_attention_inputs(
         head_dim=head_dim,
         block_size=bs,
         kv_scales=scales,
+        fp8=kv_format == "fp8",
     )
 
 
@@ -354,7 +385,7 @@ def attention_config(name: str, seed: int | None = None, poison: float = float("
                       decode/verify L lognormal(1024, 1) clipped [16, 4096], prefill L uniform
                       in [256, 4096]; 32/8 heads, D 128, bs 32; pool 95% full; order shuffled
     All other pools hold ceil(1.2 x live blocks).  ``kv_format="u8"`` gives the same lengths
-    and shapes with 8-bit codes and per-token scales.
+    and shapes with 8-bit codes and per-token scales, ``kv_format="fp8"`` with E4M3 codes.
     """
     if seed is None:
         seed = DEFAULT_SEEDS[name]
