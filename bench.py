@@ -14,7 +14,7 @@ Default run (one JSON line on stdout):
   * kv_cache: kv_append of the decode batch's new rows (bf16 and 8-bit), append + attention
     back to back, and kv_commit of the tree step's accepted paths;
   * attention_configs: every attention workload (decode, verify, 70B share, mixed step, tree
-    batch; bf16 and 8-bit KV) with its algorithmic bytes, step and kernel time, GB/s and
+    batch; bf16, 8-bit integer and FP8 KV) with its algorithmic bytes, step and kernel time, GB/s and
     fraction of the HBM peak;
   * spec_verify_sweep: spec_verify at vocabulary 128256 over batch sizes 16 .. 1024;
   * cpu_baseline: the fp64 CPU oracle on the same decode batch, on up to 16 host cores (forked
@@ -202,6 +202,7 @@ def setup_attention(name, dev, kv_format="bf16"):
                   inp.head_dim, inp.block_size)
     d["scales"] = scales
     d["tree_mask"] = inp.tree_mask.to(dev) if inp.tree_mask is not None else None
+    d["fp8"] = inp.fp8
     return inp, d, pools, out, ws, nbytes
 
 
@@ -365,7 +366,7 @@ def run_attention_only(args, dev, name):
     step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
                                          d["q_lens"], out=out, workspace=ws,
                                          kv_scales=None if sc is None else sc[i % len(pools)],
-                                         tree_mask=d["tree_mask"])
+                                         tree_mask=d["tree_mask"], fp8=d["fp8"])
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
@@ -392,7 +393,7 @@ def measure_attention(name, dev, args, kv_format="bf16"):
     step = lambda i: vap.paged_attn_step(d["q"], pools[i % len(pools)], d["block_tables"], d["ctx_lens"],
                                          d["q_lens"], out=out, workspace=ws,
                                          kv_scales=None if sc is None else sc[i % len(pools)],
-                                         tree_mask=d["tree_mask"])
+                                         tree_mask=d["tree_mask"], fp8=d["fp8"])
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
@@ -716,6 +717,7 @@ def run_default(args, dev):
             configs[nm] = measure_attention(nm, dev, args)
             if nm != "tree_verify_step":
                 configs[nm + " u8"] = measure_attention(nm, dev, args, kv_format="u8")
+                configs[nm + " fp8"] = measure_attention(nm, dev, args, kv_format="fp8")
     # ---- spec_verify over batch sizes (vocabulary 128256)
     sweep = spec_verify_sweep(dev, args) if not args.no_configs else None
 
@@ -807,7 +809,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["default", "copy", "attn-only", "verify-only"], default="default")
     ap.add_argument("--workload", default="llama3_8b_decode")
-    ap.add_argument("--kv-format", choices=["bf16", "u8"], default="bf16", help="KV cache format (attn-only mode)")
+    ap.add_argument("--kv-format", choices=["bf16", "u8", "fp8"], default="bf16", help="KV cache format (attn-only mode)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="skip the HIP graph timings (eager steps only)")

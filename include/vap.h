@@ -156,6 +156,19 @@ int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scal
                        void* stream);
 
 /*
+ * paged_attn_step_fp8 -- paged_attn_step_u8 with FP8 codes: each byte of kv_codes is an OCP FP8
+ * E4M3 value (sign, 4-bit exponent with bias 7, 3-bit mantissa; subnormals; no infinities), and
+ * element = scale * (e4m3 - zero) with the same per-token, per-KV-head kv_scales layout
+ * (tempatgunting.com article, section "Quantization and Precision Choices for KV": FP8 or INT8
+ * KV with per-head or per-token scale factors, dequantised inside the attention kernel).  A
+ * symmetric FP8 cache stores zero points of 0.  Everything else (shape, q, tables, lengths, out,
+ * workspace, errors) is as for paged_attn_step_u8; the same workspace serves both.
+ */
+int paged_attn_step_fp8(const void* q, const void* kv_codes, const float* kv_scales, const int32_t* block_tables,
+                        const int32_t* ctx_lens, const int32_t* q_lens, float* out, const vap_attn_shape* shape,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attn_step_tree -- paged_attn_step where each sequence's q_len new rows are the nodes of
  * a draft token tree verified in one pass under a tree attention mask (neuralmasteryai.com
  * "Continuous Batching & Speculative Decoding", section "4. Tree Attention & Medusa Heads").

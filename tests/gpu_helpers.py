@@ -27,6 +27,8 @@ def to_device(inp: workloads.AttnInputs, dev=None):
              ctx_lens=inp.ctx_lens.to(dev), q_lens=inp.q_lens.to(dev))
     if inp.kv_scales is not None:
         d["kv_scales"] = inp.kv_scales.to(dev)
+    if inp.fp8:
+        d["fp8"] = True
     return d
 
 
@@ -36,6 +38,10 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 
 def oracle_rows(inp: workloads.AttnInputs, rows=None, scale=None) -> dict:
+    if inp.fp8:
+        return OA.paged_attention_fp8(bits(inp.q), inp.kv_pool.numpy(), inp.kv_scales.numpy(),
+                                      inp.block_tables.numpy(), inp.ctx_lens.numpy(), inp.q_lens.numpy(),
+                                      scale=scale, rows=rows)
     if inp.kv_scales is not None:
         return OA.paged_attention_u8(bits(inp.q), inp.kv_pool.numpy(), inp.kv_scales.numpy(),
                                      inp.block_tables.numpy(), inp.ctx_lens.numpy(), inp.q_lens.numpy(),
@@ -84,6 +90,8 @@ def config_oracle(name: str, kv_format: str = "bf16") -> dict:
     inp = config_inputs(name, kv_format)
     tm = None if inp.tree_mask is None else inp.tree_mask.numpy()
     args = (inp.block_tables.numpy(), inp.ctx_lens.numpy(), inp.q_lens.numpy())
+    if inp.fp8:
+        return OA_.paged_attention_fp8(bits(inp.q), inp.kv_pool.numpy(), inp.kv_scales.numpy(), *args, tree_mask=tm)
     if inp.kv_scales is not None:
         return OA_.paged_attention_u8(bits(inp.q), inp.kv_pool.numpy(), inp.kv_scales.numpy(), *args, tree_mask=tm)
     return OA_.paged_attention_bf16(bits(inp.q), bits(inp.kv_pool), *args, tree_mask=tm)

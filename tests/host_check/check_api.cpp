@@ -78,6 +78,10 @@ void attention_case(const vap_attn_shape& s) {
                               (float*)D6, &s, workspace(bytes), bytes, nullptr),
            VAP_OK, l0, "paged_attn_step_u8");
     l0 = check_launches;
+    expect(paged_attn_step_fp8(D1, D2, (const float*)D7, (const int32_t*)D3, (const int32_t*)D4, (const int32_t*)D5,
+                               (float*)D6, &s, workspace(bytes), bytes, nullptr),
+           VAP_OK, l0, "paged_attn_step_fp8");
+    l0 = check_launches;
     expect(paged_attn_step_tree(D1, D2, nullptr, (const int32_t*)D3, (const int32_t*)D4, (const int32_t*)D5,
                                 (const uint64_t*)D8, (float*)D6, &s, workspace(bytes), bytes, nullptr),
            VAP_OK, l0, "paged_attn_step_tree");

@@ -93,8 +93,9 @@ hipError_t launch_attn_plan(const AttnParams& p, hipStream_t) {
   attn_regions(p, 64, true);
   return hipSuccess;
 }
-hipError_t launch_attn_main(const AttnParams& p, int D, int, int NRT, bool, int num_wg, int wg_waves, hipStream_t,
+hipError_t launch_attn_main(const AttnParams& p, int D, int, int NRT, int kv, int num_wg, int wg_waves, hipStream_t,
                             KTimer) {
+  need(kv >= 0 && kv <= 2 && (kv == 0) == (p.kcodes == nullptr), "cache format", p.desc, kv);
   ++check_launches;
   attn_regions(p, D, p.B > kLdsPlanMaxSeqs);
   need(p.RG == 16 * NRT, "rows per unit", p.desc, p.RG);

@@ -53,6 +53,7 @@ SIGNATURES = {
     "vap_attn_workspace_min_bytes": (_sz, [_pshape]),
     "paged_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "paged_attn_step_u8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
+    "paged_attn_step_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "paged_attn_step_tree": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pshape, _vp, _sz, _vp]),
     "vap_verify_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "spec_verify": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -163,17 +164,20 @@ def attn_workspace(shape: AttnShape, device=None) -> torch.Tensor:
 
 def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, scale: float = 0.0,
                     workspace: torch.Tensor | None = None, stream=None, kv_scales=None,
-                    tree_mask=None) -> torch.Tensor:
+                    tree_mask=None, fp8: bool = False) -> torch.Tensor:
     """Paged attention for one ragged batch; see ``paged_attn_step`` in include/vap.h.
 
     q bf16 [T, Hq, D]; kv_pool bf16 [2, NB, bs, Hkv, D]; block_tables int32 [B, MB];
     ctx_lens, q_lens int32 [B]; returns out fp32 [T, Hq, D].  With ``kv_scales`` (fp32
-    [NB, Hkv, bs, 4]) the pool holds uint8 codes and ``paged_attn_step_u8`` is called.  With
-    ``tree_mask`` (int64 [T] holding uint64 ancestor masks) ``paged_attn_step_tree`` is called.
+    [NB, Hkv, bs, 4]) the pool holds uint8 codes and ``paged_attn_step_u8`` is called, or with
+    ``fp8=True`` E4M3 codes and ``paged_attn_step_fp8``.  With ``tree_mask`` (int64 [T] holding
+    uint64 ancestor masks) ``paged_attn_step_tree`` is called (bf16 or uint8 codes).
     """
     lib = load_library()
     dev = q.device
     kv8 = kv_scales is not None
+    if fp8 and (not kv8 or tree_mask is not None):
+        raise ValueError("fp8 needs kv_scales and no tree_mask")
     _need(q, "q", torch.bfloat16, 3)
     _need(kv_pool, "kv_pool", torch.uint8 if kv8 else torch.bfloat16, 5, dev)
     _need(block_tables, "block_tables", torch.int32, 2, dev)
@@ -205,10 +209,10 @@ def paged_attn_step(q, kv_pool, block_tables, ctx_lens, q_lens, out=None, *, sca
                                           tree_mask.data_ptr(), out.data_ptr(), ctypes.byref(shape),
                                           workspace.data_ptr(), workspace.numel(), _stream(stream))
         elif kv8:
-            rc = lib.paged_attn_step_u8(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr(),
-                                        block_tables.data_ptr(), ctx_lens.data_ptr(), q_lens.data_ptr(),
-                                        out.data_ptr(), ctypes.byref(shape), workspace.data_ptr(),
-                                        workspace.numel(), _stream(stream))
+            fn = lib.paged_attn_step_fp8 if fp8 else lib.paged_attn_step_u8
+            rc = fn(q.data_ptr(), kv_pool.data_ptr(), kv_scales.data_ptr(), block_tables.data_ptr(),
+                    ctx_lens.data_ptr(), q_lens.data_ptr(), out.data_ptr(), ctypes.byref(shape),
+                    workspace.data_ptr(), workspace.numel(), _stream(stream))
         else:
             rc = lib.paged_attn_step(q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),
                                      ctx_lens.data_ptr(), q_lens.data_ptr(), out.data_ptr(),

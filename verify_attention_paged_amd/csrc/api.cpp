@@ -327,7 +327,8 @@ namespace {
 // Shared body of the bf16 and 8-bit entry points: kv_scales == nullptr selects the bf16 pool.
 int attn_step(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,
               const int32_t* ctx_lens, const int32_t* q_lens, const uint64_t* tree_mask, float* out,
-              const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream_, bool kv8) {
+              const vap_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream_, bool kv8,
+              bool fp8 = false) {
   AttnPlanChoice c;
   int rc = check_attn_shape(shape, &c);
   if (rc != VAP_OK) return rc;
@@ -410,7 +411,7 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
     if (e != hipSuccess) return fail(VAP_EHIP, "plan launch: %s", hipGetErrorString(e));
   }
   const KTimer t = timer_slot(0);
-  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8, W / wg_waves, wg_waves, stream, t);
+  e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8 ? (fp8 ? 2 : 1) : 0, W / wg_waves, wg_waves, stream, t);
   timer_commit(0, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
   e = launch_attn_combine(P, c.D, d->num_cus, stream);
@@ -436,6 +437,13 @@ int paged_attn_step_u8(const void* q, const void* kv_codes, const float* kv_scal
                        void* stream) {
   return attn_step(q, kv_codes, kv_scales, block_tables, ctx_lens, q_lens, nullptr, out, shape, workspace,
                    workspace_bytes, stream, true);
+}
+
+int paged_attn_step_fp8(const void* q, const void* kv_codes, const float* kv_scales, const int32_t* block_tables,
+                        const int32_t* ctx_lens, const int32_t* q_lens, float* out, const vap_attn_shape* shape,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_step(q, kv_codes, kv_scales, block_tables, ctx_lens, q_lens, nullptr, out, shape, workspace,
+                   workspace_bytes, stream, true, true);
 }
 
 int paged_attn_step_tree(const void* q, const void* kv, const float* kv_scales, const int32_t* block_tables,

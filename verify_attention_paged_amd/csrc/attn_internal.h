@@ -102,7 +102,8 @@ struct AttnParams {
 
 // launchers (attn_plan.hip, attn_paged.hip, attn_combine.hip); return hipError_t of the launch
 hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, int wg_waves,
+// kv: 0 = bf16 cache, 1 = 8-bit integer codes, 2 = FP8 (E4M3) codes
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int kv, int num_wg, int wg_waves,
                             hipStream_t stream, KTimer t = {});
 hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);

@@ -404,12 +404,27 @@ __device__ __forceinline__ float row_sum4(float x) {
 // byte i of w as a float (an 8-bit code is exact in fp32 and in bf16)
 __device__ __forceinline__ float code_f32(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xffu); }
 
+// The four codes of a word as floats: unsigned integers (8-bit cache) or, for F8, E4M3 values
+// (the FP8 cache; gfx950's packed conversion decodes OCP E4M3, two codes per instruction).  Both
+// are exact in bf16, so the tile's bf16 MFMAs stay exact in their inputs.
+template <bool F8>
+__device__ __forceinline__ void codes_f32(uint32_t w, float (&f)[4]) {
+  if constexpr (F8) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = code_f32(w, i);
+  }
+}
+
 // One tile of the 8-bit cache.  With x = s (c - z) per token: the score of token j is
 // s_k,j (q.c_j - z_k,j sum(q)), so the K codes go to the MFMA as they are (exact in bf16) and
 // the per-token scale is applied to the 16 scores; the output is
 // sum_j p_j s_v,j c_j - sum_j p_j s_v,j z_v,j, so P is scaled by s_v per token and the second
 // sum is kept per row (o_run, subtracted at the end).
-template <int D, int NRT, bool MASKED>
+template <int D, int NRT, bool MASKED, bool F8>
 __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, int t_end, const RowVis<NRT>& vis,
                                               const bf16x8 (&qb)[NRT][D / 32], const float (&qsum)[NRT],
                                               float scale_log2, float (&m_run)[NRT], float (&l_run)[NRT],
@@ -419,9 +434,10 @@ __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, 
   bf16x8 ka[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    const uint32_t w0 = t.kc[2 * kk], w1 = t.kc[2 * kk + 1];
-    const uint4 u = make_uint4(pack_bf16(code_f32(w0, 0), code_f32(w0, 1)), pack_bf16(code_f32(w0, 2), code_f32(w0, 3)),
-                               pack_bf16(code_f32(w1, 0), code_f32(w1, 1)), pack_bf16(code_f32(w1, 2), code_f32(w1, 3)));
+    float a[4], b[4];
+    codes_f32<F8>(t.kc[2 * kk], a);
+    codes_f32<F8>(t.kc[2 * kk + 1], b);
+    const uint4 u = make_uint4(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3]));
     ka[kk] = as_bf16x8(u);
   }
   float sv[NRT][4];
@@ -490,7 +506,11 @@ __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, 
   for (int jt = 0; jt < NJT; ++jt) {
     float v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = code_f32(t.vc[r][jt >> 2], jt & 3);
+    for (int r = 0; r < 4; ++r) {
+      float f[4];
+      codes_f32<F8>(t.vc[r][jt >> 2], f);
+      v[r] = f[jt & 3];
+    }
     const uint2 vt = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -556,7 +576,7 @@ __device__ __forceinline__ void unit_rows(const AttnParams& P, int kvh, int rg, 
   }
 }
 
-template <int D, int BS, int NRT, bool KV8, bool ONCE>
+template <int D, int BS, int NRT, bool KV8, bool ONCE, bool F8 = false>
 __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, int W, int T1, int PS,
                                 int lane, int c, int g, SplitDesc& desc) {
   constexpr int NKK = D / 32;
@@ -670,7 +690,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
     };
     auto compute = [&](const KVTile<D, KV8>& X, int i, auto masked) {
       if constexpr (KV8)
-        compute_tile8<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, qsum, P.scale_log2,
+        compute_tile8<D, NRT, decltype(masked)::value, F8>(X, tw0 + i * kTile, t_end, vis, qb, qsum, P.scale_log2,
                                                        m_run, l_run, o_run, acc, g);
       else
         compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, P.scale_log2, m_run,
@@ -755,7 +775,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
   }
 }
 
-template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
+template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8, bool F8>
 __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT == 2 ? VAP_ATTN_WAVES_2RT : 1)) void attn_main_kernel(const AttnParams P) {
   extern __shared__ int s_mem[];
   const int lane = threadIdx.x & 63;
@@ -837,7 +857,7 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
       sg.whole = (sg.ub == 0) && (sg.seg == sg.nb);
       sg.slot = first ? 0 : 1;
       if constexpr (KV8)
-        process_segment<D, BS, NRT, true, false>(P, sg, h, W, T1, PS, lane, c, g, desc);
+        process_segment<D, BS, NRT, true, false, F8>(P, sg, h, W, T1, PS, lane, c, g, desc);
       else if (nrg > 1)                   // K/V read again by the sequence's other row groups
         process_segment<D, BS, NRT, false, false>(P, sg, h, W, T1, PS, lane, c, g, desc);
       else
@@ -861,10 +881,10 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
   }
 }
 
-template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8>
+template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8, bool F8>
 hipError_t launch_main_t(const AttnParams& p, int num_wg, int wg_waves, hipStream_t stream, KTimer t) {
   const size_t lds = LDS_PLAN ? attn_main_lds_bytes(p.B) : 0;
-  hipExtLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8>), dim3(num_wg), dim3(64 * wg_waves),
+  hipExtLaunchKernelGGL((attn_main_kernel<D, BS, NRT, LDS_PLAN, KV8, F8>), dim3(num_wg), dim3(64 * wg_waves),
                         (uint32_t)lds, stream, t.start, t.stop, 0, p);
   return hipGetLastError();
 }
@@ -877,18 +897,22 @@ size_t attn_main_lds_bytes(int B) { return size_t(4 * B + 1) * sizeof(int); }
   X(64, 16, 1) X(64, 16, 2) X(64, 16, 4) X(64, 32, 1) X(64, 32, 2) X(64, 32, 4) \
   X(128, 16, 1) X(128, 16, 2) X(128, 16, 4) X(128, 32, 1) X(128, 32, 2) X(128, 32, 4)
 
-hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, bool kv8, int num_wg, int wg_waves,
+// kv: 0 = bf16 cache, 1 = 8-bit integer codes, 2 = FP8 (E4M3) codes
+template <int d, int bs, int nrt, bool lds>
+hipError_t launch_main_kv(const AttnParams& p, int kv, int num_wg, int wg_waves, hipStream_t stream, KTimer t) {
+  if (kv == 1) return launch_main_t<d, bs, nrt, lds, true, false>(p, num_wg, wg_waves, stream, t);
+  if (kv == 2) return launch_main_t<d, bs, nrt, lds, true, true>(p, num_wg, wg_waves, stream, t);
+  return launch_main_t<d, bs, nrt, lds, false, false>(p, num_wg, wg_waves, stream, t);
+}
+
+hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int kv, int num_wg, int wg_waves,
                             hipStream_t stream, KTimer t) {
   if (wg_waves < 1 || wg_waves > kWavesPerWG) return hipErrorInvalidValue;
   const bool lds = p.B <= kLdsPlanMaxSeqs;
-#define X(d, bs, nrt)                                                                         \
-  if (D == d && BS == bs && NRT == nrt) {                                                     \
-    if (kv8)                                                                                  \
-      return lds ? launch_main_t<d, bs, nrt, true, true>(p, num_wg, wg_waves, stream, t)                   \
-                 : launch_main_t<d, bs, nrt, false, true>(p, num_wg, wg_waves, stream, t);                 \
-    return lds ? launch_main_t<d, bs, nrt, true, false>(p, num_wg, wg_waves, stream, t)                    \
-               : launch_main_t<d, bs, nrt, false, false>(p, num_wg, wg_waves, stream, t);                  \
-  }
+#define X(d, bs, nrt)                                                                           \
+  if (D == d && BS == bs && NRT == nrt)                                                         \
+    return lds ? launch_main_kv<d, bs, nrt, true>(p, kv, num_wg, wg_waves, stream, t)           \
+               : launch_main_kv<d, bs, nrt, false>(p, kv, num_wg, wg_waves, stream, t);
   VAP_ATTN_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -898,10 +922,10 @@ const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8
 #define X(d, bs, nrt)                                                                          \
   if (D == d && BS == bs && NRT == nrt) {                                                      \
     if (kv8)                                                                                   \
-      return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, true>) \
-                      : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, true>); \
-    return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, false>) \
-                    : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, false>); \
+      return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, true, false>) \
+                      : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, true, false>); \
+    return lds_plan ? reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, true, false, false>) \
+                    : reinterpret_cast<const void*>(&attn_main_kernel<d, bs, nrt, false, false, false>); \
   }
   VAP_ATTN_VARIANTS(X)
 #undef X
