@@ -168,6 +168,7 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
 //   V^T operand for tile jt (v_mfma_f32_16x16x16bf16_1k, k-slots 4g + r = tokens 4g + r) is
 //   16-bit word jt of its four V loads, and its P^T operand is exactly its four S^T values.
 constexpr int kTile = 16;
+constexpr int kXCDs = 8;    // accelerator complex dies of an MI355X, each with its own L2
 
 template <int D, bool KV8>
 struct KVTile;
@@ -780,7 +781,13 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
   extern __shared__ int s_mem[];
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int w = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  // Holder of this wave, XCD-aware: the GPU dispatches workgroup i to XCD i % kXCDs, and each XCD
+  // has its own L2, so each XCD takes a contiguous range of holders.  Units that read the same K/V
+  // (the row groups of a prefill chunk's KV head) are consecutive in work order and then share
+  // one L2.  Which wave runs which holder changes nothing else (results are bitwise the same).
+  int wg = blockIdx.x;
+  if (gridDim.x % kXCDs == 0) wg = (int)(blockIdx.x % kXCDs) * (int)(gridDim.x / kXCDs) + (int)(blockIdx.x / kXCDs);
+  const int w = uniform(wg * (blockDim.x >> 6) + (threadIdx.x >> 6));
 
   // per-sequence tables: in this workgroup's LDS (ds_read, counted apart from the vector loads
   // in flight) or, for very large batches, in global memory written by the plan kernel
