@@ -187,7 +187,10 @@ int check_attn_shape(const vap_attn_shape* s, AttnPlanChoice* c) {
 // faster (a quarter fewer partials to merge).  The 8-bit cache's heavier tile math and
 // prefill batches want the fourth wave (8-bit decode 43.5 against 50.6 us, mixed batch 346
 // against 364 us).
-int attn_wg_waves(const AttnPlanChoice& c) { return (!c.kv8 && c.rows_per_seq < 8) ? 3 : kWavesPerWG; }
+#ifndef VAP_DECODE_WG_WAVES
+#define VAP_DECODE_WG_WAVES 3
+#endif
+int attn_wg_waves(const AttnPlanChoice& c) { return (!c.kv8 && c.rows_per_seq < 8) ? VAP_DECODE_WG_WAVES : kWavesPerWG; }
 
 int worker_waves(const DevInfo* d, const AttnPlanChoice& c) {
   const int occ = d->attn_occ[c.D == 128][c.BS == 32][c.NRT == 1 ? 0 : (c.NRT == 2 ? 1 : 2)][c.kv8 ? 1 : 0];

@@ -160,8 +160,13 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
 // ---------------------------------------------------------------------------------------
 
 // A tile is 16 consecutive tokens of one block (tiles start at multiples of 16).
-//   K: lane (c, g) loads token c, dims 32*kk + 8*g .. +7 -> A operands of S^T = K Q^T
-//      (v_mfma_f32_16x16x32_bf16); in S^T lane (c, g) then holds row c at tokens 4g + r.
+//   K: the A operands of S^T = K Q^T (v_mfma_f32_16x16x32_bf16) are, at lane (c, g), token c,
+//      dims 32*kk + 8*g .. +7; in S^T lane (c, g) then holds row c at tokens 4g + r.  At
+//      D = 128 (bf16) K is loaded like V -- lane (c, g) loads tokens 4g + r, bytes 16c .. +15,
+//      so each load instruction reads four whole 256-byte head rows -- and reaches the operand
+//      layout through a wave-private LDS tile (kKViaLds below).  Loaded directly in the operand
+//      layout, each instruction reads 64 bytes of 16 rows (half cache lines), which measured
+//      about 11% slower in a no-math gather over a decode batch (5.9 against 6.6 TB/s).
 //   V: lane (c, g) loads, for its tokens 4g + r (r = 0..3), the D/16 consecutive dims
 //      (D/16)*c .. +D/16-1 (16 bytes at D = 128, 8 at D = 64).
 //   Output tile jt (16 dims x 16 rows) holds dim (D/16)*m + jt at its row m, so lane (c, g)'s
@@ -175,9 +180,18 @@ struct KVTile;
 
 template <int D>
 struct KVTile<D, false> {
-  bf16x8 ka[D / 32];
+  bf16x8 ka[D / 32];       // K: operand layout, or (kKViaLds at D = 128) as loaded, ka[r] = tokens 4g + r
   uint32_t vw[4][D / 32];
 };
+
+#ifndef VAP_K_VIA_LDS
+#define VAP_K_VIA_LDS 1
+#endif
+constexpr bool kKViaLds = VAP_K_VIA_LDS != 0;
+constexpr int kKRow = 17;   // LDS row of one token: 16 chunks of 16 bytes and one chunk of padding
+
+template <int D>
+constexpr bool k_via_lds() { return kKViaLds && D == 128; }
 
 // 8-bit cache: lane (c, g) holds the K codes of token c, dims (D/4) g .. +D/4-1; the V codes of
 // tokens 4g + r, dims (D/16) c .. +D/16-1; and (k_scale, k_zero, v_scale, v_zero) of tokens
@@ -237,9 +251,15 @@ __device__ __forceinline__ void load_tile(KVTile<D, false>& t, const uint16_t* k
   const int range = live ? kTile * tok_bytes : 0;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0 * tok_stride, range);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * tok_stride, range);
+  if constexpr (k_via_lds<D>()) {
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    t.ka[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k + 64 * kk, 0, POLICY));
+    for (int r = 0; r < 4; ++r)
+      t.ka[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, vo_v, r * tok_bytes, POLICY));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      t.ka[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k + 64 * kk, 0, POLICY));
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if constexpr (D == 128) {
@@ -321,9 +341,22 @@ template <int D, int NRT, bool MASKED>
 __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, int t_end, const RowVis<NRT>& vis,
                                              const bf16x8 (&qb)[NRT][D / 32], float scale_log2,
                                              float (&m_run)[NRT], float (&l_run)[NRT],
-                                             f32x4 (&acc)[NRT][D / 16], int g) {
+                                             f32x4 (&acc)[NRT][D / 16], int g, uint4* klds) {
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
+  // K in the operand layout: through this wave's LDS tile when it was loaded as whole rows
+  // (written and read back by the same wave: its LDS accesses complete in order, no barrier)
+  bf16x8 ka[NKK];
+  if constexpr (k_via_lds<D>()) {
+    const int c = threadIdx.x & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) klds[(4 * g + r) * kKRow + c] = __builtin_bit_cast(uint4, t.ka[r]);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ka[kk] = as_bf16x8(klds[c * kKRow + 4 * kk + g]);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ka[kk] = t.ka[kk];
+  }
   f32x4 sc[NRT];
   bool ok[NRT][4];
   float mx[NRT];
@@ -332,7 +365,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, 
   for (int rt = 0; rt < NRT; ++rt) {
     sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) sc[rt] = mfma16x16x32(t.ka[kk], qb[rt][kk], sc[rt]);
+    for (int kk = 0; kk < NKK; ++kk) sc[rt] = mfma16x16x32(ka[kk], qb[rt][kk], sc[rt]);
     float m = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -579,7 +612,7 @@ __device__ __forceinline__ void unit_rows(const AttnParams& P, int kvh, int rg, 
 
 template <int D, int BS, int NRT, bool KV8, bool ONCE, bool F8 = false>
 __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, int W, int T1, int PS,
-                                int lane, int c, int g, SplitDesc& desc) {
+                                int lane, int c, int g, SplitDesc& desc, uint4* klds) {
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
   constexpr int RG = 16 * NRT;
@@ -695,7 +728,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
                                                        m_run, l_run, o_run, acc, g);
       else
         compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, P.scale_log2, m_run,
-                                                      l_run, acc, g);
+                                                      l_run, acc, g, klds);
     };
     // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
     // which would make the compiler keep a second copy of the accumulators.  The unmasked loop
@@ -779,6 +812,9 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
 template <int D, int BS, int NRT, bool LDS_PLAN, bool KV8, bool F8>
 __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT == 2 ? VAP_ATTN_WAVES_2RT : 1)) void attn_main_kernel(const AttnParams P) {
   extern __shared__ int s_mem[];
+  // each wave's K transpose tile (bf16 cache at D = 128 only)
+  __shared__ uint4 s_klds[(!KV8 && k_via_lds<D>()) ? kWavesPerWG * kTile * kKRow : 1];
+  uint4* const klds = s_klds + ((!KV8 && k_via_lds<D>()) ? (threadIdx.x >> 6) * kTile * kKRow : 0);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   // Holder of this wave, XCD-aware: the GPU dispatches workgroup i to XCD i % kXCDs, and each XCD
@@ -864,11 +900,11 @@ __global__ __launch_bounds__(kAttnThreads, NRT == 1 ? VAP_ATTN_WAVES_1RT : (NRT 
       sg.whole = (sg.ub == 0) && (sg.seg == sg.nb);
       sg.slot = first ? 0 : 1;
       if constexpr (KV8)
-        process_segment<D, BS, NRT, true, false, F8>(P, sg, h, W, T1, PS, lane, c, g, desc);
+        process_segment<D, BS, NRT, true, false, F8>(P, sg, h, W, T1, PS, lane, c, g, desc, klds);
       else if (nrg > 1)                   // K/V read again by the sequence's other row groups
-        process_segment<D, BS, NRT, false, false>(P, sg, h, W, T1, PS, lane, c, g, desc);
+        process_segment<D, BS, NRT, false, false>(P, sg, h, W, T1, PS, lane, c, g, desc, klds);
       else
-        process_segment<D, BS, NRT, false, true>(P, sg, h, W, T1, PS, lane, c, g, desc);
+        process_segment<D, BS, NRT, false, true>(P, sg, h, W, T1, PS, lane, c, g, desc, klds);
       pos += sg.seg;
       first = false;
     }
