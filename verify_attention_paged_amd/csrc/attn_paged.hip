@@ -731,31 +731,69 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
                                                       l_run, acc, g, klds);
     };
     // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
-    // which would make the compiler keep a second copy of the accumulators.  The unmasked loop
-    // is a two-stage pipeline: tile i+1 is in flight while tile i is computed; the two
-    // buffers rotate (no register copies) and every load is issued unconditionally, so the
-    // compiler never has to drain the load counter at a branch.
+    // which would make the compiler keep a second copy of the accumulators.  Both loops are
+    // one two-stage pipeline: tile i+1 is in flight while tile i is computed, across the hand-
+    // over too (the unmasked loop's last issue loads the first masked tile); the two buffers
+    // rotate and every load is issued unconditionally (a tile that is not live gets an empty
+    // range), so the compiler never has to drain the load counter at a branch.
     const int nu = min(nt, max(0, n_unmasked - wt));
-    if (nu > 0) {
+    if constexpr (!KV8) {
       KVTile<D, KV8> ta, tb;
       issue(ta, 0, true);
       int i = 0;
-      for (; i + 1 < nu; i += 2) {    // both tiles of a pair are always computed
+      for (; i + 1 < nu; i += 2) {      // both tiles of a pair are always computed
         issue(tb, i + 1, true);
         stage_fence();
         compute(ta, i, std::false_type{});
         stage_fence();
-        issue(ta, i + 2, i + 2 < nu);  // the next pair's first tile, or the odd last one
+        issue(ta, i + 2, i + 2 < nt);   // the next pair's first tile, the odd last one, or a masked one
         stage_fence();
         compute(tb, i + 1, std::false_type{});
         stage_fence();
       }
-      if (i < nu) compute(ta, i, std::false_type{});
-    }
-    for (int i = nu; i < nt; ++i) {
-      KVTile<D, KV8> t0;
-      issue(t0, i, true);
-      compute(t0, i, std::true_type{});
+      if (i < nu) {                     // the odd last unmasked tile; the first masked one goes in flight
+        issue(tb, i + 1, i + 1 < nt);
+        stage_fence();
+        compute(ta, i, std::false_type{});
+        stage_fence();
+        ta = tb;
+        ++i;
+      }
+      // ta holds tile i, the first masked tile (if any)
+      for (; i + 1 < nt; i += 2) {
+        issue(tb, i + 1, true);
+        stage_fence();
+        compute(ta, i, std::true_type{});
+        stage_fence();
+        issue(ta, i + 2, i + 2 < nt);
+        stage_fence();
+        compute(tb, i + 1, std::true_type{});
+        stage_fence();
+      }
+      if (i < nt) compute(ta, i, std::true_type{});
+    } else {
+      // 8-bit cache: the masked tiles one at a time (a second buffer there spills registers)
+      if (nu > 0) {
+        KVTile<D, KV8> ta, tb;
+        issue(ta, 0, true);
+        int i = 0;
+        for (; i + 1 < nu; i += 2) {
+          issue(tb, i + 1, true);
+          stage_fence();
+          compute(ta, i, std::false_type{});
+          stage_fence();
+          issue(ta, i + 2, i + 2 < nu);
+          stage_fence();
+          compute(tb, i + 1, std::false_type{});
+          stage_fence();
+        }
+        if (i < nu) compute(ta, i, std::false_type{});
+      }
+      for (int i = nu; i < nt; ++i) {
+        KVTile<D, KV8> t0;
+        issue(t0, i, true);
+        compute(t0, i, std::true_type{});
+      }
     }
   }
   if (derr) atomicOr(&P.hdr->err, derr);      // any lane: errors are per table entry / row
