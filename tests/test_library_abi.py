@@ -132,12 +132,14 @@ def _a256(x):
 
 def test_verifier_workspace_layouts(lib):
     """Header, then one record per sequence (its ticket first, then its data: 256 fp64 chunk
-    sums; for a tree also the walk's end state); the logits workspace puts the statistics
-    partials (16 bytes per row and 2048-token chunk) before the records."""
+    sums; for a tree also the walk's end state and the 16 x 16 chunk sums its workgroups
+    share); the logits workspace puts the statistics partials (16 bytes per row and 2048-token
+    chunk) before the records."""
     rec = 16 + 8 * 256
+    walk = 8 * 256
     for B in (1, 7, 1000, 1 << 22):
         assert lib.vap_verify_workspace_bytes(B, 4, 128256) == _a256(256 + B * rec)
-        assert lib.vap_tree_verify_workspace_bytes(B) == _a256(256 + B * (rec + 32))
+        assert lib.vap_tree_verify_workspace_bytes(B) == _a256(256 + B * (rec + 32 + walk))
     for B, k, V in ((1, 4, 1 << 20), (1000, 0, 4), (16, 4, 128256), (3, 64, 2049)):
         part = B * (2 * k + 1) * ((V + 2047) // 2048) * 16
         assert lib.vap_verify_logits_workspace_bytes(B, k, V) == _a256(_a256(256 + part) + B * rec)

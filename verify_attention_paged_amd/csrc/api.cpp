@@ -558,6 +558,13 @@ int spec_verify_logits(const float* target_logits, const float* draft_logits, co
   return ok();
 }
 
+// A workgroup of the tree walk waits for the other workgroups' chunk sums only while they keep
+// arriving: at most this long without a new one (100 MHz ticks: 6 us), then it computes the rest
+// itself.
+#ifndef VAP_WALK_WAIT_TICKS
+#define VAP_WALK_WAIT_TICKS 600
+#endif
+
 size_t vap_tree_verify_workspace_bytes(int32_t num_seqs) {
   if (num_seqs < 0 || num_seqs > kMaxVerifySeqs) return 0;
   return tree_verify_bytes(num_seqs);
@@ -597,6 +604,10 @@ int spec_verify_tree(const float* p, const float* q, const int32_t* parents, con
   P.vec4 = (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
   P.err = reinterpret_cast<int32_t*>(ws);
   P.rec = SeqRecords{ws + 256, (long long)kTreeRec};
+  // workgroups walking each sequence together: up to two 1024-thread workgroups per CU in all,
+  // and no more than a shared sum has chunks
+  P.S = std::max(1, std::min({kMaxWalkWgs, walk_chunks(vocab).C, 2 * d->num_cus / num_seqs}));
+  P.wait_ticks = VAP_WALK_WAIT_TICKS;
 
   // draw chunks: as spec_verify
   const DrawChunks ch = draw_chunks(num_seqs, vocab, d->num_cus);

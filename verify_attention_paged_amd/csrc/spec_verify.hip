@@ -692,6 +692,12 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
   const int c0 = wg * G, c1 = min(C, c0 + G);
   const int tid = threadIdx.x;
   const TreeDraw d = *P.rec.at<const TreeDraw>(b, kTreeRecDraw);
+  if (wg == 0 && d.passes > 0) {
+    // the walk's shared chunk sums are consumed (the walk kernel has finished): zero them for
+    // the next call
+    unsigned long long* wslots = P.rec.at<unsigned long long>(b, kTreeRecWalk);
+    for (int i = tid; i < d.passes * kWalkChunks; i += kThreads) clear_slot(wslots + i);
+  }
   const long long row = (long long)b * P.N + d.node;
   const float* prow = P.p + row * P.V;
   const float* qrow = P.q + row * P.V;

@@ -187,9 +187,24 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------
-// Tree verification: one walk workgroup per sequence, then the final draw.
+// Tree verification: a walk (S workgroups per sequence walking together and sharing its
+// vocabulary-wide sums), then the final draw.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxTreeNodes = 64;
+constexpr int kWalkPasses = 16;   // residual sums of a walk that its workgroups share
+constexpr int kWalkChunks = 16;   // each such sum is split into this many chunk sums at most
+constexpr int kMaxWalkWgs = 16;   // workgroups per sequence at most
+
+// Chunks of the walk's residual sums: kWalkChunks at most, each a multiple of 4096 elements (so
+// a 1024-thread workgroup takes whole float4s), the last one possibly shorter.
+struct WalkChunks {
+  int32_t C, CS;
+};
+inline __host__ __device__ WalkChunks walk_chunks(int V) {
+  const int per = (V + kWalkChunks - 1) / kWalkChunks;
+  const int CS = ((per + 4095) / 4096) * 4096;
+  return WalkChunks{(V + CS - 1) / CS, CS};
+}
 
 // Where the walk of one sequence ended: the final draw is from max(0, p - c q) of node `node`
 // (c = 0: p itself), or, if those weights are all zero, from max(0, p - c_prev q) (a walk that
@@ -200,7 +215,8 @@ struct TreeDraw {
   double c_prev;
   int32_t node;
   int32_t n;
-  int32_t pad[2];
+  int32_t passes;   // shared sums of the walk (their slots are cleared by the draw kernel)
+  int32_t pad;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -212,11 +228,16 @@ struct TreeDraw {
 //     +kTreeRecDraw   TreeDraw, written by the walk, read by the draw kernel
 //     +kTreeRecSums   published slots [kMaxChunks]: the draw's chunk sums (zero between calls,
 //                     see publish_slot)
+//     +kTreeRecWalk   published slots [kWalkPasses][kWalkChunks]: the chunk sums of the walk's
+//                     shared residual sums sum_x max(0, p - c q) (zero between calls: the draw
+//                     kernel clears what the walk used)
 // ---------------------------------------------------------------------------------------
 constexpr int kTreeRecDraw = 16;
 constexpr int kTreeRecSums = kTreeRecDraw + (int)sizeof(TreeDraw);
-constexpr size_t kTreeRec = kTreeRecSums + 8 * kMaxChunks;
-static_assert(kTreeRecSums % 16 == 0, "tree record fields stay 16-byte aligned");
+constexpr int kTreeRecWalk = kTreeRecSums + 8 * kMaxChunks;
+constexpr size_t kTreeRec = kTreeRecWalk + 8 * kWalkPasses * kWalkChunks;
+static_assert(kTreeRecSums % 16 == 0 && kTreeRecWalk % 16 == 0 && kTreeRec % 16 == 0,
+              "tree record fields stay 16-byte aligned");
 
 inline size_t tree_verify_bytes(long long B) { return align256(256 + (size_t)B * kTreeRec); }
 
@@ -231,8 +252,10 @@ struct TreeVerifyParams {
   int32_t* n_accepted;      // [B]
   int32_t B, N, V;
   bool vec4;                // V % 4 == 0 and p, q 16-byte aligned
+  int32_t S;                // workgroups walking each sequence together
+  int32_t wait_ticks;       // how long a workgroup waits for another chunk sum (100 MHz ticks)
   int32_t* err;
-  SeqRecords rec;           // TreeDraw of each sequence, written at the end of its walk
+  SeqRecords rec;           // TreeDraw of each sequence, written at the end of its walk; walk slots
 };
 
 struct TreeDrawParams {
