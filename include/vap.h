@@ -78,10 +78,11 @@ extern "C" {
                                    a tree of more than 64 rows (the row is then repaired: own
                                    bit set, later bits cleared; or kept causal)              */
 #define VAP_DERR_TEMP 0x40      /* temperature negative or not finite (the sequence is greedy)  */
-#define VAP_DERR_SYNC 0x80      /* the verifiers: a workgroup reading a value that another
-                                   workgroup of the same call has already stored waited past a
-                                   guard of about a quarter of a second (never expected: the
-                                   guard only keeps every wait finite)                          */
+#define VAP_DERR_SYNC 0x80      /* spec_verify, spec_verify_logits and spec_verify_tree's draw: a
+                                   workgroup reading a value that another workgroup of the same
+                                   call has already stored waited past a guard of about a
+                                   quarter of a second (never expected: the guard only keeps
+                                   every wait finite)                                          */
 
 /*
  * Shape of one attention step.
@@ -307,9 +308,13 @@ size_t vap_tree_verify_workspace_bytes(int32_t num_seqs);
  * it with p_cur = its target row.  With no child left, one token is drawn from p_cur (inverse
  * CDF in ascending token id, t = uniforms[0] * sum).  A chain-shaped tree gives spec_verify's
  * result.  Invalid parents set VAP_DERR_TREE (the node is then nobody's child); draft ids
- * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk (one
- * workgroup per sequence, which streams every residual sum itself), then the final draw spread
- * over the GPU.  The workspace (zero-filled before first use) serves spec_verify_tree calls only.
+ * outside the vocabulary VAP_DERR_DRAFT_ID (rejected).  Two kernels on `stream`: the walk (up
+ * to 16 workgroups per sequence, which take the same decisions and share the chunks of each
+ * residual sum through the workspace; none ever waits on another for more than a short bounded
+ * time, after which it computes the missing chunks itself), then the final draw spread over the
+ * GPU, which also zeroes what the walk left in the workspace.  Results do not depend on how
+ * many workgroups walk.  The workspace (zero-filled before first use) serves spec_verify_tree
+ * calls only.
  */
 int spec_verify_tree(const float* p, const float* q, const int32_t* parents, const int32_t* tokens,
                      const float* uniforms, int32_t* out_ids, int32_t* out_path, int32_t* n_accepted,

@@ -182,6 +182,15 @@ def test_large_batch_small_vocab():
     _compare(p, q, ids, u, "B=4096")
 
 
+def test_batch_with_eight_chunks_per_workgroup():
+    """256 sequences at V = 128256: 32 chunks of 4008 tokens per row, four workgroups per
+    sequence, so each workgroup streams eight consecutive chunks -- the count from which the
+    chunk loads take the non-temporal path."""
+    vin = workloads.verify_config("spec_verify_step", seed=4242, batch=256)
+    p, q, ids, u = _margin_inputs(vin, 4243)
+    _compare(p, q, ids, u, "B=256, V=128256")
+
+
 def test_largest_vocabulary():
     """V = 2^20, the largest vocabulary: 256 chunks of 4096 tokens per row."""
     rng = np.random.default_rng(2020)
