@@ -51,6 +51,10 @@
 #ifndef VAP_ATTN_WAVES_2RT
 #define VAP_ATTN_WAVES_2RT 2     // waves per SIMD with two 16-row tiles per unit
 #endif
+// P.V of units with an even number of 16-row tiles (bf16 cache) on the 32x32x16 bf16 MFMA
+#ifndef VAP_PV32
+#define VAP_PV32 1
+#endif
 
 namespace vap {
 namespace {
@@ -58,6 +62,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -72,6 +77,25 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16x16x16(uint2 a, uint2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
+// gfx950 runs this one at the full bf16 rate (16x16x16 above at half of it)
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Output accumulators of a unit of NRT 16-row tiles.  16x16 layout: lane (c, g) holds rows
+// 16 rt + c, dims (D/16)(4g + r) + jt in v[rt][jt][r].  32x32 layout (PV32, NRT even): lane
+// (h, a, c) = 32 h + 16 a + c holds row 32 rp + 16 a + c in v[rp][jt][4q + e], dim
+// (D/2)(q & 1) + (D/4) h + (D/16) e + 2 jt + (q >> 1).
+template <int D, int NRT, bool PV32>
+struct Acc {
+  f32x4 v[NRT][D / 16];
+};
+template <int D, int NRT>
+struct Acc<D, NRT, true> {
+  f32x16 v[NRT / 2][D / 32];
+};
+template <int NRT, bool KV8>
+constexpr bool pv32() { return VAP_PV32 != 0 && !KV8 && NRT % 2 == 0; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -325,6 +349,17 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// x0 on the lanes of even 16-lane rows, x1 on odd rows, for per-row values that all lanes (c, g)
+// of one c hold alike (row maxima, sums, output rows): the odd rows take x1 from their even
+// neighbour.  A plain select between two array elements would be turned into a dynamic index,
+// which puts the array in scratch memory.
+__device__ __forceinline__ uint32_t pick_row(uint32_t x0, uint32_t x1) {
+  return __builtin_amdgcn_permlane16_swap(x0, x1, false, false)[0];
+}
+__device__ __forceinline__ float pick_row(float x0, float x1) {
+  return __uint_as_float(pick_row(__float_as_uint(x0), __float_as_uint(x1)));
+}
+
 // two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -337,11 +372,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // rounding, and most tiles skip the accumulator rescale.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int D, int NRT, bool MASKED>
+template <int D, int NRT, bool MASKED, bool PV32>
 __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, int t_end, const RowVis<NRT>& vis,
                                              const bf16x8 (&qb)[NRT][D / 32], float scale_log2,
                                              float (&m_run)[NRT], float (&l_run)[NRT],
-                                             f32x4 (&acc)[NRT][D / 16], int g, uint4* klds) {
+                                             Acc<D, NRT, PV32>& acc, int g, uint4* klds) {
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
   // K in the operand layout: through this wave's LDS tile when it was loaded as whole rows
@@ -381,14 +416,26 @@ __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, 
     grow = grow || (mx[rt] > m_run[rt] + kRescaleLog2);
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // uniform branch
+    float alpha[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const float m_new = fmaxf(m_run[rt], mx[rt]);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[rt] - m_new);
-      l_run[rt] *= alpha;
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] *= alpha;
+      alpha[rt] = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[rt] - m_new);
+      l_run[rt] *= alpha[rt];
       m_run[rt] = m_new;
+    }
+    if constexpr (PV32) {
+#pragma unroll
+      for (int rp = 0; rp < NRT / 2; ++rp) {
+        const float al = pick_row(alpha[2 * rp], alpha[2 * rp + 1]);   // this lane's row: tile 2 rp + (g & 1)
+#pragma unroll
+        for (int jt = 0; jt < D / 32; ++jt) acc.v[rp][jt] *= al;
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) acc.v[rt][jt] *= alpha[rt];
     }
   }
   uint2 ph[NRT], pl[NRT];
@@ -409,20 +456,57 @@ __device__ __forceinline__ void compute_tile(const KVTile<D, false>& t, int tg, 
     ph[rt] = make_uint2(h01, h23);
     pl[rt] = make_uint2(l01, l23);
   }
+  if constexpr (PV32) {
+    // O^T (32 dims x 32 rows) += V^T (32 dims x 16 tokens) P^T (16 tokens x 32 rows).  Lane
+    // (h, a, c) supplies tokens 8h .. 8h+7: P^T of row 16a + c of the pair, and V of dim
+    // (D/16) c + 2 jt + a.  It holds tokens 8h + 4a .. +3 of both tiles' rows c and both dims,
+    // so one swap between 16-lane rows a = 0 and a = 1 completes each operand.
+    uint4 pbh[NRT / 2], pbl[NRT / 2];
 #pragma unroll
-  for (int jt = 0; jt < NJT; ++jt) {
-    const uint32_t sel = (jt & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t src[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      src[r] = t.vw[r][jt >> 1];
-      if (MASKED) src[r] = (tg + 4 * g + r < t_end) ? src[r] : 0u;
+    for (int rp = 0; rp < NRT / 2; ++rp) {
+      const auto h0 = __builtin_amdgcn_permlane16_swap(ph[2 * rp].x, ph[2 * rp + 1].x, false, false);
+      const auto h1 = __builtin_amdgcn_permlane16_swap(ph[2 * rp].y, ph[2 * rp + 1].y, false, false);
+      const auto l0 = __builtin_amdgcn_permlane16_swap(pl[2 * rp].x, pl[2 * rp + 1].x, false, false);
+      const auto l1 = __builtin_amdgcn_permlane16_swap(pl[2 * rp].y, pl[2 * rp + 1].y, false, false);
+      pbh[rp] = make_uint4(h0[0], h1[0], h0[1], h1[1]);
+      pbl[rp] = make_uint4(l0[0], l1[0], l0[1], l1[1]);
     }
-    const uint2 vt = make_uint2(__builtin_amdgcn_perm(src[1], src[0], sel), __builtin_amdgcn_perm(src[3], src[2], sel));
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      acc[rt][jt] = mfma16x16x16(vt, ph[rt], acc[rt][jt]);
-      acc[rt][jt] = mfma16x16x16(vt, pl[rt], acc[rt][jt]);
+    for (int jt = 0; jt < D / 32; ++jt) {
+      uint32_t src[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        src[r] = t.vw[r][jt];
+        if (MASKED) src[r] = (tg + 4 * g + r < t_end) ? src[r] : 0u;
+      }
+      // even dim (kept by a = 0) and odd dim (kept by a = 1) of this lane's four tokens
+      const auto e0 = __builtin_amdgcn_permlane16_swap(__builtin_amdgcn_perm(src[1], src[0], 0x05040100u),
+                                                       __builtin_amdgcn_perm(src[1], src[0], 0x07060302u), false, false);
+      const auto e1 = __builtin_amdgcn_permlane16_swap(__builtin_amdgcn_perm(src[3], src[2], 0x05040100u),
+                                                       __builtin_amdgcn_perm(src[3], src[2], 0x07060302u), false, false);
+      const uint4 va = make_uint4(e0[0], e1[0], e0[1], e1[1]);
+#pragma unroll
+      for (int rp = 0; rp < NRT / 2; ++rp) {
+        acc.v[rp][jt] = mfma32x32x16(va, pbh[rp], acc.v[rp][jt]);
+        acc.v[rp][jt] = mfma32x32x16(va, pbl[rp], acc.v[rp][jt]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      const uint32_t sel = (jt & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t src[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        src[r] = t.vw[r][jt >> 1];
+        if (MASKED) src[r] = (tg + 4 * g + r < t_end) ? src[r] : 0u;
+      }
+      const uint2 vt = make_uint2(__builtin_amdgcn_perm(src[1], src[0], sel), __builtin_amdgcn_perm(src[3], src[2], sel));
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        acc.v[rt][jt] = mfma16x16x16(vt, ph[rt], acc.v[rt][jt]);
+        acc.v[rt][jt] = mfma16x16x16(vt, pl[rt], acc.v[rt][jt]);
+      }
     }
   }
 }
@@ -596,6 +680,24 @@ __device__ __forceinline__ void write_rows(float* out, const int (&out_row)[NRT]
   }
 }
 
+// One row pair of 32x32 accumulators (PV32): lane (h, a, c) writes its row's dims (D/2) b +
+// (D/4) h + (D/16) e + o for b < 2, e < 4, o < D/16 (element o of that run is v[o >> 1]
+// [4 (2 (o & 1) + b) + e]) at row + (D/4) h.  Output rows are scaled by 1/l, partials by 1.
+template <int D>
+__device__ __forceinline__ void store_row32(float* row, const f32x16 (&v)[D / 32], float mul, int lane) {
+  float* op = row + (D / 4) * (lane >> 5);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int o = 0; o < D / 16; o += 4) {
+        const f32x4 x = {v[o >> 1][4 * b + e], v[o >> 1][4 * (2 + b) + e], v[(o >> 1) + 1][4 * b + e],
+                         v[(o >> 1) + 1][4 * (2 + b) + e]};
+        *reinterpret_cast<f32x4*>(op + (D / 2) * b + (D / 16) * e + o) = x * mul;
+      }
+}
+
 template <int D, int NRT>
 __device__ __forceinline__ void unit_rows(const AttnParams& P, int kvh, int rg, int Q, int qoff, int c,
                                           int (&out_row)[NRT], int& nrows) {
@@ -616,6 +718,7 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
   constexpr int NKK = D / 32;
   constexpr int NJT = D / 16;
   constexpr int RG = 16 * NRT;
+  constexpr bool PV32 = pv32<NRT, KV8>();
   const int G = P.G;
   const int row0 = sg.rg * RG;
   const int t_start = sg.ub * BS;
@@ -680,14 +783,23 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
   }
 
   float m_run[NRT], l_run[NRT], o_run[NRT];
-  f32x4 acc[NRT][NJT];
+  Acc<D, NRT, PV32> acc;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     m_run[rt] = kNegInf;
     l_run[rt] = 0.f;
     o_run[rt] = 0.f;
+  }
+  if constexpr (PV32) {
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rp = 0; rp < NRT / 2; ++rp)
+#pragma unroll
+      for (int jt = 0; jt < D / 32; ++jt) acc.v[rp][jt] = f32x16{};
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc.v[rt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // The tile loop walks the segment in windows of 64 KV blocks.  A window's pool block ids are
@@ -725,10 +837,10 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
     auto compute = [&](const KVTile<D, KV8>& X, int i, auto masked) {
       if constexpr (KV8)
         compute_tile8<D, NRT, decltype(masked)::value, F8>(X, tw0 + i * kTile, t_end, vis, qb, qsum, P.scale_log2,
-                                                       m_run, l_run, o_run, acc, g);
+                                                       m_run, l_run, o_run, acc.v, g);
       else
-        compute_tile<D, NRT, decltype(masked)::value>(X, tw0 + i * kTile, t_end, vis, qb, P.scale_log2, m_run,
-                                                      l_run, acc, g, klds);
+        compute_tile<D, NRT, decltype(masked)::value, PV32>(X, tw0 + i * kTile, t_end, vis, qb, P.scale_log2, m_run,
+                                                            l_run, acc, g, klds);
     };
     // Unmasked tiles first, then the masked suffix: two loops rather than a branch per tile,
     // which would make the compiler keep a second copy of the accumulators.  Both loops are
@@ -808,29 +920,54 @@ __device__ void process_segment(const AttnParams& P, const Segment& sg, int h, i
     if constexpr (KV8) {            // subtract the zero points' share from every output dim
       const float osum = row_sum4(o_run[rt]);
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) acc[rt][jt] -= osum;
+      for (int jt = 0; jt < NJT; ++jt) acc.v[rt][jt] -= osum;
     }
   }
-  if (sg.whole) {
-    write_rows<D, NRT>(P.out, out_row, acc, lsum, g);
-    return;
-  }
-  // partial: store this segment's (max, sum, unnormalised rows) in its slot, rows in natural
-  // dim order; the combine kernel reads them after this kernel has finished
+  if constexpr (PV32) {
+    // lane (h, a, c) holds row 32 rp + 16 a + c of the unit, that is row c of tile 2 rp + a
+    if (sg.whole) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int r_in_unit = rt * 16 + c;
-    if (r_in_unit < nrows) {
-      const long long prow = ((long long)h * 2 + sg.slot) * RG + r_in_unit;
-      float* pp = P.part_acc + prow * D + (D / 4) * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int j4 = 0; j4 < NJT; j4 += 4)
-          *reinterpret_cast<float4*>(pp + NJT * r + j4) =
-              make_float4(acc[rt][j4][r], acc[rt][j4 + 1][r], acc[rt][j4 + 2][r], acc[rt][j4 + 3][r]);
+      for (int rp = 0; rp < NRT / 2; ++rp) {
+        const int orow = (int)pick_row((uint32_t)out_row[2 * rp], (uint32_t)out_row[2 * rp + 1]);
+        if (orow >= 0)
+          store_row32<D>(P.out + (long long)orow * D, acc.v[rp], 1.f / pick_row(lsum[2 * rp], lsum[2 * rp + 1]), lane);
       }
-      if (g == 0) P.part_ml[prow] = make_float2(m_run[rt], lsum[rt]);
+      return;
+    }
+    // partial: this segment's (max, sum, unnormalised rows) in its slot, natural dim order; the
+    // combine kernel reads them after this kernel has finished
+#pragma unroll
+    for (int rp = 0; rp < NRT / 2; ++rp) {
+      const int r_in_unit = 32 * rp + 16 * (g & 1) + c;
+      if (r_in_unit < nrows) {
+        const long long prow = ((long long)h * 2 + sg.slot) * RG + r_in_unit;
+        store_row32<D>(P.part_acc + prow * D, acc.v[rp], 1.f, lane);
+        if (lane < 32)
+          P.part_ml[prow] = make_float2(pick_row(m_run[2 * rp], m_run[2 * rp + 1]), pick_row(lsum[2 * rp], lsum[2 * rp + 1]));
+      }
+    }
+  } else {
+    if (sg.whole) {
+      write_rows<D, NRT>(P.out, out_row, acc.v, lsum, g);
+      return;
+    }
+    // partial: store this segment's (max, sum, unnormalised rows) in its slot, rows in natural
+    // dim order; the combine kernel reads them after this kernel has finished
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int r_in_unit = rt * 16 + c;
+      if (r_in_unit < nrows) {
+        const long long prow = ((long long)h * 2 + sg.slot) * RG + r_in_unit;
+        float* pp = P.part_acc + prow * D + (D / 4) * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int j4 = 0; j4 < NJT; j4 += 4)
+            *reinterpret_cast<float4*>(pp + NJT * r + j4) =
+                make_float4(acc.v[rt][j4][r], acc.v[rt][j4 + 1][r], acc.v[rt][j4 + 2][r], acc.v[rt][j4 + 3][r]);
+        }
+        if (g == 0) P.part_ml[prow] = make_float2(m_run[rt], lsum[rt]);
+      }
     }
   }
   if (sg.ub == 0) {

@@ -106,11 +106,51 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-// Fixed-order workgroup sum (same tree every time).
+// Cross-lane moves of the draw's reductions and scans through DPP (row shifts and row
+// broadcasts): a modifier on a VALU move, where __shfl_* takes one LDS-crossbar round trip
+// (ds_bpermute) per 32-bit half.  Lanes without a source, or outside ROW_MASK, read 0.  The
+// wave must be fully active.
+constexpr int kDppRowShr = 0x110, kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Sum over lanes 0 .. lane, in a fixed order: steps of 1, 2, 4, 8 lanes inside each 16-lane
+// row, then row 0's total into row 1 and row 2's into row 3, then lane 31's into rows 2 and 3.
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_f64<kDppRowShr + 1>(x);
+  x += dpp_f64<kDppRowShr + 2>(x);
+  x += dpp_f64<kDppRowShr + 4>(x);
+  x += dpp_f64<kDppRowShr + 8>(x);
+  x += dpp_f64<kDppRowBcast15, 0xa>(x);
+  x += dpp_f64<kDppRowBcast31, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ double lane_value(double x, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Workgroup index in sequence-major order, XCD-aware: the GPU deals workgroup i to XCD i % 8
+// and each XCD has its own L2, so each XCD takes a contiguous range of indices.  The workgroups
+// of one sequence then share an L2, and the one that finishes the draw rescans a chunk that a
+// sibling streamed from that L2 instead of from HBM.
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int seq_major_index() {
+  if (gridDim.x % kXCDs != 0) return blockIdx.x;
+  return (int)(blockIdx.x % kXCDs) * (int)(gridDim.x / kXCDs) + (int)(blockIdx.x / kXCDs);
+}
+
+// Fixed-order workgroup sum (same order every time).
 __device__ __forceinline__ double block_sum(double x, double* s_red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  x = wave_sum(x);
-  if (lane == 0) s_red[wv] = x;
+  x = wave_incl_scan(x);
+  if (lane == 63) s_red[wv] = x;
   __syncthreads();
   double t = 0.0;
 #pragma unroll
@@ -122,12 +162,8 @@ __device__ __forceinline__ double block_sum(double x, double* s_red) {
 // Exclusive workgroup scan of one double per thread; `total` gets the sum.
 __device__ __forceinline__ double block_exclusive_scan(double x, double* s_red, double& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  double incl = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
+  const double incl = wave_incl_scan(x);
+  const double excl = dpp_f64<kDppWaveShr1>(incl);   // lane - 1's inclusive sum; 0 on lane 0
   if (lane == 63) s_red[wv] = incl;
   __syncthreads();
   double before = 0.0;
@@ -138,7 +174,21 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double* s_red, 
     total += s_red[i];
   }
   __syncthreads();
-  return before + incl - x;
+  return before + excl;
+}
+
+// The value of the first thread (in thread order) with `has`: one ballot per wave, then the
+// waves in order; INT_MAX if none.
+__device__ __forceinline__ int block_first(bool has, int x, int* s_int) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(has);
+  if (lane == 0) s_int[wv] = m ? __builtin_amdgcn_readlane(x, __ffsll((long long)m) - 1) : INT_MAX;
+  __syncthreads();
+  int t = INT_MAX;
+#pragma unroll
+  for (int i = kThreads / 64 - 1; i >= 0; --i) t = s_int[i] != INT_MAX ? s_int[i] : t;
+  __syncthreads();
+  return t;
 }
 
 __device__ __forceinline__ int block_min(int x, int* s_int) {
@@ -184,38 +234,55 @@ __device__ __forceinline__ float4 ld_f4(const float* p) {
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <bool VEC4, class W, bool NT = false>
-__device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, const W& w, int x0, int x1) {
-  const bool residual = w.residual;
-  double acc = 0.0;
-  if (VEC4) {
-    constexpr int kIt = kMaxChunkLen / (4 * kThreads);
-    float4 pv[kIt], qv[kIt];
+// A thread's share of one chunk in registers: loaded (every load issued at once), then summed
+// (chunk_partial does both; publish_chunk_sums keeps the next chunk's loads in flight while it
+// sums the current one).
+template <bool VEC4>
+struct ChunkRegs {
+  static constexpr int kIt = VEC4 ? kMaxChunkLen / (4 * kThreads) : kMaxChunkLen / kThreads;
+  float4 pv[VEC4 ? kIt : 1], qv[VEC4 ? kIt : 1];
+  float ps[VEC4 ? 1 : kIt], qs[VEC4 ? 1 : kIt];
+};
+
+template <bool VEC4, bool NT>
+__device__ __forceinline__ void chunk_load(ChunkRegs<VEC4>& r, const float* prow, const float* qrow, bool residual,
+                                           int x0, int x1) {
+  constexpr int kIt = ChunkRegs<VEC4>::kIt;
 #pragma unroll
-    for (int i = 0; i < kIt; ++i) {
+  for (int i = 0; i < kIt; ++i) {
+    if constexpr (VEC4) {
       const int x = min(x0 + 4 * ((int)threadIdx.x + i * kThreads), x1 - 4);
-      pv[i] = ld_f4<NT>(prow + x);
-      qv[i] = residual ? ld_f4<NT>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < kIt; ++i) {
-      if (x0 + 4 * ((int)threadIdx.x + i * kThreads) < x1)
-        acc += w(pv[i].x, qv[i].x) + w(pv[i].y, qv[i].y) + w(pv[i].z, qv[i].z) + w(pv[i].w, qv[i].w);
-    }
-  } else {
-    constexpr int kIt = kMaxChunkLen / kThreads;
-    float pv[kIt], qv[kIt];
-#pragma unroll
-    for (int i = 0; i < kIt; ++i) {
+      r.pv[i] = ld_f4<NT>(prow + x);
+      r.qv[i] = residual ? ld_f4<NT>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
       const int x = min(x0 + (int)threadIdx.x + i * kThreads, x1 - 1);
-      pv[i] = prow[x];
-      qv[i] = residual ? qrow[x] : 0.f;
+      r.ps[i] = prow[x];
+      r.qs[i] = residual ? qrow[x] : 0.f;
     }
+  }
+}
+
+template <bool VEC4, class W>
+__device__ __forceinline__ double chunk_sum(const ChunkRegs<VEC4>& r, const W& w, int x0, int x1) {
+  constexpr int kIt = ChunkRegs<VEC4>::kIt;
+  double acc = 0.0;
 #pragma unroll
-    for (int i = 0; i < kIt; ++i)
-      if (x0 + (int)threadIdx.x + i * kThreads < x1) acc += w(pv[i], qv[i]);
+  for (int i = 0; i < kIt; ++i) {
+    if constexpr (VEC4) {
+      if (x0 + 4 * ((int)threadIdx.x + i * kThreads) < x1)
+        acc += w(r.pv[i].x, r.qv[i].x) + w(r.pv[i].y, r.qv[i].y) + w(r.pv[i].z, r.qv[i].z) + w(r.pv[i].w, r.qv[i].w);
+    } else {
+      if (x0 + (int)threadIdx.x + i * kThreads < x1) acc += w(r.ps[i], r.qs[i]);
+    }
   }
   return acc;
+}
+
+template <bool VEC4, class W, bool NT = false>
+__device__ __forceinline__ double chunk_partial(const float* prow, const float* qrow, const W& w, int x0, int x1) {
+  ChunkRegs<VEC4> r;
+  chunk_load<VEC4, NT>(r, prow, qrow, w.residual, x0, x1);
+  return chunk_sum<VEC4>(r, w, x0, x1);
 }
 
 // Smallest x in chunk [x0, x1) whose running sum base + C exceeds t (INT_MAX if none), with
@@ -273,8 +340,10 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
     run += wx;
     if (found == INT_MAX && a + j < b && run > t) found = a + j;
   }
-  first_above = block_min(found, s_int);
-  last_positive = block_max(lastpos, s_int);
+  // slices are in token order, so the first thread that found one holds the smallest x
+  first_above = block_first(found != INT_MAX, found, s_int);
+  // needed only when rounding left t at or past the chunk's total (uniform branch)
+  last_positive = first_above == INT_MAX ? block_max(lastpos, s_int) : -1;
 }
 
 __device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi) {
@@ -335,10 +404,20 @@ __device__ __forceinline__ bool arrive(int32_t* ticket, int last) {
 template <bool VEC4, bool NT, class W>
 __device__ __forceinline__ void publish_chunk_sums(const float* prow, const float* qrow, const W& w, int c0, int c1,
                                                    int CS, int V, unsigned long long* slots, double* s_red) {
-  for (int c = c0; c < c1; ++c) {
-    const int x0 = c * CS;
-    const double part = block_sum(chunk_partial<VEC4, W, NT>(prow, qrow, w, x0, min(V, x0 + CS)), s_red);
+  // two chunks in flight: chunk c + 1 loads while chunk c is summed
+  ChunkRegs<VEC4> ra, rb;
+  auto load = [&](ChunkRegs<VEC4>& r, int c) { chunk_load<VEC4, NT>(r, prow, qrow, w.residual, c * CS, min(V, c * CS + CS)); };
+  auto finish = [&](const ChunkRegs<VEC4>& r, int c) {
+    const double part = block_sum(chunk_sum<VEC4>(r, w, c * CS, min(V, c * CS + CS)), s_red);
     if (threadIdx.x == 0) publish_slot(slots + c, part);
+  };
+  if (c0 < c1) load(ra, c0);
+  for (int c = c0; c < c1; c += 2) {
+    if (c + 1 < c1) load(rb, c + 1);
+    finish(ra, c);
+    if (c + 1 >= c1) break;
+    if (c + 2 < c1) load(ra, c + 2);
+    finish(rb, c + 1);
   }
 }
 
@@ -369,13 +448,8 @@ __device__ int finish_draw(unsigned long long* slots, int C, int CS, int V, floa
       if (4 * lane + j < C) clear_slot(slots + 4 * lane + j);
     if (late) atomicOr(err, VAP_DERR_SYNC);
     const double mine = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-    double incl = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    Z = __shfl(incl, 63);
+    const double incl = wave_incl_scan(mine);
+    Z = lane_value(incl, 63);
     if (Z > 0.0) {
       const double t = (double)uk * Z;
       // first chunk whose inclusive running sum exceeds t; else (rounding left t at or above
@@ -461,8 +535,9 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   __shared__ double s_tab[LOGITS ? 64 : 1];                     // 2^(j/64)
 
   const int C = P.C, WPS = P.WPS;
-  const int b = blockIdx.x / WPS;
-  const int wg = blockIdx.x - b * WPS;            // this workgroup's chunks: [c0, c1)
+  const int L = seq_major_index();
+  const int b = L / WPS;
+  const int wg = L - b * WPS;                     // this workgroup's chunks: [c0, c1)
   const int G = (C + WPS - 1) / WPS;
   const int c0 = wg * G, c1 = min(C, c0 + G);
   const int tid = threadIdx.x;
@@ -686,8 +761,9 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
   __shared__ double s_red[kThreads / 64];
   __shared__ int s_int[kThreads / 64];
   const int C = P.C, WPS = P.WPS;
-  const int b = blockIdx.x / WPS;
-  const int wg = blockIdx.x - b * WPS;            // this workgroup's chunks: [c0, c1)
+  const int L = seq_major_index();
+  const int b = L / WPS;
+  const int wg = L - b * WPS;                     // this workgroup's chunks: [c0, c1)
   const int G = (C + WPS - 1) / WPS;
   const int c0 = wg * G, c1 = min(C, c0 + G);
   const int tid = threadIdx.x;
