@@ -438,10 +438,16 @@ __device__ int finish_draw(unsigned long long* slots, int C, int CS, int V, floa
   if (tid < 64) {
     double cs[4];
     bool late = false;
+    // the lane's four slots in one round trip (lanes past C read chunk C - 1 and ignore it); a
+    // slot not yet visible is waited for
+    unsigned long long x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = __hip_atomic_load(slots + min(4 * lane + j, C - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = 4 * lane + j;
-      cs[j] = ci < C ? read_slot(slots + ci, &late) : 0.0;
+      cs[j] = ci >= C ? 0.0 : (x[j] != 0ull ? __longlong_as_double((long long)~x[j]) : read_slot(slots + ci, &late));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
