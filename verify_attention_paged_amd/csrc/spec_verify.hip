@@ -100,12 +100,6 @@ struct TreeDrawWeight {
   }
 };
 
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-  return x;
-}
-
 // Cross-lane moves of the draw's reductions and scans through DPP (row shifts and row
 // broadcasts): a modifier on a VALU move, where __shfl_* takes one LDS-crossbar round trip
 // (ds_bpermute) per 32-bit half.  Lanes without a source, or outside ROW_MASK, read 0.  The
@@ -129,6 +123,9 @@ __device__ __forceinline__ double wave_incl_scan(double x) {
   x += dpp_f64<kDppRowBcast31, 0xc>(x);
   return x;
 }
+// Sum of x over the wave, on every lane (fixed order)
+__device__ __forceinline__ double wave_total(double x);
+
 __device__ __forceinline__ double lane_value(double x, int lane) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(x);
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
@@ -353,6 +350,31 @@ __device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi)
   }
 }
 
+// One DPP step of the wave's (max, first argmax): lanes without a source take (-inf, INT_MAX).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void argmax_dpp_step(float& m, int& i) {
+  const float om = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(m), CTRL,
+                                                              ROW_MASK, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(INT_MAX, i, CTRL, ROW_MASK, 0xf, false);
+  argmax_merge(m, i, om, oi);
+}
+
+// The wave's max and the smallest index holding it, on every lane: the steps of wave_incl_scan
+// with argmax_merge (associative and commutative), then lane 63's result.  The wave must be
+// fully active.
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  argmax_dpp_step<kDppRowShr + 1>(m, i);
+  argmax_dpp_step<kDppRowShr + 2>(m, i);
+  argmax_dpp_step<kDppRowShr + 4>(m, i);
+  argmax_dpp_step<kDppRowShr + 8>(m, i);
+  argmax_dpp_step<kDppRowBcast15, 0xa>(m, i);
+  argmax_dpp_step<kDppRowBcast31, 0xc>(m, i);
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+__device__ __forceinline__ double wave_total(double x) { return lane_value(wave_incl_scan(x), 63); }
+
 // Merge the chunk partials of `rows` consecutive logit rows (part: [rows][C1]) into s_st: per
 // row M = max m_c with its first argmax, and (unless greedy) S = sum_c S_c 2^((m_c - M) cT), in a
 // fixed order.  Partials are staged through LDS in groups of rows; wave w merges rows w, w+4, ...
@@ -372,12 +394,11 @@ __device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool
       float M = -INFINITY;
       int I = INT_MAX;
       for (int c = lane; c < C1; c += 64) argmax_merge(M, I, st[c].m, st[c].argmax);
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) argmax_merge(M, I, __shfl_xor(M, d), __shfl_xor(I, d));
+      wave_argmax(M, I);
       double S = 0.0;
       if (!greedy) {
         for (int c = lane; c < C1; c += 64) S += st[c].S * exp2_f64(((double)st[c].m - (double)M) * cT, tab);
-        S = wave_sum(S);
+        S = wave_total(S);
       }
       if (lane == 0) s_st[r0 + rr] = LogitRowStat{S, M, I};
     }
@@ -708,14 +729,13 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
         m = v[j];
         mi = index(d, j);
       }
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) argmax_merge(m, mi, __shfl_xor(m, dd), __shfl_xor(mi, dd));
+    wave_argmax(m, mi);
     double S = 0.0;
     if (!d.greedy) {
 #pragma unroll
       for (int j = 0; j < kEl; ++j)
         if (index(d, j) < d.x1) S += exp2_f64(((double)v[j] - (double)m) * d.cT, s_tab);
-      S = wave_sum(S);
+      S = wave_total(S);
     }
     if (lane == 0) P.part[it] = LogitRowStat{S, m, mi};
   };
