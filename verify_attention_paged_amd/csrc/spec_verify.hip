@@ -100,39 +100,6 @@ struct TreeDrawWeight {
   }
 };
 
-// Cross-lane moves of the draw's reductions and scans through DPP (row shifts and row
-// broadcasts): a modifier on a VALU move, where __shfl_* takes one LDS-crossbar round trip
-// (ds_bpermute) per 32-bit half.  Lanes without a source, or outside ROW_MASK, read 0.  The
-// wave must be fully active.
-constexpr int kDppRowShr = 0x110, kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
-  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-// Sum over lanes 0 .. lane, in a fixed order: steps of 1, 2, 4, 8 lanes inside each 16-lane
-// row, then row 0's total into row 1 and row 2's into row 3, then lane 31's into rows 2 and 3.
-__device__ __forceinline__ double wave_incl_scan(double x) {
-  x += dpp_f64<kDppRowShr + 1>(x);
-  x += dpp_f64<kDppRowShr + 2>(x);
-  x += dpp_f64<kDppRowShr + 4>(x);
-  x += dpp_f64<kDppRowShr + 8>(x);
-  x += dpp_f64<kDppRowBcast15, 0xa>(x);
-  x += dpp_f64<kDppRowBcast31, 0xc>(x);
-  return x;
-}
-// Sum of x over the wave, on every lane (fixed order)
-__device__ __forceinline__ double wave_total(double x);
-
-__device__ __forceinline__ double lane_value(double x, int lane) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
 // Workgroup index in sequence-major order, XCD-aware: the GPU deals workgroup i to XCD i % 8
 // and each XCD has its own L2, so each XCD takes a contiguous range of indices.  The workgroups
 // of one sequence then share an L2, and the one that finishes the draw rescans a chunk that a
@@ -373,7 +340,6 @@ __device__ __forceinline__ void wave_argmax(float& m, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
-__device__ __forceinline__ double wave_total(double x) { return lane_value(wave_incl_scan(x), 63); }
 
 // Merge the chunk partials of `rows` consecutive logit rows (part: [rows][C1]) into s_st: per
 // row M = max m_c with its first argmax, and (unless greedy) S = sum_c S_c 2^((m_c - M) cT), in a

@@ -44,20 +44,14 @@ constexpr int kMaxNodes = 64;
 constexpr int kRound = 2;    // float4 pairs (or 4x that many floats) per chunk and thread in flight
 constexpr int kBatch = 4;    // chunks computed together
 
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-  return x;
-}
-
 // Fixed-order workgroup sums of kBatch doubles per thread: thread k < kBatch returns the sum of
 // the threads' x[k] (other threads return 0).
 __device__ __forceinline__ double block_sums(const double (&x)[kBatch], double (*s_red)[kThreads / 64]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
-    const double v = wave_sum(x[k]);
-    if (lane == 0) s_red[k][wv] = v;
+    const double v = wave_incl_scan(x[k]);   // lane 63 holds the wave's sum
+    if (lane == 63) s_red[k][wv] = v;
   }
   __syncthreads();
   double t = 0.0;

@@ -26,6 +26,38 @@ struct SeqRecords {
   __host__ __device__ T* at(long long b, int off) const { return reinterpret_cast<T*>(base + b * stride + off); }
 };
 
+// Cross-lane moves of the verifiers' reductions and scans through DPP (row shifts and row
+// broadcasts): a modifier on a VALU move, where __shfl_* takes one LDS-crossbar round trip
+// (ds_bpermute) per 32-bit half.  Lanes without a source, or outside ROW_MASK, read 0.  The
+// wave must be fully active.
+constexpr int kDppRowShr = 0x110, kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Sum over lanes 0 .. lane, in a fixed order: steps of 1, 2, 4, 8 lanes inside each 16-lane
+// row, then row 0's total into row 1 and row 2's into row 3, then lane 31's into rows 2 and 3.
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_f64<kDppRowShr + 1>(x);
+  x += dpp_f64<kDppRowShr + 2>(x);
+  x += dpp_f64<kDppRowShr + 4>(x);
+  x += dpp_f64<kDppRowShr + 8>(x);
+  x += dpp_f64<kDppRowBcast15, 0xa>(x);
+  x += dpp_f64<kDppRowBcast31, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ double lane_value(double x, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Sum of x over the wave, on every lane (fixed order)
+__device__ __forceinline__ double wave_total(double x) { return lane_value(wave_incl_scan(x), 63); }
+
 // Publishing an fp64 value to other workgroups through a workspace slot.  The slot holds the
 // complement of the value's bits and is zero between calls, so a reader can tell a value that
 // is not yet visible (zero) from any value: no value published here has all 64 bits set (the
