@@ -109,16 +109,35 @@ __device__ __forceinline__ void stage_fence() { __builtin_amdgcn_sched_barrier(0
 // in-workgroup plan
 // ---------------------------------------------------------------------------------------
 
+// A lane's value moved by DPP (row shifts and broadcasts, a VALU operand modifier) in 32-bit
+// pieces; lanes without a source, or outside ROW_MASK, read 0
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_move(T x) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
+    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __builtin_bit_cast(T, ((unsigned long long)hi << 32) | lo);
+  }
+}
+
+// Exclusive workgroup scan of one integer per thread (DPP steps inside each wave: 1, 2, 4 and 8
+// lanes within 16-lane rows, then the row totals).  s_tmp is written before the barrier and read
+// after it; the caller puts a barrier between this and the next write of s_tmp.
 template <typename T>
 __device__ __forceinline__ T wg_exclusive_scan(T x, T* s_tmp, T& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;        // waves in this workgroup (at most kWavesPerWG)
   T incl = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const T y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
+  incl += dpp_move<0x111, 0xf>(incl);    // row_shr:1
+  incl += dpp_move<0x112, 0xf>(incl);    // row_shr:2
+  incl += dpp_move<0x114, 0xf>(incl);    // row_shr:4
+  incl += dpp_move<0x118, 0xf>(incl);    // row_shr:8
+  incl += dpp_move<0x142, 0xa>(incl);    // row_bcast:15 into rows 1 and 3
+  incl += dpp_move<0x143, 0xc>(incl);    // row_bcast:31 into rows 2 and 3
   if (lane == 63) s_tmp[wv] = incl;
   __syncthreads();
   T before = 0;
@@ -130,7 +149,6 @@ __device__ __forceinline__ T wg_exclusive_scan(T x, T* s_tmp, T& total) {
       total += s_tmp[i];
     }
   }
-  __syncthreads();
   return before + incl - x;
 }
 
@@ -170,6 +188,7 @@ __device__ void build_plan_lds(const AttnParams& P, int* s_L, int* s_Q, int* s_q
     }
     carry_q += qtot;
     carry_w += wtot;
+    __syncthreads();                     // s_t64 and s_t32 are written again by the next pass
   }
   if (tid == 0) {
     s_off[P.B] = carry_w;
