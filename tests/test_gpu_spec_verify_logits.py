@@ -213,3 +213,35 @@ def test_one_buffer_with_changing_workspace_sizes():
         print("workspace bytes", nbytes, (B, k, V), flush=True)
         _compare(*_margin(inp, 20 + i), f"call {i} {(B, k, V)}", workspace=buf[:nbytes])
     assert vap.get_device_error(buf) == 0
+
+
+def test_greedy_argmax_ties_pick_the_first_index():
+    """Greedy rows whose maximum appears several times: in one lane, across lanes of one
+    statistics chunk, and across chunks (2048 tokens each) and verification workgroups.  The
+    argmax is the smallest such index (the oracle's reading, np.argmax), so a draft at a later
+    tied position is rejected and the emitted token is the first tied index; the sampled
+    sequence checks that the ties leave the row statistics right."""
+    rng = np.random.default_rng(31)
+    B, k, V = 5, 3, 3 * 2048 + 777
+    zp = rng.uniform(-1.0, 1.0, (B, k + 1, V)).astype(np.float32)
+    zq = rng.uniform(-1.0, 1.0, (B, k, V)).astype(np.float32)
+    first = np.zeros((B, k + 1), dtype=np.int64)
+    later = np.zeros((B, k + 1), dtype=np.int64)
+    for b in range(B):
+        for i in range(k + 1):
+            f = int(rng.integers(0, V // 2))
+            ties = sorted({f, f + 1, f + 64 * int(rng.integers(1, 8)), f + 2048, V - 1 - int(rng.integers(0, 300))})
+            zp[b, i, ties] = 4.0
+            first[b, i], later[b, i] = ties[0], ties[int(rng.integers(1, len(ties)))]
+    temps = np.array([0.0, 0.0, 0.0, 0.0, 1.0])
+    inp = workloads.make_logits_verify_inputs(41, zp, zq, temps)
+    ids = inp.draft_ids.numpy().copy()
+    ids[0] = first[0, :k]                                  # all accepted: bonus = first argmax of row k
+    ids[1] = [later[1, 0], first[1, 1], first[1, 2]]       # a later tie is rejected at once
+    ids[2] = [first[2, 0], first[2, 1], later[2, 2]]       # rejected at the last draft
+    ids[3] = [first[3, 0], later[3, 1], first[3, 2]]
+    inp = workloads.LogitsVerifyInputs(**{**inp.__dict__, "draft_ids": torch.as_tensor(ids)})
+    zp_, zq_, ids_, u, T = _margin(inp, 8)
+    ref = _compare(zp_, zq_, ids_, u, T, "argmax ties")
+    assert list(ref[1][:4]) == [3, 0, 2, 1]
+    assert ref[0][0, 3] == first[0, 3] and ref[0][1, 0] == first[1, 0] and ref[0][2, 2] == first[2, 2]
