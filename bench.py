@@ -206,8 +206,20 @@ def setup_attention(name, dev, kv_format="bf16"):
     return inp, d, pools, out, ws, nbytes
 
 
-def time_loop(fn, steps, warmup):
+# Within a timed region, one step in TIMER_EVERY launches its kernels with the library's timer
+# events (launch-stamped start/stop events): a launch that carries them also signals its
+# completion, which cost about 4.6 us per decode step, so stamping every launch would time
+# the instrumentation along with the step.  Kernel durations are the mean over the stamped
+# launches of the same timed region.
+TIMER_EVERY = 8
+
+
+def time_loop(fn, steps, warmup, sample_timer=False):
+    """Milliseconds per step over `steps` calls after `warmup` untimed ones (stream events
+    around the loop), and the wall time.  With sample_timer, the library's kernel timer is on
+    for steps 0, TIMER_EVERY, 2 TIMER_EVERY, ... of the timed loop only, and off afterwards."""
     import torch
+    import verify_attention_paged_amd as vap
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -217,7 +229,11 @@ def time_loop(fn, steps, warmup):
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
+        if sample_timer:
+            vap.timer_enable(i % TIMER_EVERY == 0)
         fn(warmup + i)
+    if sample_timer:
+        vap.timer_enable(False)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -370,7 +386,7 @@ def run_attention_only(args, dev, name):
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
-    ms, wall = time_loop(step, args.steps, 0)
+    ms, wall = time_loop(step, args.steps, 0, sample_timer=True)
     kms, cnt = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_enable(False)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -397,7 +413,7 @@ def measure_attention(name, dev, args, kv_format="bf16"):
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
-    ms, _ = time_loop(step, args.steps, 0)
+    ms, _ = time_loop(step, args.steps, 0, sample_timer=True)
     kms, cnt = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_enable(False)
     if vap.get_device_error(ws):
@@ -442,7 +458,7 @@ def spec_verify_sweep(dev, args):
         vap.timer_enable(True)
         time_loop(step, 0, args.warmup)
         vap.timer_read(vap.TIMER_VERIFY, reset=True)
-        ms, _ = time_loop(step, args.steps, 0)
+        ms, _ = time_loop(step, args.steps, 0)   # every launch stamped: the kernel time is the figure here
         kms, cnt = vap.timer_read(vap.TIMER_VERIFY, reset=True)
         vap.timer_enable(False)
         kms /= max(1, cnt)
@@ -503,7 +519,7 @@ def run_default(args, dev):
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
-    ms, wall = time_loop(step, args.steps, 0)
+    ms, wall = time_loop(step, args.steps, 0, sample_timer=True)
     kms_total, kcount = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     if vap.get_device_error(ws):
         raise RuntimeError("device reported a data error on the decode batch")
@@ -536,7 +552,7 @@ def run_default(args, dev):
     time_loop(vstep, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_read(vap.TIMER_VERIFY, reset=True)
-    vms, _ = time_loop(vstep, args.steps, 0)
+    vms, _ = time_loop(vstep, args.steps, 0, sample_timer=True)
     vattn_ms, c0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     sv_ms, c1 = vap.timer_read(vap.TIMER_VERIFY, reset=True)
     vap.timer_enable(False)
@@ -575,7 +591,7 @@ def run_default(args, dev):
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
     vap.timer_read(vap.TIMER_TREE_DRAW, reset=True)
-    tms, _ = time_loop(tstep, args.steps, 0)
+    tms, _ = time_loop(tstep, args.steps, 0, sample_timer=True)
     tattn_ms, tc0 = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     tsv_ms, tc1 = vap.timer_read(vap.TIMER_TREE_VERIFY, reset=True)
     tdr_ms, tc2 = vap.timer_read(vap.TIMER_TREE_DRAW, reset=True)
@@ -602,7 +618,7 @@ def run_default(args, dev):
     vap.timer_enable(True)
     time_loop(qstep, 0, args.warmup)
     vap.timer_read(vap.TIMER_ATTENTION, reset=True)
-    qms, _ = time_loop(qstep, args.steps, 0)
+    qms, _ = time_loop(qstep, args.steps, 0, sample_timer=True)
     qk_total, qk_count = vap.timer_read(vap.TIMER_ATTENTION, reset=True)
     vap.timer_enable(False)
     if vap.get_device_error(qws):
@@ -626,7 +642,7 @@ def run_default(args, dev):
     time_loop(lstep, 0, args.warmup)
     vap.timer_read(vap.TIMER_LOGIT_STATS, reset=True)
     vap.timer_read(vap.TIMER_VERIFY_LOGITS, reset=True)
-    lms, _ = time_loop(lstep, args.steps, 0)
+    lms, _ = time_loop(lstep, args.steps, 0, sample_timer=True)
     st_ms, sc = vap.timer_read(vap.TIMER_LOGIT_STATS, reset=True)
     lv_ms, lc = vap.timer_read(vap.TIMER_VERIFY_LOGITS, reset=True)
     vap.timer_enable(False)
@@ -678,18 +694,18 @@ def run_default(args, dev):
     for key, fn in (("bf16", app), ("u8", app8)):
         time_loop(fn, 0, args.warmup)
         vap.timer_read(vap.TIMER_KV_APPEND, reset=True)
-        call_ms, _ = time_loop(fn, args.steps, 0)
+        call_ms, _ = time_loop(fn, args.steps, 0, sample_timer=True)
         ktot, kcnt = vap.timer_read(vap.TIMER_KV_APPEND, reset=True)
         res[key] = (call_ms, ktot / max(1, kcnt))
     time_loop(app_step, 0, args.warmup)
-    as_ms, _ = time_loop(app_step, args.steps, 0)
+    as_ms, _ = time_loop(app_step, args.steps, 0, sample_timer=True)
     # commit the tree step's accepted paths (as the tree verifier left them) on one tree pool
     out_lens = torch.empty_like(td["ctx_lens"])
     com = lambda i: vap.kv_commit(tpools[0], td["block_tables"], td["ctx_lens"], td["q_lens"], t_n, path=t_path,
                                   out_ctx_lens=out_lens, workspace=kvws)
     time_loop(com, 0, args.warmup)
     vap.timer_read(vap.TIMER_KV_COMMIT, reset=True)
-    com_ms, _ = time_loop(com, args.steps, 0)
+    com_ms, _ = time_loop(com, args.steps, 0, sample_timer=True)
     ctot, ccnt = vap.timer_read(vap.TIMER_KV_COMMIT, reset=True)
     vap.timer_enable(False)
     if vap.get_device_error(kvws):
@@ -855,7 +871,7 @@ def run_verify_only(args, dev):
     vap.timer_enable(True)
     time_loop(step, 0, args.warmup)
     vap.timer_read(vap.TIMER_VERIFY, reset=True)
-    ms, _ = time_loop(step, args.steps, 0)
+    ms, _ = time_loop(step, args.steps, 0, sample_timer=True)
     kms, cnt = vap.timer_read(vap.TIMER_VERIFY, reset=True)
     n = n_acc.cpu().numpy()
     nbytes = verify_bytes(n, ver.k, ver.vocab)
