@@ -161,8 +161,8 @@ __device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0
   write_row(st, r_raw);
 }
 
-// One workgroup per K consecutive descriptors (K chosen so that the whole grid is resident
-// at once): lanes 0 .. K-1 load them in one round trip, then the workgroup merges the units
+// One workgroup per K consecutive descriptors (K chosen so that the grid takes at most two
+// residency rounds): lanes 0 .. K-1 load them in one round trip, then the workgroup merges the units
 // that valid ones open, in order.  Every holder's descriptor (worker waves' shares, then pool
 // pieces) is written on every call, zeroed when it opens no split unit (including the waves
 // past the step's work and the pool pieces the step does not use), so no other check is
@@ -196,11 +196,13 @@ hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStrea
   // waves per workgroup: 2 for 16-row units (decode), 8 for 32-row units, 16 for 64-row units.
   // Most descriptors are empty; for decode batches the smaller workgroups measured faster
   // (less to dispatch, and four quads need no more waves).  K descriptors per workgroup keep
-  // the grid within one residency round at 16 waves per CU (the D = 128 kernel's register
-  // budget allows 4 waves per SIMD), so no workgroup waits for another to leave; two-wave
-  // workgroups take at least 2 (fewer workgroups to dispatch measured slightly faster).
+  // the grid within two residency rounds at 16 waves per CU (the D = 128 kernel's register
+  // budget allows 4 waves per SIMD): a workgroup merges its units one after another, and
+  // halving K from one round's worth took 4 us off the mixed batch's combine (more units in
+  // flight at once); two-wave workgroups take at least 2 (fewer workgroups to dispatch
+  // measured slightly faster).
   const int nw = p.RG > 32 ? 16 : (p.RG > 16 ? 8 : 2);
-  const long long resident = (long long)std::max(1, num_cus) * 16;
+  const long long resident = (long long)std::max(1, num_cus) * 16 * 2;
   const int K = (int)std::min<long long>(64, std::max<long long>(nw == 2 ? 2 : 1, ((long long)p.NH * nw + resident - 1) / resident));
   const dim3 grid((unsigned)((p.NH + K - 1) / K)), block(64 * nw);
   if (D == 64) {
