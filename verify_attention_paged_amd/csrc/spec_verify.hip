@@ -50,25 +50,30 @@ __device__ __forceinline__ double residual_or_p(float p, float q, bool residual)
   return residual ? fmax(0.0, d) : d;
 }
 
-// 2^a in fp64 for a <= 0 (arguments below -1080, and NaN, give 0): a = (n + j/64) + r with
-// n + j/64 = rint(64 a) / 64, j in [0, 64) and |r| <= 1/128; 2^(j/64) comes from a 64-entry table
-// (tab, filled by fill_exp2_table) and 2^r = e^(r ln 2) from its Taylor series through r^3
-// (coefficients (ln 2)^i / i!, truncation below 4e-11 relative); the product is scaled by 2^n.
+// 2^(b / 64) in fp64 for b <= 0 (arguments below -69120 = 64 * -1080, and NaN, give 0):
+// b = n + r with n = rint(b) and |r| <= 1/2; 2^(n/64) = 2^(n >> 6) * 2^((n & 63)/64), the second
+// factor from a 64-entry table (tab, filled by fill_exp2_table), and 2^(r/64) = e^(r ln 2 / 64)
+// from its Taylor series through r^3 (coefficients (ln 2 / 64)^i / i!, truncation below 4e-11
+// relative).  A caller that scales its argument by a per-row factor folds the 64 into that
+// factor: scaling by a power of two is exact, so the result is that of exp2_f64.
 __device__ __forceinline__ void fill_exp2_table(double* tab) {
   if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
 }
 
-__device__ __forceinline__ double exp2_f64(double a, const double* tab) {
-  a = fmax(a, -1080.0);
-  const double n64 = rint(a * 64.0);
-  const double r = fma(n64, -1.0 / 64.0, a);
-  const int ni = (int)n64;
-  double p = 0.055504108664821576;
-  p = fma(p, r, 0.2402265069591007);
-  p = fma(p, r, 0.6931471805599453);
+__device__ __forceinline__ double exp2_64th(double b, const double* tab) {
+  b = fmax(b, -69120.0);
+  const double n = rint(b);
+  const double r = b - n;                          // exact
+  const int ni = (int)n;
+  double p = 0.055504108664821576 / 262144.0;      // (ln 2)^3 / 3! / 64^3
+  p = fma(p, r, 0.2402265069591007 / 4096.0);      // (ln 2)^2 / 2! / 64^2
+  p = fma(p, r, 0.6931471805599453 / 64.0);        // ln 2 / 64
   p = fma(p, r, 1.0);
   return ldexp(p * tab[ni & 63], ni >> 6);
 }
+
+// 2^a for a <= 0 (below -1080, and NaN, give 0)
+__device__ __forceinline__ double exp2_f64(double a, const double* tab) { return exp2_64th(a * 64.0, tab); }
 
 // Weight of a token in the row that is sampled, from the two values loaded for it (the target
 // and draft entries; the draft entry is 0 and unused when !residual).
@@ -79,14 +84,14 @@ struct ProbWeight {
 
 struct LogitWeight {
   bool residual;
-  double mp, mq, c, inv_sp, inv_sq;   // row maxima, log2(e) / T, reciprocals of the row sums
+  double mp, mq, c64, inv_sp, inv_sq; // row maxima, 64 log2(e) / T, reciprocals of the row sums
   const double* tab;                  // 2^(j/64) table in LDS
   __device__ __forceinline__ double operator()(float zp, float zq) const {
     // p and q are each rounded before the difference: fusing q's product into the
     // subtraction would leave p's rounding error behind where p = q (an empty residual)
 #pragma clang fp contract(off)
-    const double p = exp2_f64(((double)zp - mp) * c, tab) * inv_sp;
-    return residual ? fmax(0.0, p - exp2_f64(((double)zq - mq) * c, tab) * inv_sq) : p;
+    const double p = exp2_64th(((double)zp - mp) * c64, tab) * inv_sp;
+    return residual ? fmax(0.0, p - exp2_64th(((double)zq - mq) * c64, tab) * inv_sq) : p;
   }
 };
 
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if constexpr (LOGITS) {
     const LogitRowStat sp = s_st[n];
     const LogitRowStat sq = residual ? s_st[k + 1 + n] : sp;
-    w = LogitWeight{residual, (double)sp.m, (double)sq.m, cT, 1.0 / sp.S, 1.0 / sq.S, s_tab};
+    w = LogitWeight{residual, (double)sp.m, (double)sq.m, 64.0 * cT, 1.0 / sp.S, 1.0 / sq.S, s_tab};
   } else {
     w = ProbWeight{residual};
   }
@@ -635,36 +640,57 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
 // while they reduce the current one (lane j holds 32 tokens; max and first argmax by cross-lane
 // shuffles, then the fp64 sum of exponentials).  Each item writes its partial with a plain
 // store; the verification kernel merges them.  Draft rows of greedy sequences are skipped.
-template <bool VEC4>
+//
+// Every item issues the same loads on every path: an item with nothing to read (past the last
+// one, or a skipped draft row) reads the first 16 bytes of the target logits in every lane.
+// With loads that depend on the path, the compiler's wait counts must assume the shortest
+// queue, and the reduce of one item then waits for the loads of the next.
+constexpr int kStatTempsLds = 4096;   // 16 KB
+
+// TLDS: the batch's temperatures are staged in LDS (batches of up to kStatTempsLds sequences);
+// a global load of the temperature would make the next item's loads wait for the current one's.
+template <bool VEC4, bool TLDS>
 __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsParams P) {
   constexpr int kEl = kStatChunk / 64;
   __shared__ double s_tab[64];
-  fill_exp2_table(s_tab);
-  __syncthreads();
+  __shared__ float s_temps[TLDS ? kStatTempsLds : 1];
   const int lane = threadIdx.x & 63;
   const int k = P.k, C = P.C, V = P.V;
   const int rows_per_seq = 2 * k + 1;
   const int items = P.B * rows_per_seq * C;             // < 2^31 (checked on the host)
   const int stride = gridDim.x * (kThreads / 64);
+  fill_exp2_table(s_tab);
+  if (TLDS)
+    for (int i = threadIdx.x; i < P.B; i += kThreads) s_temps[i] = P.temps[i];
 
   struct Item {
     const float* z;
     int x0, x1;
     bool need, greedy;
-    double cT;
+    double c64;   // 64 log2(e) / T
   };
   auto item_of = [&](int it) {
     Item d;
-    const int row = it / C;
-    const int c = it - row * C;
-    const int b = row / rows_per_seq, r = row - b * rows_per_seq;
-    const float T = P.temps[b];
-    d.greedy = greedy_temperature(T);
-    d.need = !(d.greedy && r > k);
-    d.cT = d.greedy ? 0.0 : 1.4426950408889634 / (double)T;
-    d.z = r <= k ? P.zp + ((long long)b * (k + 1) + r) * V : P.zq + ((long long)b * k + (r - k - 1)) * V;
-    d.x0 = c * kStatChunk;
-    d.x1 = min(V, d.x0 + kStatChunk);
+    d.need = false;
+    d.greedy = true;
+    d.c64 = 0.0;
+    d.z = P.zp;
+    d.x0 = 0;
+    d.x1 = VEC4 ? 4 : 1;
+    if (it < items) {
+      const int row = it / C;
+      const int c = it - row * C;
+      const int b = row / rows_per_seq, r = row - b * rows_per_seq;
+      const float T = TLDS ? s_temps[b] : P.temps[b];
+      d.greedy = greedy_temperature(T);
+      if (!(d.greedy && r > k)) {
+        d.need = true;
+        d.c64 = d.greedy ? 0.0 : 64.0 * (1.4426950408889634 / (double)T);
+        d.z = r <= k ? P.zp + ((long long)b * (k + 1) + r) * V : P.zq + ((long long)b * k + (r - k - 1)) * V;
+        d.x0 = c * kStatChunk;
+        d.x1 = min(V, d.x0 + kStatChunk);
+      }
+    }
     return d;
   };
   // lane's element j: VEC4 -> x0 + 4 (lane + 64 (j / 4)) + j % 4, else x0 + lane + 64 j (both
@@ -673,7 +699,6 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
     return VEC4 ? d.x0 + 4 * (lane + 64 * (j >> 2)) + (j & 3) : d.x0 + lane + 64 * j;
   };
   auto load = [&](const Item& d, float (&v)[kEl]) {
-    if (!d.need) return;
 #pragma unroll
     for (int j = 0; j < kEl; j += 4) {
       if (VEC4) {
@@ -685,25 +710,33 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
       }
     }
   };
-  auto reduce = [&](const Item& d, int it, const float (&v)[kEl]) {
-    if (!d.need) return;
+  // FULL: the item is a whole chunk (every row's chunks but its last), so no element is masked
+  auto reduce_t = [&](auto full, const Item& d, int it, const float (&v)[kEl]) {
+    constexpr bool FULL = decltype(full)::value;
     float m = -INFINITY;
     int mi = INT_MAX;
 #pragma unroll
-    for (int j = 0; j < kEl; ++j)
-      if (index(d, j) < d.x1 && v[j] > m) {
-        m = v[j];
-        mi = index(d, j);
-      }
+    for (int j = 0; j < kEl; ++j) {
+      const bool take = (FULL || index(d, j) < d.x1) & (v[j] > m);
+      m = take ? v[j] : m;
+      mi = take ? index(d, j) : mi;
+    }
     wave_argmax(m, mi);
     double S = 0.0;
     if (!d.greedy) {
 #pragma unroll
-      for (int j = 0; j < kEl; ++j)
-        if (index(d, j) < d.x1) S += exp2_f64(((double)v[j] - (double)m) * d.cT, s_tab);
+      for (int j = 0; j < kEl; ++j) {
+        const double e = exp2_64th(((double)v[j] - (double)m) * d.c64, s_tab);
+        S += (FULL || index(d, j) < d.x1) ? e : 0.0;
+      }
       S = wave_total(S);
     }
     if (lane == 0) P.part[it] = LogitRowStat{S, m, mi};
+  };
+  auto reduce = [&](const Item& d, int it, const float (&v)[kEl]) {
+    if (!d.need) return;
+    if (d.x1 - d.x0 == kStatChunk) reduce_t(std::true_type{}, d, it, v);
+    else reduce_t(std::false_type{}, d, it, v);
   };
 
   // this call's verification tickets and chunk-sum slots start at zero whatever an earlier call
@@ -715,6 +748,7 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
     if (j == 0) *P.rec.ticket(b) = 0;
     else P.rec.at<unsigned long long>(b, kVerifyRecSums)[j - 1] = 0ull;
   }
+  __syncthreads();
   int it = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6));
   if (it >= items) return;
   float va[kEl], vb[kEl];
@@ -723,18 +757,14 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
   while (true) {
     // ping: b's loads in flight while a is reduced, then pong
     const int nb = it + stride;
-    if (nb < items) {
-      db = item_of(nb);
-      load(db, vb);
-    }
+    db = item_of(nb);
+    load(db, vb);
     reduce(da, it, va);
     if (nb >= items) break;
     it = nb;
     const int na = it + stride;
-    if (na < items) {
-      da = item_of(na);
-      load(da, va);
-    }
+    da = item_of(na);
+    load(da, va);
     reduce(db, it, vb);
     if (na >= items) break;
     it = na;
@@ -812,11 +842,15 @@ hipError_t launch_spec_verify_logits(const VerifyParams& p, bool vec4, hipStream
 
 hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, hipStream_t stream, KTimer t) {
   const dim3 grid((unsigned)num_wg);
+  const bool tlds = p.B <= kStatTempsLds;
+#define VAP_LAUNCH_STATS(V4, TL)                                                                       \
+  hipExtLaunchKernelGGL((logit_stats_kernel<V4, TL>), grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p)
   if (vec4) {
-    hipExtLaunchKernelGGL(logit_stats_kernel<true>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (tlds) VAP_LAUNCH_STATS(true, true); else VAP_LAUNCH_STATS(true, false);
   } else {
-    hipExtLaunchKernelGGL(logit_stats_kernel<false>, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, p);
+    if (tlds) VAP_LAUNCH_STATS(false, true); else VAP_LAUNCH_STATS(false, false);
   }
+#undef VAP_LAUNCH_STATS
   return hipGetLastError();
 }
 
