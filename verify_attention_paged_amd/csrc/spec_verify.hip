@@ -37,6 +37,7 @@
 // within rounding of the fp64 oracle.
 #include <cfloat>
 #include <type_traits>
+#include <utility>
 
 #include "vap_internal.h"
 
@@ -84,14 +85,14 @@ struct ProbWeight {
 
 struct LogitWeight {
   bool residual;
-  double mp, mq, c64, inv_sp, inv_sq; // row maxima, 64 log2(e) / T, reciprocals of the row sums
-  const double* tab;                  // 2^(j/64) table in LDS
+  double nmp, nmq, c64, inv_sp, inv_sq;  // -(row max) * c64, 64 log2(e) / T, reciprocals of the row sums
+  const double* tab;                     // 2^(j/64) table in LDS
   __device__ __forceinline__ double operator()(float zp, float zq) const {
     // p and q are each rounded before the difference: fusing q's product into the
     // subtraction would leave p's rounding error behind where p = q (an empty residual)
 #pragma clang fp contract(off)
-    const double p = exp2_64th(((double)zp - mp) * c64, tab) * inv_sp;
-    return residual ? fmax(0.0, p - exp2_64th(((double)zq - mq) * c64, tab) * inv_sq) : p;
+    const double p = exp2_64th(fma((double)zp, c64, nmp), tab) * inv_sp;
+    return residual ? fmax(0.0, p - exp2_64th(fma((double)zq, c64, nmq), tab) * inv_sq) : p;
   }
 };
 
@@ -606,7 +607,8 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if constexpr (LOGITS) {
     const LogitRowStat sp = s_st[n];
     const LogitRowStat sq = residual ? s_st[k + 1 + n] : sp;
-    w = LogitWeight{residual, (double)sp.m, (double)sq.m, 64.0 * cT, 1.0 / sp.S, 1.0 / sq.S, s_tab};
+    w = LogitWeight{residual, -(double)sp.m * (64.0 * cT), -(double)sq.m * (64.0 * cT), 64.0 * cT, 1.0 / sp.S,
+                    1.0 / sq.S, s_tab};
   } else {
     w = ProbWeight{residual};
   }
@@ -645,7 +647,17 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
 // one, or a skipped draft row) reads the first 16 bytes of the target logits in every lane.
 // With loads that depend on the path, the compiler's wait counts must assume the shortest
 // queue, and the reduce of one item then waits for the loads of the next.
+// f(0), f(1), ... with compile-time arguments, stopping at the first that returns true
+template <typename F, int... I>
+__device__ __forceinline__ bool each_until(F& f, std::integer_sequence<int, I...>) {
+  return (f(std::integral_constant<int, I>{}) || ...);
+}
+
 constexpr int kStatTempsLds = 4096;   // 16 KB
+#ifndef VAP_STAT_STAGES
+#define VAP_STAT_STAGES 2
+#endif
+constexpr int kStatStages = VAP_STAT_STAGES;   // statistics items per wave in flight or in reduction
 
 // TLDS: the batch's temperatures are staged in LDS (batches of up to kStatTempsLds sequences);
 // a global load of the temperature would make the next item's loads wait for the current one's.
@@ -669,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
     bool need, greedy;
     double c64;   // 64 log2(e) / T
   };
-  auto item_of = [&](int it) {
+  auto item_of = [&](int it) __attribute__((always_inline)) {
     Item d;
     d.need = false;
     d.greedy = true;
@@ -695,10 +707,10 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
   };
   // lane's element j: VEC4 -> x0 + 4 (lane + 64 (j / 4)) + j % 4, else x0 + lane + 64 j (both
   // increase with j); loads past the chunk read a clamped address and are masked
-  auto index = [&](const Item& d, int j) {
+  auto index = [&](const Item& d, int j) __attribute__((always_inline)) {
     return VEC4 ? d.x0 + 4 * (lane + 64 * (j >> 2)) + (j & 3) : d.x0 + lane + 64 * j;
   };
-  auto load = [&](const Item& d, float (&v)[kEl]) {
+  auto load = [&](const Item& d, float (&v)[kEl]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kEl; j += 4) {
       if (VEC4) {
@@ -710,33 +722,33 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
       }
     }
   };
-  // FULL: the item is a whole chunk (every row's chunks but its last), so no element is masked
-  auto reduce_t = [&](auto full, const Item& d, int it, const float (&v)[kEl]) {
-    constexpr bool FULL = decltype(full)::value;
+  auto reduce = [&](const Item& d, int it, float (&v)[kEl]) __attribute__((always_inline)) {
+    if (!d.need) return;
+    // the last chunk of a row: elements past its end become -inf, which are never the max and
+    // whose exponential is exactly 0, so one reduction serves every chunk
+    if (d.x1 - d.x0 != kStatChunk) {
+#pragma unroll
+      for (int j = 0; j < kEl; ++j) v[j] = index(d, j) < d.x1 ? v[j] : -INFINITY;
+    }
     float m = -INFINITY;
     int mi = INT_MAX;
 #pragma unroll
     for (int j = 0; j < kEl; ++j) {
-      const bool take = (FULL || index(d, j) < d.x1) & (v[j] > m);
+      const bool take = v[j] > m;
       m = take ? v[j] : m;
       mi = take ? index(d, j) : mi;
     }
     wave_argmax(m, mi);
     double S = 0.0;
     if (!d.greedy) {
+      // 64 (z - m) log2(e) / T as one fma with the rounded product m c64: an argument error of
+      // ulp(m c64), a relative error near 1e-14 in the term, far below the polynomial's 4e-11
+      const double mc64 = -(double)m * d.c64;
 #pragma unroll
-      for (int j = 0; j < kEl; ++j) {
-        const double e = exp2_64th(((double)v[j] - (double)m) * d.c64, s_tab);
-        S += (FULL || index(d, j) < d.x1) ? e : 0.0;
-      }
+      for (int j = 0; j < kEl; ++j) S += exp2_64th(fma((double)v[j], d.c64, mc64), s_tab);
       S = wave_total(S);
     }
     if (lane == 0) P.part[it] = LogitRowStat{S, m, mi};
-  };
-  auto reduce = [&](const Item& d, int it, const float (&v)[kEl]) {
-    if (!d.need) return;
-    if (d.x1 - d.x0 == kStatChunk) reduce_t(std::true_type{}, d, it, v);
-    else reduce_t(std::false_type{}, d, it, v);
   };
 
   // this call's verification tickets and chunk-sum slots start at zero whatever an earlier call
@@ -751,23 +763,28 @@ __global__ __launch_bounds__(kThreads) void logit_stats_kernel(const LogitStatsP
   __syncthreads();
   int it = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6));
   if (it >= items) return;
-  float va[kEl], vb[kEl];
-  Item da = item_of(it), db;
-  load(da, va);
-  while (true) {
-    // ping: b's loads in flight while a is reduced, then pong
-    const int nb = it + stride;
-    db = item_of(nb);
-    load(db, vb);
-    reduce(da, it, va);
-    if (nb >= items) break;
-    it = nb;
-    const int na = it + stride;
-    da = item_of(na);
-    load(da, va);
-    reduce(db, it, vb);
-    if (na >= items) break;
-    it = na;
+  // kStatStages buffers in rotation: the loads of the next kStatStages - 1 items are in flight
+  // while one is reduced (the rotation is unrolled, so every buffer stays in registers)
+  float v[kStatStages][kEl];
+  Item d[kStatStages];
+#pragma unroll
+  for (int s = 0; s + 1 < kStatStages; ++s) {
+    d[s] = item_of(it + s * stride);
+    load(d[s], v[s]);
+  }
+  // one step per buffer s (a compile-time index): refill the buffer reduced last, reduce s;
+  // true once the wave's last item is reduced
+  auto step = [&](auto sc) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int n = (s + kStatStages - 1) % kStatStages;
+    d[n] = item_of(it + (kStatStages - 1) * stride);
+    load(d[n], v[n]);
+    reduce(d[s], it, v[s]);
+    if (it + stride >= items) return true;
+    it += stride;
+    return false;
+  };
+  while (!each_until(step, std::make_integer_sequence<int, kStatStages>{})) {
   }
 }
 
