@@ -351,30 +351,39 @@ __device__ __forceinline__ void wave_argmax(float& m, int& i) {
 // row M = max m_c with its first argmax, and (unless greedy) S = sum_c S_c 2^((m_c - M) cT), in a
 // fixed order.  Partials are staged through LDS in groups of rows; wave w merges rows w, w+4, ...
 constexpr int kMergeStage = 2048;   // 16-byte partials staged per pass (32 KB)
+constexpr int kMergePre = 4;        // partials per thread loaded ahead (one pass of up to 1024)
+static_assert(kMergePre == 4, "the verification kernel holds four prefetched partials per thread");
+
+// rows [r0, r0 + nr) from the staged partials (their first row at s_stage[0]); ends with a barrier
+__device__ void merge_staged_rows(const uint4* s_stage, int C1, int r0, int nr, bool greedy, double cT,
+                                  LogitRowStat* s_st, const double* tab) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int rr = wv; rr < nr; rr += kThreads / 64) {
+    const LogitRowStat* st = reinterpret_cast<const LogitRowStat*>(s_stage) + rr * C1;
+    float M = -INFINITY;
+    int I = INT_MAX;
+    for (int c = lane; c < C1; c += 64) argmax_merge(M, I, st[c].m, st[c].argmax);
+    wave_argmax(M, I);
+    double S = 0.0;
+    if (!greedy) {
+      for (int c = lane; c < C1; c += 64) S += st[c].S * exp2_f64(((double)st[c].m - (double)M) * cT, tab);
+      S = wave_total(S);
+    }
+    if (lane == 0) s_st[r0 + rr] = LogitRowStat{S, M, I};
+  }
+  __syncthreads();
+}
 
 __device__ void merge_row_stats(const LogitRowStat* part, int C1, int rows, bool greedy, double cT,
                                 LogitRowStat* s_st, uint4* s_stage, const double* tab) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const int per = max(1, kMergeStage / C1);
   for (int r0 = 0; r0 < rows; r0 += per) {
     const int nr = min(per, rows - r0);
     const uint4* src = reinterpret_cast<const uint4*>(part + (long long)r0 * C1);
     for (int e = tid; e < nr * C1; e += kThreads) s_stage[e] = src[e];
     __syncthreads();
-    for (int rr = wv; rr < nr; rr += kThreads / 64) {
-      const LogitRowStat* st = reinterpret_cast<const LogitRowStat*>(s_stage) + rr * C1;
-      float M = -INFINITY;
-      int I = INT_MAX;
-      for (int c = lane; c < C1; c += 64) argmax_merge(M, I, st[c].m, st[c].argmax);
-      wave_argmax(M, I);
-      double S = 0.0;
-      if (!greedy) {
-        for (int c = lane; c < C1; c += 64) S += st[c].S * exp2_f64(((double)st[c].m - (double)M) * cT, tab);
-        S = wave_total(S);
-      }
-      if (lane == 0) s_st[r0 + rr] = LogitRowStat{S, M, I};
-    }
-    __syncthreads();
+    merge_staged_rows(s_stage, C1, r0, nr, greedy, cT, s_st, tab);
   }
 }
 
@@ -545,31 +554,62 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   const long long srow = (long long)b * (2 * k + 1);   // first statistics row of sequence b
   bool greedy = false;
   double cT = 0.0;
+  // the first wave's draft token, its uniform and (both paths) the two entries at that token:
+  // loaded before the merge of the row statistics, which they do not depend on
+  // (a token outside [0, V) reads entry 0 and is rejected; the loads take no branch, so that no
+  // wait for them is placed before the merge's own loads)
+  int x = 0;
+  float r = 0.f, px = 0.f, qx = 0.f;
+  if (tid == 64) s_uk = P.uniforms[(long long)b * (k + 1) + k];
+  if (tid < k) {
+    x = P.draft_ids[(long long)b * k + lane];
+    r = P.uniforms[(long long)b * (k + 1) + lane];
+    const int xc = (x >= 0 && x < V) ? x : 0;
+    px = P.p[((long long)b * (k + 1) + lane) * V + xc];
+    qx = P.q[((long long)b * k + lane) * V + xc];
+  }
+  const bool inside = x >= 0 && x < V;
   if constexpr (LOGITS) {
+    // the partials of all 2k + 1 rows (a greedy sequence's draft rows are merged but unused), in
+    // one pass when they fit kMergePre per thread, loaded before the temperature is known
+    const int C1 = P.C1, rows = 2 * k + 1, n_el = rows * C1;
+    const uint4* src = reinterpret_cast<const uint4*>(P.part + srow * C1);
+    const bool one_pass = n_el <= kMergePre * kThreads && n_el <= kMergeStage;
+    // (four named registers: an array here is kept in scratch memory)
+    uint4 pre0, pre1, pre2, pre3;
+    if (one_pass) {
+      pre0 = src[min(tid, n_el - 1)];
+      pre1 = src[min(tid + kThreads, n_el - 1)];
+      pre2 = src[min(tid + 2 * kThreads, n_el - 1)];
+      pre3 = src[min(tid + 3 * kThreads, n_el - 1)];
+    }
     const float T = P.temps[b];
     greedy = greedy_temperature(T);
     if (!(T >= 0.f && T <= FLT_MAX) && wg == 0 && tid == 0) atomicOr(P.err, VAP_DERR_TEMP);
     cT = greedy ? 0.0 : 1.4426950408889634 / (double)T;
     fill_exp2_table(s_tab);   // visible after the merge's first barrier
-    merge_row_stats(P.part + srow * P.C1, P.C1, greedy ? k + 1 : 2 * k + 1, greedy, cT, s_st, s_stage, s_tab);
+    if (one_pass) {
+      if (tid < n_el) s_stage[tid] = pre0;
+      if (tid + kThreads < n_el) s_stage[tid + kThreads] = pre1;
+      if (tid + 2 * kThreads < n_el) s_stage[tid + 2 * kThreads] = pre2;
+      if (tid + 3 * kThreads < n_el) s_stage[tid + 3 * kThreads] = pre3;
+      __syncthreads();
+      merge_staged_rows(s_stage, C1, 0, greedy ? k + 1 : rows, greedy, cT, s_st, s_tab);
+    } else {
+      merge_row_stats(P.part + srow * C1, C1, greedy ? k + 1 : rows, greedy, cT, s_st, s_stage, s_tab);
+    }
+    // the gathered values are first used here: without this the compiler converts them where
+    // they are loaded, which waits for those loads before the partials' loads are issued
+    asm volatile("" : "+v"(px), "+v"(qx), "+v"(r));
   }
 
-  // 1. accept tests (first wave; k <= 64); the second wave fetches u_k meanwhile
-  if (tid == 64) s_uk = P.uniforms[(long long)b * (k + 1) + k];
+  // 1. accept tests (first wave; k <= 64)
   if (tid < 64) {
     bool reject = false;
     if (lane < k) {
-      const int x = P.draft_ids[(long long)b * k + lane];
-      const bool inside = x >= 0 && x < V;
       if (!inside && wg == 0) atomicOr(P.err, VAP_DERR_DRAFT_ID);
-      const double r = (double)P.uniforms[(long long)b * (k + 1) + lane];
       if constexpr (!LOGITS) {
-        float pv = 0.f, qv = 0.f;
-        if (inside) {
-          pv = P.p[((long long)b * (k + 1) + lane) * V + x];
-          qv = P.q[((long long)b * k + lane) * V + x];
-        }
-        reject = !(pv > 0.f && r * (double)qv <= (double)pv);
+        reject = !(inside && px > 0.f && (double)r * (double)qx <= (double)px);
       } else {
         if (!inside) {
           reject = true;
@@ -577,9 +617,9 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
           reject = x != s_st[lane].argmax;
         } else {
           const LogitRowStat sp = s_st[lane], sq = s_st[k + 1 + lane];
-          const double pv = exp2_f64(((double)P.p[((long long)b * (k + 1) + lane) * V + x] - sp.m) * cT, s_tab) / sp.S;
-          const double qv = exp2_f64(((double)P.q[((long long)b * k + lane) * V + x] - sq.m) * cT, s_tab) / sq.S;
-          reject = !(pv > 0.0 && r * qv <= pv);
+          const double pv = exp2_f64(((double)px - sp.m) * cT, s_tab) / sp.S;
+          const double qv = exp2_f64(((double)qx - sq.m) * cT, s_tab) / sq.S;
+          reject = !(pv > 0.0 && (double)r * qv <= pv);
         }
       }
       s_ids[lane] = x;
