@@ -182,10 +182,10 @@ def test_large_batch_small_vocab():
     _compare(p, q, ids, u, "B=4096")
 
 
-def test_batch_with_eight_chunks_per_workgroup():
-    """256 sequences at V = 128256: 32 chunks of 4008 tokens per row, four workgroups per
-    sequence, so each workgroup streams eight consecutive chunks -- the count from which the
-    chunk loads take the non-temporal path."""
+def test_batch_with_thirty_two_chunks_per_workgroup():
+    """256 sequences at V = 128256: 126 chunks of 1020 tokens per row, four workgroups per
+    sequence, so each workgroup streams 32 consecutive chunks (eight per wave) -- the count from
+    which the chunk loads take the non-temporal path."""
     vin = workloads.verify_config("spec_verify_step", seed=4242, batch=256)
     p, q, ids, u = _margin_inputs(vin, 4243)
     _compare(p, q, ids, u, "B=256, V=128256")
@@ -200,6 +200,18 @@ def test_largest_vocabulary():
     vin = workloads.make_verify_inputs(2020, p_logits=pl, q_logits=ql, rng=rng)
     p, q, ids, u = _margin_inputs(vin, 11)
     _compare(p, q, ids, u, "V=2^20")
+
+
+def test_vocabulary_with_chunks_of_two_pieces_not_a_multiple_of_four():
+    """V = 300001: 256 chunks of 1172 tokens, each summed by one wave in two pieces (1024 + 148),
+    with the scalar (not 16-byte) loads, and the select over 16 tokens per thread."""
+    rng = np.random.default_rng(3001)
+    B, k, V = 3, 4, 300001
+    pl = 3.0 * rng.standard_normal((B, k + 1, V))
+    ql = pl[:, :k] + 0.7 * rng.standard_normal((B, k, V))
+    vin = workloads.make_verify_inputs(3001, p_logits=pl, q_logits=ql, rng=rng)
+    p, q, ids, u = _margin_inputs(vin, 12)
+    _compare(p, q, ids, u, "V=300001")
 
 
 def test_monte_carlo_emitted_distribution():

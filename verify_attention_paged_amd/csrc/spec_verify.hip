@@ -205,8 +205,7 @@ __device__ __forceinline__ float4 ld_f4(const float* p) {
 }
 
 // A thread's share of one chunk in registers: loaded (every load issued at once), then summed
-// (chunk_partial does both; publish_chunk_sums keeps the next chunk's loads in flight while it
-// sums the current one).
+// (chunk_partial does both; the fallback of finish_draw sums whole chunks with it).
 template <bool VEC4>
 struct ChunkRegs {
   static constexpr int kIt = VEC4 ? kMaxChunkLen / (4 * kThreads) : kMaxChunkLen / kThreads;
@@ -258,10 +257,9 @@ __device__ __forceinline__ double chunk_partial(const float* prow, const float* 
 // Smallest x in chunk [x0, x1) whose running sum base + C exceeds t (INT_MAX if none), with
 // the running sum taken in ascending token id; also the largest x with w_x > 0 (-1 if none).
 // Each thread takes a contiguous slice of at most kSlice elements held in registers (chunks
-// are at most kThreads * kSlice long), so the scan never goes back to memory.
-constexpr int kSlice = 16;
-
-template <bool VEC4, class W>
+// are at most kThreads * kSlice long), so the scan never goes back to memory: kSlice = 4 for
+// chunks of up to kDrawPiece tokens, 16 for the longer chunks of vocabularies above 256 kDrawPiece.
+template <bool VEC4, int kSlice, class W>
 __device__ __forceinline__ void chunk_select(const float* prow, const float* qrow, const W& w,
                                              int x0, int x1, double base, double t,
                                              double* s_red, int* s_int, int& first_above,
@@ -399,27 +397,77 @@ __device__ __forceinline__ bool arrive(int32_t* ticket, int last) {
 }
 
 // Sums of w over this workgroup's chunks [c0, c1) of the row(s) at prow / qrow, each published to
-// its slot.  Launches whose workgroups take kNtChunks chunks or more (large batches, where the draw
-// streams at bandwidth) load them non-temporally (NT): 163 against 177 us at 1024 sequences of
-// vocabulary 128256, while small batches, bound by their round trips, measured slightly slower.
+// its slot: wave v sums chunks c0 + v, c0 + v + 4, ..., each in pieces of up to kDrawPiece tokens
+// (lane-strided 16-byte loads, the next piece's loads in flight while one is summed), and its
+// lane 0 publishes the chunk's sum.  Launches whose workgroups take kNtChunks chunks or more
+// (large batches, where the draw streams at bandwidth) load them non-temporally (NT): bytes that
+// no other load of the call reads again run closer to the HBM peak that way, while small
+// batches, bound by their round trips, measured slightly slower.
+template <bool VEC4>
+struct PieceRegs {
+  static constexpr int kIt = VEC4 ? kDrawPiece / 256 : kDrawPiece / 64;   // per lane
+  float4 pv[VEC4 ? kIt : 1], qv[VEC4 ? kIt : 1];
+  float ps[VEC4 ? 1 : kIt], qs[VEC4 ? 1 : kIt];
+};
 
 template <bool VEC4, bool NT, class W>
 __device__ __forceinline__ void publish_chunk_sums(const float* prow, const float* qrow, const W& w, int c0, int c1,
-                                                   int CS, int V, unsigned long long* slots, double* s_red) {
-  // two chunks in flight: chunk c + 1 loads while chunk c is summed
-  ChunkRegs<VEC4> ra, rb;
-  auto load = [&](ChunkRegs<VEC4>& r, int c) { chunk_load<VEC4, NT>(r, prow, qrow, w.residual, c * CS, min(V, c * CS + CS)); };
-  auto finish = [&](const ChunkRegs<VEC4>& r, int c) {
-    const double part = block_sum(chunk_sum<VEC4>(r, w, c * CS, min(V, c * CS + CS)), s_red);
-    if (threadIdx.x == 0) publish_slot(slots + c, part);
+                                                   int CS, int V, unsigned long long* slots) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int kIt = PieceRegs<VEC4>::kIt;
+  const int np = (CS + kDrawPiece - 1) / kDrawPiece;            // pieces per chunk
+  const int nc = c1 - c0 > wv ? (c1 - c0 - wv + 3) / 4 : 0;    // this wave's chunks
+  const int n = nc * np;                                        // this wave's pieces
+  // piece f: chunk c0 + wv + 4 (f / np), tokens [x0, x1)
+  auto range = [&](int f, int& x0, int& x1) {
+    const int c = c0 + wv + 4 * (f / np);
+    const int e = min(V, c * CS + CS);
+    x0 = c * CS + (f % np) * kDrawPiece;
+    x1 = min(e, x0 + kDrawPiece);
   };
-  if (c0 < c1) load(ra, c0);
-  for (int c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) load(rb, c + 1);
-    finish(ra, c);
-    if (c + 1 >= c1) break;
-    if (c + 2 < c1) load(ra, c + 2);
-    finish(rb, c + 1);
+  auto load = [&](PieceRegs<VEC4>& r, int f) {
+    int x0, x1;
+    range(f, x0, x1);
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      if constexpr (VEC4) {
+        const int x = min(x0 + 4 * (lane + 64 * i), x1 - 4);
+        r.pv[i] = ld_f4<NT>(prow + x);
+        r.qv[i] = w.residual ? ld_f4<NT>(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        const int x = min(x0 + lane + 64 * i, x1 - 1);
+        r.ps[i] = prow[x];
+        r.qs[i] = w.residual ? qrow[x] : 0.f;
+      }
+    }
+  };
+  double acc = 0.0;
+  auto finish = [&](const PieceRegs<VEC4>& r, int f) {
+    int x0, x1;
+    range(f, x0, x1);
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      if constexpr (VEC4) {
+        if (x0 + 4 * (lane + 64 * i) < x1)
+          acc += w(r.pv[i].x, r.qv[i].x) + w(r.pv[i].y, r.qv[i].y) + w(r.pv[i].z, r.qv[i].z) + w(r.pv[i].w, r.qv[i].w);
+      } else {
+        if (x0 + lane + 64 * i < x1) acc += w(r.ps[i], r.qs[i]);
+      }
+    }
+    if (f % np == np - 1) {   // the chunk's last piece
+      const double part = wave_total(acc);
+      if (lane == 0) publish_slot(slots + c0 + wv + 4 * (f / np), part);
+      acc = 0.0;
+    }
+  };
+  PieceRegs<VEC4> ra, rb;
+  if (n > 0) load(ra, 0);
+  for (int f = 0; f < n; f += 2) {
+    if (f + 1 < n) load(rb, f + 1);
+    finish(ra, f);
+    if (f + 1 >= n) break;
+    if (f + 2 < n) load(ra, f + 2);
+    finish(rb, f + 1);
   }
 }
 
@@ -517,7 +565,11 @@ __device__ int finish_draw(unsigned long long* slots, int C, int CS, int V, floa
   if (cstar >= 0) {
     const int a = cstar * CS, e = min(V, a + CS);
     int first_above, last_positive;
-    chunk_select<VEC4>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above, last_positive);
+    if (CS <= kDrawPiece)
+      chunk_select<VEC4, kDrawPiece / kThreads>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above, last_positive);
+    else
+      chunk_select<VEC4, kMaxChunkLen / kThreads>(prow, srow_q, wsel, a, e, base, t, s_red, s_int, first_above,
+                                                  last_positive);
     token = (first_above != INT_MAX) ? first_above : (last_positive >= 0 ? last_positive : 0);
   }
   return token;
@@ -655,7 +707,8 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
 
   // 2-3. the sums of w over this workgroup's chunks
   unsigned long long* sums = P.rec.at<unsigned long long>(b, kVerifyRecSums);
-  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, V, sums, s_red);
+  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, V, sums);
+  __syncthreads();   // every wave has published before the workgroup arrives
   if (tid == 0) s_last = arrive(P.rec.ticket(b), WPS - 1);
   __syncthreads();
   if (!s_last) return;
@@ -858,7 +911,8 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
   const float* qrow = P.q + row * P.V;
   const TreeDrawWeight w{d.c > 0.0, d.c};
   unsigned long long* sums = P.rec.at<unsigned long long>(b, kTreeRecSums);
-  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, P.V, sums, s_red);
+  publish_chunk_sums<VEC4, NT>(prow, qrow, w, c0, c1, P.CS, P.V, sums);
+  __syncthreads();   // every wave has published before the workgroup arrives
   if (tid == 0) s_last = arrive(P.rec.ticket(b), WPS - 1);
   __syncthreads();
   if (!s_last) return;
@@ -872,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(const TreeDrawParam
 }  // namespace
 
 // Workgroups that stream at least this many chunks load them non-temporally (see publish_chunk_sums).
-constexpr int kNtChunks = 8;
+constexpr int kNtChunks = 32;
 
 template <bool LOGITS>
 hipError_t launch_verify_t(const VerifyParams& p, bool vec4, hipStream_t stream, KTimer t) {

@@ -183,25 +183,30 @@ hipError_t launch_logit_stats(const LogitStatsParams& p, bool vec4, int num_wg, 
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 
 // Vocabulary chunking of a verification draw over B sequences on a GPU of `cus` CUs: C chunks of
-// CS tokens per row (CS a multiple of 4 and at most 4096, since the selecting workgroup holds a
-// chunk in registers; about two chunks per CU over the batch), and WPS workgroups per sequence,
-// each taking ceil(C / WPS) consecutive chunks (about four workgroups per CU over the batch, so
-// large batches stream many chunks per workgroup instead of paying the accept tests per chunk).
+// CS tokens per row (C <= kMaxChunks slots; CS a multiple of 4, at most kDrawPiece = 1024 while
+// the vocabulary allows, else up to 4096), about eight chunks per CU over the batch.  One wave
+// sums a chunk (in pieces of kDrawPiece tokens) and publishes it; the selecting workgroup holds
+// one chunk in registers.  WPS workgroups per sequence each take G = ceil(C / WPS) consecutive
+// chunks, their four waves taking every fourth: about four workgroups per CU over the batch, and
+// at least four chunks per workgroup.
+constexpr int kDrawPiece = 1024;
 struct DrawChunks {
   int C, CS, WPS;
 };
 
 inline DrawChunks draw_chunks(long long B, long long V, int cus) {
-  long long C = (2LL * cus + B - 1) / B;
+  long long C = (8LL * cus + B - 1) / B;
   const long long cmax = (V + 255) / 256 < kMaxChunks ? (V + 255) / 256 : kMaxChunks;
   C = C < 1 ? 1 : (C > cmax ? cmax : C);
-  if (C < 1) C = 1;
+  const long long cmin = (V + kDrawPiece - 1) / kDrawPiece;
+  if (C < cmin) C = cmin < kMaxChunks ? cmin : kMaxChunks;
   if (C < (V + 4095) / 4096) C = (V + 4095) / 4096;
   long long CS = (V + C - 1) / C;
   CS = (CS + 3) / 4 * 4;
   C = (V + CS - 1) / CS;
   long long WPS = (4LL * cus + B - 1) / B;
-  WPS = WPS < 1 ? 1 : (WPS > C ? C : WPS);
+  const long long wmax = (C + 3) / 4;
+  WPS = WPS < 1 ? 1 : (WPS > wmax ? wmax : WPS);
   const long long G = (C + WPS - 1) / WPS;
   WPS = (C + G - 1) / G;          // no workgroup without a chunk
   return DrawChunks{(int)C, (int)CS, (int)WPS};
