@@ -730,16 +730,6 @@ __global__ __launch_bounds__(kThreads) void spec_verify_kernel(const VerifyParam
   if (tid == 0) P.n_accepted[b] = n;
 }
 
-// Row statistics of the logits (see LogitRowStat), per chunk of kStatChunk tokens: persistent
-// waves take (row, chunk) items with a grid stride and keep the next item's loads in flight
-// while they reduce the current one (lane j holds 32 tokens; max and first argmax by cross-lane
-// shuffles, then the fp64 sum of exponentials).  Each item writes its partial with a plain
-// store; the verification kernel merges them.  Draft rows of greedy sequences are skipped.
-//
-// Every item issues the same loads on every path: an item with nothing to read (past the last
-// one, or a skipped draft row) reads the first 16 bytes of the target logits in every lane.
-// With loads that depend on the path, the compiler's wait counts must assume the shortest
-// queue, and the reduce of one item then waits for the loads of the next.
 // f(0), f(1), ... with compile-time arguments, stopping at the first that returns true
 template <typename F, int... I>
 __device__ __forceinline__ bool each_until(F& f, std::integer_sequence<int, I...>) {
@@ -752,6 +742,18 @@ constexpr int kStatTempsLds = 4096;   // 16 KB
 #endif
 constexpr int kStatStages = VAP_STAT_STAGES;   // statistics items per wave in flight or in reduction
 
+// Row statistics of the logits (see LogitRowStat), per chunk of kStatChunk tokens: persistent
+// waves take (row, chunk) items with a grid stride and keep the next kStatStages - 1 items'
+// loads in flight while they reduce the current one (each lane holds 32 tokens; max and first
+// argmax by compares per lane and DPP steps, then the fp64 sum of exponentials).  Each item
+// writes its partial with a plain store; the verification kernel merges them.  Draft rows of
+// greedy sequences are skipped.
+//
+// Every item issues the same loads on every path: an item with nothing to read (past the last
+// one, or a skipped draft row) reads the first 16 bytes of the target logits in every lane.
+// With loads that depend on the path, the compiler's wait counts must assume the shortest
+// queue, and the reduce of one item then waits for the loads of the next.
+//
 // TLDS: the batch's temperatures are staged in LDS (batches of up to kStatTempsLds sequences);
 // a global load of the temperature would make the next item's loads wait for the current one's.
 template <bool VEC4, bool TLDS>
