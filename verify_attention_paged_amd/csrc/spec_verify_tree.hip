@@ -44,18 +44,19 @@ constexpr int kMaxNodes = 64;
 constexpr int kRound = 2;    // float4 pairs (or 4x that many floats) per chunk and thread in flight
 constexpr int kBatch = 4;    // chunks computed together
 
-// Fixed-order workgroup sums of kBatch doubles per thread: thread k < kBatch returns the sum of
-// the threads' x[k] (other threads return 0).
-__device__ __forceinline__ double block_sums(const double (&x)[kBatch], double (*s_red)[kThreads / 64]) {
+// Fixed-order workgroup sums of NB doubles per thread: thread k < NB returns the sum of the
+// threads' x[k] (other threads return 0).
+template <int NB>
+__device__ __forceinline__ double block_sums(const double (&x)[NB], double (*s_red)[kThreads / 64]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
+  for (int k = 0; k < NB; ++k) {
     const double v = wave_incl_scan(x[k]);   // lane 63 holds the wave's sum
     if (lane == 63) s_red[k][wv] = v;
   }
   __syncthreads();
   double t = 0.0;
-  if (threadIdx.x < kBatch) {
+  if (threadIdx.x < NB) {
     for (int i = 0; i < kThreads / 64; ++i) t += s_red[threadIdx.x][i];
   }
   __syncthreads();
@@ -67,21 +68,21 @@ __device__ __forceinline__ double weight(float p, float q, double c) {
   return fmax(0.0, fma(-c, (double)q, (double)p));
 }
 
-// This thread's partial sums of max(0, p - c q) over chunks js[0 .. n-1] of the row pair: thread
-// t takes the chunk's float4s t, t + 1024, ... (VEC4) or its elements t, t + 1024, ..., and adds
-// them in that order.  Every load of a round is issued before any is used.
-template <bool VEC4>
+// This thread's partial sums of max(0, p - c q) over chunks js[0 .. n-1] (n <= NB) of the row
+// pair: thread t takes the chunk's float4s t, t + 1024, ... (VEC4) or its elements t, t + 1024,
+// ..., and adds them in that order.  Every load of a round is issued before any is used.
+template <bool VEC4, int NB>
 __device__ void chunk_partials(const float* prow, const float* qrow, double c, const int (&js)[kBatch], int n,
-                               WalkChunks wc, int V, double (&acc)[kBatch]) {
+                               WalkChunks wc, int V, double (&acc)[NB]) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) acc[k] = 0.0;
+  for (int k = 0; k < NB; ++k) acc[k] = 0.0;
   if constexpr (VEC4) {
     const int per = wc.CS / 4, V4 = V / 4;
     for (int r = 0; r < per; r += kRound * kThreads) {
-      float4 pv[kBatch][kRound], qv[kBatch][kRound];
+      float4 pv[NB][kRound], qv[NB][kRound];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
 #pragma unroll
         for (int i = 0; i < kRound; ++i) {
           const int e = min(((k < n) ? js[k] : js[0]) * per + r + i * kThreads + tid, V4 - 1);
@@ -90,7 +91,7 @@ __device__ void chunk_partials(const float* prow, const float* qrow, double c, c
         }
       }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
 #pragma unroll
         for (int i = 0; i < kRound; ++i) {
           const int off = r + i * kThreads + tid;
@@ -104,9 +105,9 @@ __device__ void chunk_partials(const float* prow, const float* qrow, double c, c
     constexpr int kR = 4 * kRound;
     const int per = wc.CS;
     for (int r = 0; r < per; r += kR * kThreads) {
-      float pv[kBatch][kR], qv[kBatch][kR];
+      float pv[NB][kR], qv[NB][kR];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
           const int e = min(((k < n) ? js[k] : js[0]) * per + r + i * kThreads + tid, V - 1);
@@ -115,7 +116,7 @@ __device__ void chunk_partials(const float* prow, const float* qrow, double c, c
         }
       }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
           const int off = r + i * kThreads + tid;
@@ -126,13 +127,24 @@ __device__ void chunk_partials(const float* prow, const float* qrow, double c, c
   }
 }
 
-// Chunk sums of chunks js[0 .. n-1]: thread k < n returns the sum of chunk js[k].
+// Chunk sums of chunks js[0 .. n-1]: thread k < n returns the sum of chunk js[k].  One chunk, or
+// two with 16-byte loads (S workgroups sharing 16 chunks: one each at S = 16, two at S = 8), load
+// and reduce only their own data; the kBatch form would issue the loads of kBatch chunks and
+// kBatch reductions.
+template <bool VEC4, int NB>
+__device__ __forceinline__ double chunk_sums_n(const float* prow, const float* qrow, double c, const int (&js)[kBatch],
+                                               int n, WalkChunks wc, int V, double (*s_red)[kThreads / 64]) {
+  double part[NB];
+  chunk_partials<VEC4, NB>(prow, qrow, c, js, n, wc, V, part);
+  return block_sums<NB>(part, s_red);
+}
+
 template <bool VEC4>
 __device__ __forceinline__ double chunk_sums(const float* prow, const float* qrow, double c, const int (&js)[kBatch],
                                              int n, WalkChunks wc, int V, double (*s_red)[kThreads / 64]) {
-  double part[kBatch];
-  chunk_partials<VEC4>(prow, qrow, c, js, n, wc, V, part);
-  return block_sums(part, s_red);
+  if (n == 1) return chunk_sums_n<VEC4, 1>(prow, qrow, c, js, n, wc, V, s_red);
+  if (VEC4 && n == 2) return chunk_sums_n<VEC4, 2>(prow, qrow, c, js, n, wc, V, s_red);   // (scalar loads: spills)
+  return chunk_sums_n<VEC4, kBatch>(prow, qrow, c, js, n, wc, V, s_red);
 }
 
 __device__ __forceinline__ unsigned long long* walk_sum(const TreeVerifyParams& P, int b, int pass, int j) {
