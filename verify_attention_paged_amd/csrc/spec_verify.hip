@@ -106,16 +106,6 @@ struct TreeDrawWeight {
   }
 };
 
-// Workgroup index in sequence-major order, XCD-aware: the GPU deals workgroup i to XCD i % 8
-// and each XCD has its own L2, so each XCD takes a contiguous range of indices.  The workgroups
-// of one sequence then share an L2, and the one that finishes the draw rescans a chunk that a
-// sibling streamed from that L2 instead of from HBM.
-constexpr int kXCDs = 8;
-__device__ __forceinline__ int seq_major_index() {
-  if (gridDim.x % kXCDs != 0) return blockIdx.x;
-  return (int)(blockIdx.x % kXCDs) * (int)(gridDim.x / kXCDs) + (int)(blockIdx.x / kXCDs);
-}
-
 // Fixed-order workgroup sum (same order every time).
 __device__ __forceinline__ double block_sum(double x, double* s_red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

@@ -168,8 +168,9 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const TreeVerifyP
   __shared__ int s_path[kMaxNodes];
 
   const int S = P.S;
-  const int b = blockIdx.x / S;
-  const int role = blockIdx.x - b * S;   // 0 writes the results
+  const int L = seq_major_index();       // a sequence's S workgroups on one XCD
+  const int b = L / S;
+  const int role = L - b * S;            // 0 writes the results
   const int tid = threadIdx.x;
   const int N = P.N, V = P.V;
   const long long row0 = (long long)b * N;

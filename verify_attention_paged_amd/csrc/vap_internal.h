@@ -26,6 +26,17 @@ struct SeqRecords {
   __host__ __device__ T* at(long long b, int off) const { return reinterpret_cast<T*>(base + b * stride + off); }
 };
 
+// Workgroup index in sequence-major order, XCD-aware: the GPU deals workgroup i to XCD i % 8
+// and each XCD has its own L2, so each XCD takes a contiguous range of indices.  The workgroups
+// of one sequence then share an L2: a draw's last workgroup rescans a chunk that a sibling
+// streamed from that L2 instead of from HBM, and the tree walk's workgroups exchange their chunk
+// sums within one XCD.
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int seq_major_index() {
+  if (gridDim.x % kXCDs != 0) return blockIdx.x;
+  return (int)(blockIdx.x % kXCDs) * (int)(gridDim.x / kXCDs) + (int)(blockIdx.x / kXCDs);
+}
+
 // Cross-lane moves of the verifiers' reductions and scans through DPP (row shifts and row
 // broadcasts): a modifier on a VALU move, where __shfl_* takes one LDS-crossbar round trip
 // (ds_bpermute) per 32-bit half.  Lanes without a source, or outside ROW_MASK, read 0.  The
