@@ -245,3 +245,15 @@ def test_greedy_argmax_ties_pick_the_first_index():
     ref = _compare(zp_, zq_, ids_, u, T, "argmax ties")
     assert list(ref[1][:4]) == [3, 0, 2, 1]
     assert ref[0][0, 3] == first[0, 3] and ref[0][1, 0] == first[1, 0] and ref[0][2, 2] == first[2, 2]
+
+
+def test_batch_above_the_lds_temperature_stage():
+    """4100 sequences: above the 4096 temperatures the statistics kernel stages in LDS, so it
+    reads each item's temperature from global memory; mixed temperatures, bit-exact."""
+    rng = np.random.default_rng(4100)
+    B, k, V = 4100, 2, 96
+    zp = (2.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zq = (zp[:, :k] + 0.6 * rng.standard_normal((B, k, V))).astype(np.float32)
+    temps = rng.choice([0.0, 0.5, 1.0, 1.7], size=B)
+    inp = workloads.make_logits_verify_inputs(4100, zp, zq, temps)
+    _compare(*_margin(inp, 41), "B=4100")

@@ -277,3 +277,18 @@ def test_one_buffer_with_changing_workspace_sizes():
         for name, a, b_ in zip(("ids", "path", "n_accepted"), got, ref):
             assert np.array_equal(a, b_), f"B={B} N={N} V={V}: {name} differ\n{a}\n{b_}"
     assert vap.get_device_error(buf) == 0
+
+
+def test_walk_with_two_chunks_per_workgroup():
+    """40 sequences at V = 128256: 16 chunks per residual sum shared by 12 workgroups per
+    sequence, so four of them sum two chunks of every shared sum (the two-chunk form) and the
+    others one; trees of 5 nodes whose root has four children, so sums are shared."""
+    rng = np.random.default_rng(4040)
+    B, N, V = 40, 5, 128256
+    pl = 3.0 * rng.standard_normal((B, N, V))
+    ql = pl + 0.7 * rng.standard_normal((B, N, V))
+    soft = lambda z: (np.exp(z - z.max(-1, keepdims=True)) / np.exp(z - z.max(-1, keepdims=True)).sum(-1, keepdims=True))
+    parents = np.tile(np.array([-1, 0, 0, 0, 0]), (B, 1))
+    tin = workloads.make_tree_verify_from_probs(4040, soft(pl).astype(np.float32), soft(ql).astype(np.float32), parents)
+    n = _compare(*_margin(tin, 14), "B=40, V=128256, two chunks per workgroup")
+    assert (n == 0).any()   # some roots reject children, so residual sums are taken
