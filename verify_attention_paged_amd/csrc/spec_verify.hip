@@ -305,10 +305,10 @@ __device__ __forceinline__ void chunk_select(const float* prow, const float* qro
 }
 
 __device__ __forceinline__ void argmax_merge(float& m, int& i, float om, int oi) {
-  if (om > m || (om == m && oi < i)) {
-    m = om;
-    i = oi;
-  }
+  // selects, not a branch: inside the DPP steps a branch costs an exec-mask round per step
+  const bool take = (om > m) | ((om == m) & (oi < i));
+  m = take ? om : m;
+  i = take ? oi : i;
 }
 
 // One DPP step of the wave's (max, first argmax): lanes without a source take (-inf, INT_MAX).
