@@ -12,14 +12,15 @@
 //   4. t = u_k * Z and the emitted token is the smallest x with C_x > t;
 //   5. out_ids = accepted drafts, the emitted token, then -1; n_accepted = n.
 //
-// How: one launch.  The vocabulary is cut into C chunks of at most 4096 tokens (about two per
-// CU over the batch), and each sequence gets WPS workgroups that take consecutive chunks (one
-// chunk each for small batches; for large batches a workgroup streams many chunks, so the
-// accept tests are not paid per chunk).  Every workgroup redoes the k gathers of step 1 (2k
-// scattered loads, cheaper than a second launch), streams its chunks of the row it needs with
-// 16-byte loads and publishes each chunk's fp64 sum.  An arrival counter per sequence elects
-// the last workgroup, which scans the C chunk sums, finds the chunk that holds t and rescans only
-// that chunk to pick the token.  The counter and the published sums return to 0, so the workspace
+// How: one launch.  The vocabulary is cut into C chunks of at most 1024 tokens where the
+// vocabulary allows (up to 4096 above 256 * 1024 tokens; about eight chunks per CU over the
+// batch), and each sequence gets WPS workgroups that take consecutive chunks, one wave per chunk
+// (four chunks per workgroup for small batches; for large batches a wave streams many chunks, so
+// the accept tests are not paid per chunk).  Every workgroup redoes the k gathers of step 1 (2k
+// scattered loads, cheaper than a second launch); each wave streams its chunks of the row it
+// needs with 16-byte loads and publishes each chunk's fp64 sum.  An arrival counter per sequence
+// elects the last workgroup, which scans the C chunk sums, finds the chunk that holds t and
+// rescans only that chunk to pick the token.  The counter and the published sums return to 0, so the workspace
 // is ready for the next call.  All bytes of the vocabulary are read once.
 //
 // Verification from logits (tempatgunting.com article, section "Speculative Decoding: Turning
@@ -33,8 +34,8 @@
 // the chunks of its own sequence's rows in LDS (M = max m_c, S = sum S_c 2^((m_c - M) log2(e) / T),
 // in chunk order, so every workgroup of a sequence gets the same values) and evaluates
 // p(x) = 2^((z_x - M) log2(e) / T) / S wherever the rule needs a probability.  No probability
-// row is written.  The exponentials are taken in fp64 (exp2_f64), which keeps every decision
-// within rounding of the fp64 oracle.
+// row is written.  The exponentials are taken in fp64 (exp2_f64, exp2_64th), which keeps every
+// decision within rounding of the fp64 oracle.
 #include <cfloat>
 #include <type_traits>
 #include <utility>
