@@ -555,6 +555,14 @@ __device__ __forceinline__ void codes_f32(uint32_t w, float (&f)[4]) {
   }
 }
 
+// Two E4M3 codes (bytes 0-1, or 2-3 for HI) of a word straight to two bf16 values: gfx950's
+// scaled conversion with scale 1.  A probe on the GPU matched it bit for bit against the f32
+// conversion then rounding to bf16 on all 256 codes; every E4M3 value is exact in bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
 // One tile of the 8-bit cache.  With x = s (c - z) per token: the score of token j is
 // s_k,j (q.c_j - z_k,j sum(q)), so the K codes go to the MFMA as they are (exact in bf16) and
 // the per-token scale is applied to the 16 scores; the output is
@@ -570,10 +578,16 @@ __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, 
   bf16x8 ka[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    float a[4], b[4];
-    codes_f32<F8>(t.kc[2 * kk], a);
-    codes_f32<F8>(t.kc[2 * kk + 1], b);
-    const uint4 u = make_uint4(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3]));
+    uint4 u;
+    if constexpr (F8) {
+      u = make_uint4(fp8_pair_bf16<false>(t.kc[2 * kk]), fp8_pair_bf16<true>(t.kc[2 * kk]),
+                     fp8_pair_bf16<false>(t.kc[2 * kk + 1]), fp8_pair_bf16<true>(t.kc[2 * kk + 1]));
+    } else {
+      float a[4], b[4];
+      codes_f32<F8>(t.kc[2 * kk], a);
+      codes_f32<F8>(t.kc[2 * kk + 1], b);
+      u = make_uint4(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3]));
+    }
     ka[kk] = as_bf16x8(u);
   }
   float sv[NRT][4];
@@ -640,14 +654,27 @@ __device__ __forceinline__ void compute_tile8(const KVTile<D, true>& t, int tg, 
   }
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt) {
-    float v[4];
+    uint2 vt;
+    if constexpr (F8) {
+      // byte jt % 4 of tokens r = 0, 1 (and 2, 3) side by side, with the next byte after them,
+      // so one conversion gives the pair for dim jt and the other for dim jt + 1
+      const int wi = jt >> 2, kb = jt & 2;
+      const uint32_t sel = (uint32_t)kb | ((uint32_t)(4 + kb) << 8) | ((uint32_t)(kb + 1) << 16) |
+                           ((uint32_t)(5 + kb) << 24);
+      const uint32_t w01 = __builtin_amdgcn_perm(t.vc[1][wi], t.vc[0][wi], sel);
+      const uint32_t w23 = __builtin_amdgcn_perm(t.vc[3][wi], t.vc[2][wi], sel);
+      vt = (jt & 1) ? make_uint2(fp8_pair_bf16<true>(w01), fp8_pair_bf16<true>(w23))
+                    : make_uint2(fp8_pair_bf16<false>(w01), fp8_pair_bf16<false>(w23));
+    } else {
+      float v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float f[4];
-      codes_f32<F8>(t.vc[r][jt >> 2], f);
-      v[r] = f[jt & 3];
+      for (int r = 0; r < 4; ++r) {
+        float f[4];
+        codes_f32<F8>(t.vc[r][jt >> 2], f);
+        v[r] = f[jt & 3];
+      }
+      vt = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
     }
-    const uint2 vt = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       acc[rt][jt] = mfma16x16x16(vt, ph[rt], acc[rt][jt]);
