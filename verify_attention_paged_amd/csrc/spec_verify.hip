@@ -20,8 +20,8 @@
 // scattered loads, cheaper than a second launch); each wave streams its chunks of the row it
 // needs with 16-byte loads and publishes each chunk's fp64 sum.  An arrival counter per sequence
 // elects the last workgroup, which scans the C chunk sums, finds the chunk that holds t and
-// rescans only that chunk to pick the token.  The counter and the published sums return to 0, so the workspace
-// is ready for the next call.  All bytes of the vocabulary are read once.
+// rescans only that chunk to pick the token.  The counter and the published sums return to 0, so
+// the workspace is ready for the next call.  All bytes of the vocabulary are read once.
 //
 // Verification from logits (tempatgunting.com article, section "Speculative Decoding: Turning
 // Verification Parallelism into Latency Wins": the verify pass yields logits and tokens are
