@@ -148,7 +148,7 @@ int main() {
   // verification at its extremes: batch up to 2^22, k up to 64, vocabulary up to 2^20
   for (int B : {1, 16, 1024, 8192, 1 << 22})
     for (int k : {0, 4, 64})
-      for (int V : {1, 3, 1000, 128256, 1 << 20}) verify_case(B, k, V);
+      for (int V : {1, 3, 1000, 128256, 262144, 262145, 300001, 1 << 20}) verify_case(B, k, V);
   for (int B : {1, 64, 8192, 1 << 22})
     for (int N : {1, 16, 64})
       for (int V : {1, 3001, 128256, 1 << 20}) tree_case(B, N, V);

@@ -119,6 +119,10 @@ hipError_t launch_spec_verify(const VerifyParams& p, bool, hipStream_t, KTimer) 
   region(p.rec.base, (long long)p.B * p.rec.stride, "verify records", 16);
   need(p.C >= 1 && p.C <= kMaxChunks && (long long)p.C * p.CS >= p.V && p.CS % 4 == 0 && p.CS <= 4096,
        "verify chunks", p.rec.base, p.C);
+  // no empty chunk, and chunks a wave sums in one piece wherever the vocabulary allows
+  need((long long)(p.C - 1) * p.CS < p.V, "verify chunks: an empty chunk", p.rec.base, p.C);
+  need((long long)p.V > (long long)kMaxChunks * kDrawPiece || p.CS <= kDrawPiece, "verify chunks: longer than a piece",
+       p.rec.base, p.CS);
   need(p.WPS >= 1 && p.WPS <= p.C && (long long)((p.C + p.WPS - 1) / p.WPS) * (p.WPS - 1) < p.C, "verify workgroups",
        p.rec.base, p.WPS);
   return hipSuccess;
