@@ -151,7 +151,7 @@ int main() {
       for (int V : {1, 3, 1000, 128256, 262144, 262145, 300001, 1 << 20}) verify_case(B, k, V);
   for (int B : {1, 64, 8192, 1 << 22})
     for (int N : {1, 16, 64})
-      for (int V : {1, 3001, 128256, 1 << 20}) tree_case(B, N, V);
+      for (int V : {1, 3001, 128256, 262145, 1 << 20}) tree_case(B, N, V);
 
   // argument errors are reported, nothing launched
   vap_attn_shape bad = shape(4, 8, 3, 128, 16, 10, 4, 4);

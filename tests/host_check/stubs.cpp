@@ -150,6 +150,10 @@ hipError_t launch_tree_draw(const TreeDrawParams& p, bool, hipStream_t, KTimer) 
   region(p.rec.base, (long long)p.B * p.rec.stride, "tree draw records", 16);
   need(p.C >= 1 && p.C <= kMaxChunks && (long long)p.C * p.CS >= p.V && p.WPS >= 1 && p.WPS <= p.C, "draw chunks",
        p.rec.base, p.C);
+  need((long long)(p.C - 1) * p.CS < p.V && p.CS % 4 == 0 && p.CS <= 4096, "draw chunks: empty or too long",
+       p.rec.base, p.CS);
+  need((long long)p.V > (long long)kMaxChunks * kDrawPiece || p.CS <= kDrawPiece, "draw chunks: longer than a piece",
+       p.rec.base, p.CS);
   return hipSuccess;
 }
 hipError_t launch_kv_append(const KVAppendParams& p, int, bool, int, hipStream_t, KTimer) {
