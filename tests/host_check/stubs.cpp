@@ -102,7 +102,7 @@ hipError_t launch_attn_main(const AttnParams& p, int D, int, int NRT, int kv, in
   need((long long)num_wg * wg_waves == p.W, "worker waves", p.desc, p.W);
   return hipSuccess;
 }
-hipError_t launch_attn_combine(const AttnParams& p, int D, int, hipStream_t) {
+hipError_t launch_attn_combine(const AttnParams& p, int D, int, bool, hipStream_t) {
   ++check_launches;
   attn_regions(p, D, p.B > kLdsPlanMaxSeqs);
   return hipSuccess;

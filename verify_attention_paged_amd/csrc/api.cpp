@@ -417,7 +417,7 @@ int attn_step(const void* q, const void* kv, const float* kv_scales, const int32
   e = launch_attn_main(P, c.D, c.BS, c.NRT, kv8 ? (fp8 ? 2 : 1) : 0, W / wg_waves, wg_waves, stream, t);
   timer_commit(0, t, e);
   if (e != hipSuccess) return fail(VAP_EHIP, "attention launch: %s", hipGetErrorString(e));
-  e = launch_attn_combine(P, c.D, d->num_cus, stream);
+  e = launch_attn_combine(P, c.D, d->num_cus, c.rows_per_seq < 8, stream);
   if (e != hipSuccess) return fail(VAP_EHIP, "combine launch: %s", hipGetErrorString(e));
   return ok();
 }

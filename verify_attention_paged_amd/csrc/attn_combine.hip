@@ -167,12 +167,26 @@ __device__ __forceinline__ void combine_unit(const AttnParams& P, int w, int4 d0
 // pieces) is written on every call, zeroed when it opens no split unit (including the waves
 // past the step's work and the pool pieces the step does not use), so no other check is
 // needed.
+//
+// With xcd_local, the workgroups that merge the worker waves' shares run on the XCDs that ran
+// those waves.  The attention kernel gives XCD x the holders [x W/8, (x+1) W/8), and workgroup i
+// goes to XCD i % 8, so workgroup i = 8 j + x (j < W/(8K)) takes the shares' descriptor group
+// x W/(8K) + j and the rest take the pool pieces' groups in the same XCD-contiguous way.  The map
+// is a permutation of the workgroups: which workgroup merges a unit changes, its result does not.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P, int K) {
+__global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams P, int K, int xcd_local) {
   __shared__ float s_ml[NW][64][2];
   __shared__ float4 s_acc[NW][D / 64][64];
   const int lane = threadIdx.x & 63;
-  const int w0 = blockIdx.x * K;
+  int g = blockIdx.x;
+  if (xcd_local) {
+    const int G = (int)gridDim.x, nS = P.W / K;
+    if (G % 8 == 0 && P.W % (8 * K) == 0 && nS <= G) {
+      const int x = g % 8, j = g / 8, s = nS / 8;
+      g = j < s ? x * s + j : nS + x * ((G - nS) / 8) + (j - s);
+    }
+  }
+  const int w0 = g * K;
   const int nd = min(K, P.NH - w0);
   if (blockIdx.x == 0 && threadIdx.x == 0) P.hdr->pool_next = 0;   // the next step starts with a full pool
   int4 e0 = make_int4(0, 0, 0, 0), e1 = make_int4(0, 0, 0, 0);
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void attn_combine_kernel(const AttnParams 
 
 }  // namespace
 
-hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStream_t stream) {
+hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, bool xcd_local, hipStream_t stream) {
   // waves per workgroup: 2 for 16-row units (decode), 8 for 32-row units, 16 for 64-row units.
   // Most descriptors are empty; for decode batches the smaller workgroups measured faster
   // (less to dispatch, and four quads need no more waves).  K descriptors per workgroup keep
@@ -200,19 +214,21 @@ hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStrea
   // budget allows 4 waves per SIMD): a workgroup merges its units one after another, and
   // halving K from one round's worth took 4 us off the mixed batch's combine (more units in
   // flight at once); two-wave workgroups take at least 2 (fewer workgroups to dispatch
-  // measured slightly faster).
+  // measured slightly faster).  xcd_local (decode- and verify-shaped batches) took about 1 us
+  // off the verify step; the mixed and tree batches, whose prefill-like units sit on a few
+  // XCDs, merged faster spread over all of them.
   const int nw = p.RG > 32 ? 16 : (p.RG > 16 ? 8 : 2);
   const long long resident = (long long)std::max(1, num_cus) * 16 * 2;
   const int K = (int)std::min<long long>(64, std::max<long long>(nw == 2 ? 2 : 1, ((long long)p.NH * nw + resident - 1) / resident));
   const dim3 grid((unsigned)((p.NH + K - 1) / K)), block(64 * nw);
   if (D == 64) {
-    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p, K);
-    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p, K);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, 2>), grid, block, 0, stream, p, K);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<64, 16>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<64, 8>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, 2>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
   } else if (D == 128) {
-    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p, K);
-    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p, K);
-    else hipLaunchKernelGGL((attn_combine_kernel<128, 2>), grid, block, 0, stream, p, K);
+    if (nw == 16) hipLaunchKernelGGL((attn_combine_kernel<128, 16>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
+    else if (nw == 8) hipLaunchKernelGGL((attn_combine_kernel<128, 8>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
+    else hipLaunchKernelGGL((attn_combine_kernel<128, 2>), grid, block, 0, stream, p, K, xcd_local ? 1 : 0);
   } else {
     return hipErrorInvalidValue;
   }

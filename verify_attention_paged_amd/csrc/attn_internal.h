@@ -105,7 +105,8 @@ hipError_t launch_attn_plan(const AttnParams& p, hipStream_t stream);
 // kv: 0 = bf16 cache, 1 = 8-bit integer codes, 2 = FP8 (E4M3) codes
 hipError_t launch_attn_main(const AttnParams& p, int D, int BS, int NRT, int kv, int num_wg, int wg_waves,
                             hipStream_t stream, KTimer t = {});
-hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, hipStream_t stream);
+// xcd_local: merge each worker wave's shares on the XCD that ran that wave (see the kernel)
+hipError_t launch_attn_combine(const AttnParams& p, int D, int num_cus, bool xcd_local, hipStream_t stream);
 const void* attn_main_kernel_ptr(int D, int BS, int NRT, bool lds_plan, bool kv8);
 size_t attn_main_lds_bytes(int B);
 
